@@ -1,0 +1,268 @@
+"""Seeded synthetic inputs for DSA decode-time candidate selection.
+
+This module only lays out inputs: the fp32 indexer-logits buffer
+``[rows, max_model_len]`` (optionally a strided "packed column" view), the
+per-row live range ``[start, end)`` and the selection sizes.  It holds none of
+the selection arithmetic (no block maxima, no ordering, no masking), so it can
+feed both the CPU oracle and the HIP path without coupling them.
+
+Shapes and distributions follow the workloads named for this method:
+
+* ``tiny``          fp32 [4, 4096], block 8, top-64 blocks then top-256 tokens,
+                    ends uniform in [1, 4096] with rows 0/1 pinned to 1 and
+                    4096, 5% of live values duplicated to force ties.
+* ``short_decode``  fp32 [96, 1048576], block 8, top-256 / top-2048, ends from
+                    lognormal(median 400, sigma 0.8) clipped to [1, 8192].
+                    This stands in for ShareGPT-length decode contexts (a few
+                    hundred tokens per request) against a 1M-wide buffer.
+* ``mtp_ragged``    [52 requests x 4 rows, 131072] viewed with column stride 2,
+                    block 16, top-128 / top-2048, per-request starts uniform in
+                    [0, 1024], ends start + U[1, 65536] offset by 0..3 per row,
+                    four edge requests with ends 1023/1024/1025/width.
+* ``long_decode``   fp32 [32, 1048576], block 8, top-2048 / top-2048, ends
+                    uniform in [262144, 1048576], 1% of live values times 8.
+* ``prefill_chunk`` fp32 [8192, 131072] = 4 sequences x 2048 queries, causal
+                    ends ctx + q + 1 with ctx uniform in [0, 120000], block 8,
+                    top-256 / top-2048.
+
+Live values are N(0, 1) fp32 drawn per row from
+``numpy.random.default_rng([seed, cfg, row])`` so any single row can be
+regenerated on its own.  Columns past ``end`` hold a quiet-NaN sentinel,
+columns before ``start`` another, and the interleaved elements of a strided
+view a third, so any stray read or write shows up bit-for-bit.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+BASE_SEED = 20261202
+
+# Quiet NaNs with distinct payloads (bit patterns), never produced by the path.
+SENTINEL_TAIL = np.uint32(0x7FC5A5A5)   # columns at or past end
+SENTINEL_HEAD = np.uint32(0x7FC1B1B1)   # columns before start
+SENTINEL_GAP = np.uint32(0x7FC3C3C3)    # interleaved elements of a strided view
+
+CONFIG_IDS = {
+    "tiny": 1,
+    "short_decode": 2,
+    "mtp_ragged": 3,
+    "long_decode": 4,
+    "prefill_chunk": 5,
+}
+
+
+@dataclasses.dataclass
+class Shape:
+    rows: int
+    width: int
+    block_size: int
+    k_blocks: int
+    k_tokens: int
+    col_stride: int = 1
+    starts_repeat: int = 1
+    ends_repeat: int = 1
+
+    @property
+    def row_stride(self) -> int:
+        return self.width * self.col_stride
+
+    @property
+    def nblocks(self) -> int:
+        return -(-self.width // self.block_size) if self.width else 0
+
+
+@dataclasses.dataclass
+class Case:
+    """One workload instance.
+
+    ``buf`` is the underlying fp32 storage ``[rows, width * col_stride]``;
+    ``logits`` is the ``[rows, width]`` view the method operates on.
+    ``starts`` is None (all rows start at 0) or int32 indexed by
+    ``row // starts_repeat``; ``ends`` is int32 indexed by
+    ``row // ends_repeat``.
+    """
+    name: str
+    shape: Shape
+    buf: np.ndarray
+    starts: Optional[np.ndarray]
+    ends: np.ndarray
+    seed: int
+
+    @property
+    def logits(self) -> np.ndarray:
+        return self.buf[:, :: self.shape.col_stride]
+
+    def live_range(self, row: int):
+        """(start, end clamped to width) of ``row`` as stored in the inputs."""
+        sh = self.shape
+        s = 0 if self.starts is None else int(self.starts[row // sh.starts_repeat])
+        e = int(self.ends[row // sh.ends_repeat])
+        return s, min(e, sh.width)
+
+
+def _row_rng(seed: int, cfg: int, row: int) -> np.random.Generator:
+    return np.random.default_rng([seed, cfg, row])
+
+
+def _fill_row(buf_row: np.ndarray, col_stride: int, width: int, s: int, e: int,
+              rng: np.random.Generator, block_size: int,
+              dup_frac: float = 0.0, outlier_frac: float = 0.0,
+              outlier_scale: float = 8.0) -> None:
+    """Write one row: head sentinel, N(0,1) live span, tail sentinel, gaps."""
+    u = buf_row.view(np.uint32)
+    if col_stride > 1:
+        u[:] = SENTINEL_GAP
+    view = u[::col_stride]
+    s_c = max(0, min(s, width))
+    e_c = max(s_c, min(e, width))
+    view[:s_c] = SENTINEL_HEAD
+    view[e_c:] = SENTINEL_TAIL
+    n = e_c - s_c
+    if n <= 0:
+        return
+    vals = rng.standard_normal(n, dtype=np.float32)
+    if outlier_frac > 0.0:
+        m = int(round(outlier_frac * n))
+        if m:
+            pos = rng.choice(n, size=m, replace=False)
+            vals[pos] *= np.float32(outlier_scale)
+    if dup_frac > 0.0 and n > 1:
+        m = int(round(dup_frac * n))
+        # Half as single-value copies between random live positions.
+        m1 = m // 2
+        if m1:
+            src = rng.integers(0, n, size=m1)
+            dst = rng.integers(0, n, size=m1)
+            vals[dst] = vals[src]
+        # Half as whole-block copies (block aligned relative to start), which
+        # makes two blocks hold identical values and hence identical scores.
+        nfull = n // block_size
+        copies = (m - m1) // max(1, block_size)
+        if nfull >= 2 and copies:
+            src_b = rng.integers(0, nfull, size=copies)
+            dst_b = rng.integers(0, nfull, size=copies)
+            for a, b in zip(src_b, dst_b):
+                vals[b * block_size:(b + 1) * block_size] = \
+                    vals[a * block_size:(a + 1) * block_size]
+    view[s_c:e_c] = vals.view(np.uint32)
+
+
+def _alloc(shape: Shape) -> np.ndarray:
+    return np.empty((shape.rows, shape.width * shape.col_stride), dtype=np.float32)
+
+
+def build_case(name: str, shape: Shape, starts: Optional[np.ndarray],
+               ends: np.ndarray, seed: int, cfg: int = 0,
+               dup_frac: float = 0.0, outlier_frac: float = 0.0,
+               rows_to_fill=None) -> Case:
+    """Allocate and fill a buffer for explicit starts/ends.
+
+    ``rows_to_fill`` (iterable of rows) limits generation to those rows; the
+    others keep the tail sentinel everywhere (useful for oracle spot checks).
+    """
+    buf = _alloc(shape)
+    if rows_to_fill is not None:
+        buf.view(np.uint32)[:] = SENTINEL_TAIL
+    case = Case(name, shape, buf, starts, np.asarray(ends, dtype=np.int32), seed)
+    rows = range(shape.rows) if rows_to_fill is None else rows_to_fill
+    for r in rows:
+        s = 0 if starts is None else int(starts[r // shape.starts_repeat])
+        e = int(case.ends[r // shape.ends_repeat])
+        _fill_row(buf[r], shape.col_stride, shape.width, s, e,
+                  _row_rng(seed, cfg, r), shape.block_size, dup_frac, outlier_frac)
+    return case
+
+
+def row_values(case: Case, row: int, cfg: int, dup_frac: float = 0.0,
+               outlier_frac: float = 0.0) -> np.ndarray:
+    """Regenerate one row of a case (same bits as ``build_case``) by itself."""
+    sh = case.shape
+    tmp = np.empty(sh.width * sh.col_stride, dtype=np.float32)
+    s = 0 if case.starts is None else int(case.starts[row // sh.starts_repeat])
+    e = int(case.ends[row // sh.ends_repeat])
+    _fill_row(tmp, sh.col_stride, sh.width, s, e, _row_rng(case.seed, cfg, row),
+              sh.block_size, dup_frac, outlier_frac)
+    return tmp
+
+
+# --------------------------------------------------------------------------
+# The five named workloads.
+# --------------------------------------------------------------------------
+
+CONFIG_SHAPES = {
+    "tiny": Shape(rows=4, width=4096, block_size=8, k_blocks=64, k_tokens=256),
+    "short_decode": Shape(rows=96, width=1048576, block_size=8, k_blocks=256,
+                          k_tokens=2048),
+    "mtp_ragged": Shape(rows=208, width=131072, block_size=16, k_blocks=128,
+                        k_tokens=2048, col_stride=2, starts_repeat=4,
+                        ends_repeat=1),
+    "long_decode": Shape(rows=32, width=1048576, block_size=8, k_blocks=2048,
+                         k_tokens=2048),
+    "prefill_chunk": Shape(rows=8192, width=131072, block_size=8, k_blocks=256,
+                           k_tokens=2048),
+}
+
+CONFIG_EXTRAS = {
+    "tiny": dict(dup_frac=0.05),
+    "short_decode": dict(),
+    "mtp_ragged": dict(),
+    "long_decode": dict(outlier_frac=0.01),
+    "prefill_chunk": dict(),
+}
+
+
+def config_bounds(name: str, seed_offset: int = 0):
+    """(shape, starts or None, ends, seed) for a named workload."""
+    cfg = CONFIG_IDS[name]
+    seed = BASE_SEED + cfg + seed_offset
+    rng = np.random.default_rng([seed, cfg, 1 << 20])
+    sh = CONFIG_SHAPES[name]
+    W = sh.width
+    if name == "tiny":
+        ends = rng.integers(1, W, size=sh.rows, endpoint=True)
+        ends[0], ends[1] = 1, W
+        return sh, None, ends.astype(np.int32), seed
+    if name == "short_decode":
+        z = rng.standard_normal(sh.rows)
+        ends = np.clip(np.rint(np.exp(math.log(400.0) + 0.8 * z)), 1, 8192)
+        return sh, None, ends.astype(np.int32), seed
+    if name == "mtp_ragged":
+        nreq = sh.rows // sh.starts_repeat
+        starts = rng.integers(0, 1024, size=nreq, endpoint=True)
+        span = rng.integers(1, 65536, size=nreq, endpoint=True)
+        base = starts + span
+        starts[:4] = 0
+        base[:4] = [1023, 1024, 1025, W]
+        ends = np.repeat(base, sh.starts_repeat) + np.tile(
+            np.arange(sh.starts_repeat), nreq)
+        return sh, starts.astype(np.int32), ends.astype(np.int32), seed
+    if name == "long_decode":
+        ends = rng.integers(262144, W, size=sh.rows, endpoint=True)
+        return sh, None, ends.astype(np.int32), seed
+    if name == "prefill_chunk":
+        nseq, q = 4, sh.rows // 4
+        ctx = rng.integers(0, 120000, size=nseq, endpoint=True)
+        ends = (ctx[:, None] + np.arange(q)[None, :] + 1).reshape(-1)
+        return sh, None, np.minimum(ends, np.iinfo(np.int32).max).astype(np.int32), seed
+    raise KeyError(name)
+
+
+def make_config(name: str, seed_offset: int = 0, rows_to_fill=None) -> Case:
+    sh, starts, ends, seed = config_bounds(name, seed_offset)
+    return build_case(name, sh, starts, ends, seed, cfg=CONFIG_IDS[name],
+                      rows_to_fill=rows_to_fill, **CONFIG_EXTRAS[name])
+
+
+def make_custom(rows: int, width: int, block_size: int, k_blocks: int,
+                k_tokens: int, ends, starts=None, col_stride: int = 1,
+                starts_repeat: int = 1, ends_repeat: int = 1, seed: int = 1,
+                dup_frac: float = 0.0, outlier_frac: float = 0.0) -> Case:
+    sh = Shape(rows, width, block_size, k_blocks, k_tokens, col_stride,
+               starts_repeat, ends_repeat)
+    st = None if starts is None else np.asarray(starts, dtype=np.int32)
+    return build_case("custom", sh, st, np.asarray(ends, dtype=np.int32), seed,
+                      cfg=0, dup_frac=dup_frac, outlier_frac=outlier_frac)

@@ -1,0 +1,441 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each ``pin_*`` function takes an oracle module ``o`` and raises
+``AssertionError`` when ``o`` disagrees with a fact fixed by the pages or by
+mathematics: IEEE-754 ordering, brute-force subset characterisations of top-k,
+hand-worked rows, closed forms and invariants.  ``test_oracle_pins.py`` runs
+them on the oracle; ``test_oracle_mutants.py`` runs them on copies of the
+oracle with one planted mistake each and requires that some pin fails.
+
+Nothing here calls the HIP library.
+"""
+from __future__ import annotations
+
+import heapq
+import itertools
+import json
+import math
+import os
+import struct
+
+import numpy as np
+
+from sparse_attention_indexer_start_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NEG_INF = float("-inf")
+
+
+def _bits(x: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def _f32(bits: int) -> float:
+    return struct.unpack("<f", struct.pack("<I", bits))[0]
+
+
+# ---------------------------------------------------------------------------
+# Order key
+# ---------------------------------------------------------------------------
+
+def pin_order_key_literals(o):
+    """Closed-form keys of IEEE-754 special values."""
+    want = [  # a list, not a dict: 0.0 and -0.0 are equal dict keys
+        (0.0, 0x80000000), (-0.0, 0x7FFFFFFF), (1.0, 0xBF800000), (-1.0, 0x407FFFFF),
+        (float("inf"), 0xFF800000), (NEG_INF, 0x007FFFFF),
+    ]
+    for v, k in want:
+        got = int(o.order_keys(np.array([v], dtype=np.float32))[0])
+        assert got == k, f"key({v!r}) = {got:#x}, want {k:#x}"
+
+
+def pin_order_key_ascending_ladder(o):
+    """A hand-ordered ladder of floats maps to strictly increasing keys."""
+    ladder = [NEG_INF, -3.4028235e38, -2.5, -1.0, -1.1754944e-38, -1e-45, -0.0,
+              0.0, 1e-45, 1.1754944e-38, 0.5, 1.0, 1.5, 3.4028235e38, float("inf")]
+    keys = o.order_keys(np.array(ladder, dtype=np.float32)).astype(np.int64)
+    assert np.all(np.diff(keys) > 0), f"keys not increasing: {keys}"
+
+
+def pin_order_key_matches_float_sort(o):
+    """On random non-zero floats the key order is numpy's float order."""
+    rng = np.random.default_rng(7)
+    v = np.concatenate([rng.standard_normal(4000).astype(np.float32),
+                        (rng.standard_normal(200) * 1e-39).astype(np.float32),
+                        (rng.standard_normal(200) * 1e30).astype(np.float32)])
+    v = v[v != 0]
+    by_key = np.argsort(o.order_keys(v), kind="stable")
+    by_val = np.argsort(v, kind="stable")
+    assert np.array_equal(v[by_key], v[by_val])
+
+
+# ---------------------------------------------------------------------------
+# Top-k with ties to the lower index
+# ---------------------------------------------------------------------------
+
+def _brute_top_k(vals, k):
+    """The unique k-subset S with every member above every non-member.
+
+    "Above" means a larger value, or an equal value at a lower index.
+    Enumerates all subsets: only for tiny inputs.
+    """
+    n = len(vals)
+    k = min(k, n)
+    found = []
+    for S in itertools.combinations(range(n), k):
+        Sset = set(S)
+        ok = all(vals[i] > vals[j] or (vals[i] == vals[j] and i < j)
+                 for i in S for j in range(n) if j not in Sset)
+        if ok:
+            found.append(list(S))
+    assert len(found) == 1
+    return found[0]
+
+
+def pin_top_k_bruteforce(o):
+    rng = np.random.default_rng(11)
+    for trial in range(120):
+        n = int(rng.integers(1, 8))
+        vals = rng.choice(np.array([-2.0, -1.0, 0.5, 1.0, 2.0, 3.0], dtype=np.float32), n)
+        k = int(rng.integers(1, n + 2))
+        want = _brute_top_k([float(x) for x in vals], k)
+        got = o.top_k_indices(o.order_keys(vals), k).tolist()
+        assert got == want, f"vals={vals.tolist()} k={k}: got {got}, want {want}"
+
+
+def pin_top_k_heapq(o):
+    """Against the standard library's heap selection on larger random rows."""
+    rng = np.random.default_rng(12)
+    for trial in range(20):
+        n = int(rng.integers(50, 3000))
+        vals = (np.round(rng.standard_normal(n) * 4) + 0.5).astype(np.float32)  # ties, no zeros
+        k = int(rng.integers(1, n + 1))
+        best = heapq.nlargest(k, ((float(v), -i) for i, v in enumerate(vals)))
+        want = sorted(-negi for _, negi in best)
+        got = o.top_k_indices(o.order_keys(vals), k).tolist()
+        assert got == want
+
+
+# ---------------------------------------------------------------------------
+# Block scores
+# ---------------------------------------------------------------------------
+
+def pin_block_scores_worked(o):
+    """Hand-worked: block maxima, partial newest block pinned to +inf."""
+    vals = np.array([1, 5, 2, 7, 3, 4, 0.5], dtype=np.float32)
+    got = o.block_scores_live(vals, 3).tolist()
+    assert got == [5.0, 7.0, float("inf")], got
+    vals = np.array([-3, -1, -2, -5, 9, 9], dtype=np.float32)
+    got = o.block_scores_live(vals, 2).tolist()
+    assert got == [-1.0, -2.0, float("inf")], got
+    # -0 ranks below +0: the score of {-0, +0} is +0 in either order.
+    for pair in ([-0.0, 0.0], [0.0, -0.0]):
+        vals = np.array(pair + [1.0, 1.0], dtype=np.float32)
+        sc = o.block_scores_live(vals, 2)
+        assert _bits(float(sc[0])) == 0x00000000, pair
+
+
+def pin_block_scores_bruteforce(o):
+    """Python ``max`` per block on random rows (no zeros), last block +inf."""
+    rng = np.random.default_rng(13)
+    for trial in range(60):
+        B = int(rng.integers(1, 9))
+        L = int(rng.integers(1, 80))
+        vals = rng.standard_normal(L).astype(np.float32)
+        vals[vals == 0] = 1.0
+        got = o.block_scores_live(vals, B)
+        nlb = math.ceil(L / B)
+        assert got.size == nlb
+        for b in range(nlb):
+            want = math.inf if b == nlb - 1 else max(float(x) for x in vals[b * B:(b + 1) * B])
+            assert float(got[b]) == want, (B, L, b)
+
+
+# ---------------------------------------------------------------------------
+# Whole chain on one row: hand-worked examples
+# ---------------------------------------------------------------------------
+
+def pin_row_fill_rule_worked(o):
+    """Hand-worked fill case.
+
+    L=10, B=4: blocks {0..3}, {4..7}, {8,9}.  K_blk=1 keeps only the newest
+    block, so columns 0..7 become -inf.  K_tok=3 takes columns 8 and 9, then the
+    lowest-index -inf column, 0.
+    """
+    vals = np.array([3, 1, 4, 1, 5, 9, 2, 6, 5, 3], dtype=np.float32)
+    sc, bl, mk, tk = o.select_row(vals, 4, 1, 3)
+    assert sc.tolist() == [4.0, 9.0, float("inf")]
+    assert bl.tolist() == [2]
+    assert mk.tolist() == [NEG_INF] * 8 + [5.0, 3.0]
+    assert tk.tolist() == [0, 8, 9]
+
+
+def pin_row_ties_worked(o):
+    """Hand-worked ties.
+
+    Blocks 0 and 1 both score 2; K_blk=2 keeps the newest block plus block 0
+    (lower id wins the tie).  Columns 4..7 are masked.  K_tok=5: the four 2s
+    at columns 0..3, then the first 1, at column 8.
+    """
+    vals = np.array([2, 2, 2, 2, 2, 2, 2, 2, 1, 1], dtype=np.float32)
+    sc, bl, mk, tk = o.select_row(vals, 4, 2, 5)
+    assert bl.tolist() == [0, 2]
+    assert mk.tolist() == [2.0] * 4 + [NEG_INF] * 4 + [1.0, 1.0]
+    assert tk.tolist() == [0, 1, 2, 3, 8]
+
+
+def pin_row_select_worked(o):
+    """Hand-worked ordinary case.
+
+    B=2, scores [0.5, 8, 3, 7, +inf]; K_blk=3 keeps blocks 1, 3 and the
+    newest block 4.  Masked row: [-inf, -inf, 8, 1, -inf, -inf, 2, 7, 4].
+    K_tok=4 picks 8, 7, 4 and 2, i.e. columns 2, 7, 8, 6.
+    """
+    vals = np.array([0.5, -1, 8, 1, 3, 2, 2, 7, 4], dtype=np.float32)
+    sc, bl, mk, tk = o.select_row(vals, 2, 3, 4)
+    assert sc.tolist() == [0.5, 8.0, 3.0, 7.0, float("inf")]
+    assert bl.tolist() == [1, 3, 4]
+    assert mk.tolist() == [NEG_INF, NEG_INF, 8, 1, NEG_INF, NEG_INF, 2, 7, 4]
+    assert tk.tolist() == [2, 6, 7, 8]
+
+
+def pin_buffer_bounds_worked(o):
+    """Start offset and an end past the width, on a strided view.
+
+    W=12, row 0 live range [3, min(20, 12)) = [3, 12): L=9, B=4 gives blocks
+    {3..6}, {7..10}, {11}.  K_blk=1 keeps only block 2 (column 11); columns
+    3..10 become -inf; K_tok=2 returns column 11 and then column 3.  Row 1
+    has end <= start and stays untouched.
+    """
+    buf = np.full((2, 24), _f32(0x7FC3C3C3), dtype=np.float32)
+    lg = buf[:, ::2]
+    lg[0, :] = np.arange(12, dtype=np.float32) + 1
+    lg[1, :] = 5.0
+    starts = np.array([3, 6], dtype=np.int32)
+    ends = np.array([20, 6], dtype=np.int32)
+    bl, tk, sc, mk = o.select_fused(lg, starts, ends, 4, 1, 2)
+    assert bl.tolist() == [[2], [-1]]
+    assert tk.tolist() == [[3, 11], [-1, -1]]
+    want0 = [1, 2, 3] + [NEG_INF] * 8 + [12]
+    assert mk[0].tolist() == want0
+    assert mk[1].tolist() == [5.0] * 12
+
+
+# ---------------------------------------------------------------------------
+# Special cases that reduce to a plain routine
+# ---------------------------------------------------------------------------
+
+def _py_top(vals, k):
+    order = sorted(range(len(vals)), key=lambda i: (-float(vals[i]), i))
+    return sorted(order[:k])
+
+
+def pin_all_blocks_kept_is_plain_topk(o):
+    """K_blk >= nlb: nothing masked and the token top-k is a plain top-k."""
+    rng = np.random.default_rng(21)
+    for trial in range(30):
+        B = int(rng.integers(1, 9))
+        L = int(rng.integers(1, 300))
+        nlb = math.ceil(L / B)
+        vals = (np.round(rng.standard_normal(L) * 3) + 0.5).astype(np.float32)
+        kt = int(rng.integers(1, L + 3))
+        sc, bl, mk, tk = o.select_row(vals, B, nlb + int(rng.integers(0, 3)), kt)
+        assert bl.tolist() == list(range(nlb))
+        assert np.array_equal(mk.view(np.uint32), vals.view(np.uint32))
+        assert tk.tolist() == _py_top(vals, min(kt, L))
+
+
+def pin_unit_blocks(o):
+    """B = 1 and K_blk = K_tok: the kept tokens are exactly the kept blocks."""
+    rng = np.random.default_rng(22)
+    for trial in range(30):
+        L = int(rng.integers(1, 200))
+        k = int(rng.integers(1, L + 2))
+        vals = rng.standard_normal(L).astype(np.float32)
+        sc, bl, mk, tk = o.select_row(vals, 1, k, k)
+        assert tk.tolist() == bl.tolist()
+        # and the kept blocks are the top-(k-1) of the other values plus the last
+        if k <= L:
+            want = sorted(_py_top(vals[:-1], k - 1) + [L - 1])
+            assert bl.tolist() == want
+
+
+def pin_short_row_keeps_everything(o):
+    """L <= K_tok: the token ids are exactly [s, e')."""
+    rng = np.random.default_rng(23)
+    for trial in range(20):
+        W = int(rng.integers(8, 200))
+        s = int(rng.integers(0, W))
+        e = int(rng.integers(s + 1, W + 10))
+        B = int(rng.integers(1, 6))
+        case = wl.make_custom(1, W, B, 1, 10_000, [e], starts=[s], seed=trial)
+        bl, tk, sc, mk = o.select_fused(case.logits, case.starts, case.ends, B, 1, 10_000)
+        n = min(e, W) - s
+        assert tk[0, :n].tolist() == list(range(s, min(e, W)))
+        assert np.all(tk[0, n:] == -1)
+
+
+# ---------------------------------------------------------------------------
+# Invariants on random cases (the spec invariants)
+# ---------------------------------------------------------------------------
+
+def check_invariants(o, case, bl, tk, sc, mk):
+    """Invariants every output must satisfy (also used on GPU outputs)."""
+    sh = case.shape
+    B = sh.block_size
+    lg = case.logits
+    for r in range(sh.rows):
+        s, e, L = o.row_bounds(r, case.starts, case.ends, sh.width,
+                               sh.starts_repeat, sh.ends_repeat)
+        nlb = -(-L // B) if L > 0 else 0
+        kb, kt = min(sh.k_blocks, nlb), min(sh.k_tokens, L)
+        b_ids, t_ids = bl[r], tk[r]
+        assert np.all(b_ids[kb:] == -1) and np.all(t_ids[kt:] == -1)
+        b_ids, t_ids = b_ids[:kb], t_ids[:kt]
+        assert np.all(np.diff(b_ids) > 0) and np.all(np.diff(t_ids) > 0)
+        mrow = np.array(mk[r], dtype=np.float32)
+        changed = mrow.view(np.uint32) != np.array(lg[r], dtype=np.float32).view(np.uint32)
+        if L == 0:
+            assert not changed.any(), "an empty row must not be written"
+            continue
+        assert b_ids[0] >= 0 and b_ids[-1] == nlb - 1, "newest block must be kept"
+        assert t_ids[0] >= s and t_ids[-1] < e
+        # scores: a value of the block, and no value of the block exceeds it
+        live = np.array(lg[r, s:e], dtype=np.float32)
+        keys = o.order_keys(live)
+        skeys = o.order_keys(sc[r, :nlb])
+        for b in range(nlb - 1):
+            blk = keys[b * B:(b + 1) * B]
+            assert skeys[b] in blk and skeys[b] >= blk.max()
+        assert float(sc[r, nlb - 1]) == math.inf
+        # selected blocks dominate unselected ones: (key, -id) is larger
+        sel = np.zeros(nlb, bool)
+        sel[b_ids] = True
+        if (~sel).any():
+            lo_sel = min((int(skeys[b]), -b) for b in np.nonzero(sel)[0])
+            hi_un = max((int(skeys[b]), -b) for b in np.nonzero(~sel)[0])
+            assert lo_sel > hi_un
+        # mask: exactly the unselected blocks' columns are -inf; rest identical
+        col_sel = np.repeat(sel, B)[:L]
+        assert not changed[:s].any() and not changed[e:].any()
+        assert np.array_equal(changed[s:e], ~col_sel)
+        assert np.all(mrow[s:e].view(np.uint32)[~col_sel] == 0xFF800000)
+        assert int(changed.sum()) == B * max(nlb - sh.k_blocks, 0)
+        # selected tokens dominate unselected ones on the masked row
+        mkeys = o.order_keys(mrow[s:e]).astype(np.int64)
+        tsel = np.zeros(L, bool)
+        tsel[t_ids - s] = True
+        if (~tsel).any():
+            lo_sel = min((mkeys[i], -i) for i in np.nonzero(tsel)[0])
+            hi_un = max((mkeys[i], -i) for i in np.nonzero(~tsel)[0])
+            assert lo_sel > hi_un
+
+
+def pin_invariants_fuzz(o):
+    rng = np.random.default_rng(31)
+    for trial in range(40):
+        R = int(rng.integers(1, 6))
+        W = int(rng.integers(1, 300))
+        B = int(rng.choice([1, 2, 3, 8, 16]))
+        nb = -(-W // B)
+        kb = int(rng.choice([1, 2, max(1, nb // 3), nb, nb + 3]))
+        kt = int(rng.choice([1, 5, max(1, W // 4), W, W + 7]))
+        ends = rng.integers(0, W + 20, size=R)
+        starts = rng.integers(0, max(1, W // 2), size=R)
+        case = wl.make_custom(R, W, B, kb, kt, ends, starts=starts, seed=trial,
+                              dup_frac=0.2)
+        bl, tk, sc, mk = o.select_fused(case.logits, case.starts, case.ends, B, kb, kt)
+        check_invariants(o, case, bl, tk, sc, mk)
+
+
+def pin_invariants_tiny_config(o):
+    case = wl.make_config("tiny")
+    sh = case.shape
+    bl, tk, sc, mk = o.select_fused(case.logits, case.starts, case.ends,
+                                    sh.block_size, sh.k_blocks, sh.k_tokens)
+    check_invariants(o, case, bl, tk, sc, mk)
+
+
+def pin_steps_compose(o):
+    """The fused chain equals its four steps run one after another."""
+    rng = np.random.default_rng(41)
+    for trial in range(15):
+        R, W = int(rng.integers(1, 5)), int(rng.integers(1, 400))
+        B = int(rng.choice([1, 3, 8, 16]))
+        kb, kt = int(rng.integers(1, 40)), int(rng.integers(1, 200))
+        ends = rng.integers(0, W + 5, size=R)
+        starts = rng.integers(0, max(1, W // 3), size=R)
+        case = wl.make_custom(R, W, B, kb, kt, ends, starts=starts, seed=100 + trial,
+                              col_stride=int(rng.integers(1, 3)))
+        lg = case.logits
+        bl, tk, sc, mk = o.select_fused(lg, case.starts, case.ends, B, kb, kt)
+        nb = -(-W // B)
+        sc2 = o.block_scores(lg, case.starts, case.ends, B, np.full((R, nb), np.nan, np.float32))
+        assert np.array_equal(sc2.view(np.uint32), sc.view(np.uint32))
+        bl2 = o.topk_blocks(sc2, case.starts, case.ends, W, B, kb)
+        assert np.array_equal(bl2, bl)
+        mk2 = o.candidate_mask(lg, case.starts, case.ends, B, bl2)
+        assert np.array_equal(mk2.view(np.uint32), mk.view(np.uint32))
+        tk2 = o.topk_tokens(mk2, case.starts, case.ends, B, kt)
+        tk3 = o.topk_tokens(lg, case.starts, case.ends, B, kt, block_ids=bl2)
+        assert np.array_equal(tk2, tk) and np.array_equal(tk3, tk)
+
+
+# ---------------------------------------------------------------------------
+# The pages' own edge lists and figures (tests/golden/page_cases.json)
+# ---------------------------------------------------------------------------
+
+def _page_end(expr: str, width: int) -> int:
+    """Evaluate the forms used in the fixture: an int, width, width-1, width//2."""
+    expr = expr.replace(" ", "")
+    if expr == "width":
+        return width
+    if expr == "width-1":
+        return width - 1
+    if expr == "width//2":
+        return width // 2
+    return int(expr)
+
+
+def pin_page_edge_ends_leave_tail(o):
+    """The report's ragged-end list: writes stay inside each row's [0, end).
+
+    Ends {0, 1, 1023, 1024, 1025, width-1, width, width//2} at widths 8192 and
+    262144 (report on PR #56628, test code), with the buffer pre-filled with a
+    sentinel; here checked on the narrow width with column strides 1 and 2.
+    """
+    g = json.load(open(os.path.join(GOLDEN, "page_cases.json")))
+    W = g["narrow_width"]
+    ends = [_page_end(x, W) for x in g["ragged_ends"]]
+    for cs in (1, 2):
+        case = wl.make_custom(len(ends), W, 16, 4, 64, ends, col_stride=cs, seed=3)
+        bl, tk, sc, mk = o.select_fused(case.logits, case.starts, case.ends, 16, 4, 64)
+        for r, e in enumerate(ends):
+            tail = mk[r, min(e, W):].view(np.uint32)
+            assert np.all(tail == wl.SENTINEL_TAIL)
+        check_invariants(o, case, bl, tk, sc, mk)
+
+
+def pin_page_figures(o):
+    """Block counts and dead-store bytes printed on the pages.
+
+    1,048,576 columns at block size 8 are 131,072 blocks (PR #57459 Summary).
+    The old full-width mask stored -inf over all 96 x 1,048,576 fp32 columns,
+    about 402 MB (report on PR #56628, motivation); under this method a row's
+    stores are bounded by its live span, so a 128-column live row stores at
+    most 512 bytes.
+    """
+    g = json.load(open(os.path.join(GOLDEN, "page_cases.json")))
+    W, B = g["decode_width"], g["decode_block_size"]
+    assert -(-W // B) == g["blocks_per_request"]
+    assert g["rows_in_mask_figure"] * W * 4 == g["full_width_store_bytes"]
+    assert abs(g["full_width_store_bytes"] / 1e6 - g["full_width_store_mb_printed"]) < 1.0
+    L = g["live_columns_in_mask_figure"]
+    vals = np.random.default_rng(5).standard_normal(L).astype(np.float32)
+    sc, bl, mk, tk = o.select_row(vals, B, 1, 1)
+    nchanged = int((mk.view(np.uint32) != vals.view(np.uint32)).sum())
+    assert nchanged * 4 <= 4 * L
+    assert nchanged == B * (-(-L // B) - 1)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
