@@ -1,0 +1,268 @@
+"""ctypes binding of ``libdsa_select.so`` (argument marshalling only).
+
+Every step of the selection runs in the HIP library; this module checks
+tensor shapes, dtypes and devices on the host, passes raw device pointers and
+the current HIP stream, and turns a negative status into an exception.  If the
+library has not been built the first call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdsa_select.so")
+
+DSA_TOPK_BLOCKS = 0
+DSA_TOPK_TOKENS = 1
+DSA_WRITE_MASK = 1
+
+STATUS_NAMES = {
+    0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED",
+    -3: "DSA_ERR_CAPTURING", -4: "DSA_ERR_HIP", -5: "DSA_ERR_DESTROYED",
+}
+
+# Every entry point that include/dsa_select.h declares.
+EXPORTED = (
+    "dsa_select_init", "dsa_select_destroy", "dsa_select_query", "dsa_block_scores",
+    "dsa_topk", "dsa_candidate_mask", "dsa_select_fused", "dsa_read_status",
+    "dsa_reset_workspace", "dsa_last_error",
+)
+
+
+class DsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("k_blocks", ctypes.c_int32), ("k_tokens", ctypes.c_int32),
+        ("width", ctypes.c_int64), ("row_stride", ctypes.c_int64),
+        ("col_stride", ctypes.c_int64), ("starts_repeat", ctypes.c_int32),
+        ("ends_repeat", ctypes.c_int32),
+    ]
+
+
+class LaunchInfo(ctypes.Structure):
+    _fields_ = [
+        ("programs_per_row", ctypes.c_int32), ("threads_per_group", ctypes.c_int32),
+        ("grid_groups", ctypes.c_int32), ("small_row_blocks", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_int64), ("fused_launches", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once; raise if it is not built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m sparse_attention_indexer_start_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i32, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint32
+        lib.dsa_select_init.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(vp)]
+        lib.dsa_select_destroy.argtypes = [vp]
+        lib.dsa_select_query.argtypes = [vp, ctypes.POINTER(LaunchInfo)]
+        lib.dsa_block_scores.argtypes = [vp, vp, vp, vp, vp, vp]
+        lib.dsa_topk.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
+        lib.dsa_candidate_mask.argtypes = [vp, vp, vp, vp, vp, vp]
+        lib.dsa_select_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, u32, vp]
+        lib.dsa_read_status.argtypes = [vp, ctypes.POINTER(u32)]
+        lib.dsa_reset_workspace.argtypes = [vp, vp]
+        lib.dsa_last_error.restype = ctypes.c_char_p
+        for name in EXPORTED:
+            if name != "dsa_last_error":
+                getattr(lib, name).restype = i32
+        _lib = lib
+        return lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        msg = load().dsa_last_error().decode(errors="replace")
+        raise DsaError(rc, msg)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class Context:
+    """One selection shape on one device (owns the library workspace).
+
+    ``logits`` tensors passed to the methods must be fp32 views of shape
+    ``[rows, width]`` with the strides given here (in elements); ``starts``
+    (optional) and ``ends`` are int32, indexed by ``row // starts_repeat`` and
+    ``row // ends_repeat``.
+    """
+
+    def __init__(self, rows: int, width: int, block_size: int, k_blocks: int,
+                 k_tokens: int, row_stride: Optional[int] = None, col_stride: int = 1,
+                 starts_repeat: int = 1, ends_repeat: int = 1, device: int = 0):
+        lib = load()
+        self.shape = Shape(rows, block_size, k_blocks, k_tokens, width,
+                           width * col_stride if row_stride is None else row_stride,
+                           col_stride, starts_repeat, ends_repeat)
+        self.device = device
+        self.nblocks = -(-width // block_size) if width else 0
+        h = ctypes.c_void_p()
+        _check(lib.dsa_select_init(ctypes.byref(self.shape), device, ctypes.byref(h)))
+        self._h = h
+
+    # -- helpers ----------------------------------------------------------
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            _check(load().dsa_select_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise DsaError(-5, "context was closed")
+        return self._h
+
+    def info(self) -> LaunchInfo:
+        li = LaunchInfo()
+        _check(load().dsa_select_query(self.handle, ctypes.byref(li)))
+        return li
+
+    def _stream(self, stream):
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        return ctypes.c_void_p(stream.cuda_stream)
+
+    def _check_logits(self, t):
+        import torch
+        sh = self.shape
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise ValueError("logits must be a float32 device tensor")
+        if tuple(t.shape) != (sh.rows, sh.width):
+            raise ValueError(f"logits shape {tuple(t.shape)} != {(sh.rows, sh.width)}")
+        if sh.rows and sh.width and (
+                (sh.rows > 1 and t.stride(0) != sh.row_stride) or
+                (sh.width > 1 and t.stride(1) != sh.col_stride)):
+            raise ValueError(f"logits strides {t.stride()} != {(sh.row_stride, sh.col_stride)}")
+
+    def _check_i32(self, t, name, n=None, shape=None):
+        import torch
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+        if n is not None and t.numel() < n:
+            raise ValueError(f"{name} has {t.numel()} elements, needs {n}")
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {shape}")
+
+    def _check_bounds(self, starts, ends):
+        sh = self.shape
+        if starts is not None:
+            self._check_i32(starts, "starts", -(-sh.rows // sh.starts_repeat))
+        self._check_i32(ends, "ends", -(-sh.rows // sh.ends_repeat))
+
+    # -- entry points -----------------------------------------------------
+    def block_scores(self, logits, starts, ends, scores, stream=None):
+        import torch
+        self._check_logits(logits)
+        self._check_bounds(starts, ends)
+        if scores.dtype != torch.float32 or not scores.is_contiguous() or \
+                tuple(scores.shape) != (self.shape.rows, self.nblocks):
+            raise ValueError("scores must be contiguous float32 [rows, nblocks]")
+        _check(load().dsa_block_scores(self.handle, _ptr(logits), _ptr(starts), _ptr(ends),
+                                       _ptr(scores), self._stream(stream)))
+
+    def topk_blocks(self, scores, starts, ends, out, stream=None):
+        import torch
+        self._check_bounds(starts, ends)
+        if scores.dtype != torch.float32 or not scores.is_contiguous() or \
+                tuple(scores.shape) != (self.shape.rows, self.nblocks):
+            raise ValueError("scores must be contiguous float32 [rows, nblocks]")
+        self._check_i32(out, "out", shape=(self.shape.rows, self.shape.k_blocks))
+        _check(load().dsa_topk(self.handle, DSA_TOPK_BLOCKS, _ptr(scores), _ptr(starts),
+                               _ptr(ends), None, _ptr(out), self._stream(stream)))
+
+    def topk_tokens(self, logits, starts, ends, block_ids, out, stream=None):
+        self._check_logits(logits)
+        self._check_bounds(starts, ends)
+        if block_ids is not None:
+            self._check_i32(block_ids, "block_ids", shape=(self.shape.rows, self.shape.k_blocks))
+        self._check_i32(out, "out", shape=(self.shape.rows, self.shape.k_tokens))
+        _check(load().dsa_topk(self.handle, DSA_TOPK_TOKENS, _ptr(logits), _ptr(starts),
+                               _ptr(ends), _ptr(block_ids), _ptr(out), self._stream(stream)))
+
+    def candidate_mask(self, logits, starts, ends, block_ids, stream=None):
+        self._check_logits(logits)
+        self._check_bounds(starts, ends)
+        self._check_i32(block_ids, "block_ids", shape=(self.shape.rows, self.shape.k_blocks))
+        _check(load().dsa_candidate_mask(self.handle, _ptr(logits), _ptr(starts), _ptr(ends),
+                                         _ptr(block_ids), self._stream(stream)))
+
+    def select_fused(self, logits, starts, ends, block_ids, token_ids, scores=None,
+                     write_mask: bool = True, stream=None):
+        import torch
+        self._check_logits(logits)
+        self._check_bounds(starts, ends)
+        self._check_i32(block_ids, "block_ids", shape=(self.shape.rows, self.shape.k_blocks))
+        self._check_i32(token_ids, "token_ids", shape=(self.shape.rows, self.shape.k_tokens))
+        if scores is not None and (scores.dtype != torch.float32 or not scores.is_contiguous()
+                                   or tuple(scores.shape) != (self.shape.rows, self.nblocks)):
+            raise ValueError("scores must be contiguous float32 [rows, nblocks]")
+        _check(load().dsa_select_fused(self.handle, _ptr(logits), _ptr(starts), _ptr(ends),
+                                       _ptr(block_ids), _ptr(token_ids), _ptr(scores),
+                                       DSA_WRITE_MASK if write_mask else 0,
+                                       self._stream(stream)))
+
+    def read_status(self) -> int:
+        v = ctypes.c_uint32(0)
+        _check(load().dsa_read_status(self.handle, ctypes.byref(v)))
+        return v.value
+
+    def reset_workspace(self, stream=None) -> None:
+        _check(load().dsa_reset_workspace(self.handle, self._stream(stream)))
+
+
+def select(logits, starts, ends, block_size: int, k_blocks: int, k_tokens: int,
+           starts_repeat: int = 1, ends_repeat: int = 1, write_mask: bool = True,
+           return_scores: bool = False):
+    """One-shot fused selection; allocates the outputs with torch."""
+    import torch
+    rows, width = logits.shape
+    ctx = Context(rows, width, block_size, k_blocks, k_tokens, row_stride=logits.stride(0),
+                  col_stride=logits.stride(1), starts_repeat=starts_repeat,
+                  ends_repeat=ends_repeat, device=logits.device.index or 0)
+    bids = torch.empty((rows, k_blocks), dtype=torch.int32, device=logits.device)
+    tids = torch.empty((rows, k_tokens), dtype=torch.int32, device=logits.device)
+    sc = None
+    if return_scores:
+        sc = torch.full((rows, ctx.nblocks), float("-inf"), dtype=torch.float32, device=logits.device)
+    ctx.select_fused(logits, starts, ends, bids, tids, sc, write_mask)
+    torch.cuda.current_stream(logits.device).synchronize()
+    ctx.close()
+    return (bids, tids, sc) if return_scores else (bids, tids)

@@ -1,0 +1,263 @@
+// Device building blocks for DSA candidate selection on gfx950 (CDNA4).
+//
+// Everything here works on 64-lane wavefronts: ballots are 64-bit, lane ranks
+// come from v_mbcnt, and the segmented block maximum uses DPP row permutes.
+// Values are never rounded: fp32 logits are mapped to order-preserving uint32
+// keys and only compared, so every reduction order gives identical bits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define DSA_DEV __device__ __forceinline__
+
+namespace dsa {
+
+// ---------------------------------------------------------------------------
+// Order key: unsigned order of the key == float order (-0 below +0).
+// ---------------------------------------------------------------------------
+constexpr uint32_t KEY_POS_INF = 0xFF800000u;   // key of +inf
+constexpr uint32_t KEY_NEG_INF = 0x007FFFFFu;   // key of -inf
+constexpr uint32_t NEG_INF_BITS = 0xFF800000u;  // fp32 bits of -inf
+
+DSA_DEV uint32_t f2key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+DSA_DEV float key2f(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront helpers (wave64)
+// ---------------------------------------------------------------------------
+DSA_DEV int lane() { return threadIdx.x & 63; }
+DSA_DEV int wave() { return threadIdx.x >> 6; }
+DSA_DEV uint64_t ballot(bool p) { return __ballot(p); }
+DSA_DEV uint32_t popc(uint64_t m) { return (uint32_t)__popcll(m); }
+// Number of set bits of m in lanes below the calling lane.
+DSA_DEV uint32_t mbcnt(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Max over aligned groups of G consecutive lanes (G in 1,2,4,8,16), every lane
+// of a group gets the group maximum.  DPP: quad_perm [1,0,3,2], quad_perm
+// [2,3,0,1], row_half_mirror, row_mirror.  The whole wave must be active.
+template <int G>
+DSA_DEV uint32_t group_max(uint32_t x) {
+  if constexpr (G >= 2)
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false));
+  if constexpr (G >= 4)
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false));
+  if constexpr (G >= 8)
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false));
+  if constexpr (G >= 16)
+    x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+DSA_DEV uint32_t wave_incl_scan(uint32_t x) {
+  const int l = lane();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// Shared memory of one workgroup.
+// ---------------------------------------------------------------------------
+constexpr int HIST_WORDS = 4096;       // 12-bit digit histogram, or a 131072-bit bitmap
+constexpr int KEY_CAP = 2048;          // block keys of a small row / list of the final stage
+constexpr int SEL_CAP = 2048;          // kept block ids
+constexpr int TK_CAP = 4096;           // token-domain keys
+constexpr int DB_CAP = 2 * KEY_CAP;    // token-domain blocks (aliases keys+ids)
+constexpr int BITMAP_BITS = HIST_WORDS * 32;
+
+struct __align__(16) Smem {
+  uint32_t hist[HIST_WORDS];
+  uint32_t kid[2 * KEY_CAP];  // [0, KEY_CAP): keys, [KEY_CAP, 2*KEY_CAP): ids;
+                              // later the token-domain block list (DB_CAP)
+  uint32_t sel[SEL_CAP];
+  uint32_t tkey[TK_CAP];
+  uint32_t selbits[KEY_CAP / 32];
+  uint32_t wv[64];
+  uint32_t misc[16];
+  DSA_DEV uint32_t* keys() { return kid; }
+  DSA_DEV uint32_t* ids() { return kid + KEY_CAP; }
+};
+
+// Exclusive scan of one value per thread over the workgroup; also the total.
+template <int NT>
+DSA_DEV uint32_t wg_excl_scan(uint32_t x, uint32_t* wv, uint32_t& total) {
+  constexpr int NW = NT / 64;
+  const uint32_t inc = wave_incl_scan(x);
+  if (lane() == 63) wv[wave()] = inc;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+  const int w = wave();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t v = wv[i];
+    off += (i < w) ? v : 0u;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return off + inc - x;
+}
+
+// hist[0..nb): find d with count(bins > d) < krem <= count(bins >= d).
+template <int NT>
+DSA_DEV void find_bin(const uint32_t* hist, int nb, uint32_t krem, Smem& sm,
+                      uint32_t& d, uint32_t& above) {
+  const int per = nb >= NT ? nb / NT : 1;
+  const int lo = (int)threadIdx.x * per;
+  if (threadIdx.x == 0) {   // defined result even if the counts fall short
+    sm.misc[0] = 0;
+    sm.misc[1] = 0;
+  }
+  uint32_t c = 0;
+  if (lo < nb)
+    for (int j = 0; j < per; ++j) c += hist[lo + j];
+  uint32_t total;
+  const uint32_t excl = wg_excl_scan<NT>(c, sm.wv, total);
+  const uint32_t sfx = total - (excl + c);   // sum over threads above this one
+  if (lo < nb && sfx < krem && krem <= sfx + c) {
+    uint32_t acc = sfx;
+    for (int j = per - 1; j >= 0; --j) {
+      const uint32_t h = hist[lo + j];
+      if (acc + h >= krem) {
+        sm.misc[0] = (uint32_t)(lo + j);
+        sm.misc[1] = acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+  d = sm.misc[0];
+  above = sm.misc[1];
+  __syncthreads();
+}
+
+// K-th largest key among getk(0..n), 1 <= K <= n: T, and q = the number of
+// elements equal to T that belong to the top K (the lowest-index ones).
+// MSB-first radix select, digits of 12, 12 and 8 bits, LDS histograms.
+template <int NT, class GetKey>
+DSA_DEV void wg_radix_select(int n, uint32_t K, GetKey getk, Smem& sm,
+                             uint32_t& T, uint32_t& q) {
+  uint32_t prefix = 0, krem = K;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+    const int bits = pass == 2 ? 8 : 12;
+    const int nb = 1 << bits;
+    const int hs = shift + bits;
+    for (int j = threadIdx.x; j < nb; j += NT) sm.hist[j] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const uint32_t k = getk(i);
+      const bool match = (hs >= 32) || ((k >> hs) == (prefix >> hs));
+      if (match) atomicAdd(&sm.hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t d, above;
+    find_bin<NT>(sm.hist, nb, krem, sm, d, above);
+    prefix |= d << shift;
+    krem -= above;
+  }
+  T = prefix;
+  q = krem;
+}
+
+// Ordered pass over [0, n): element i is kept iff key > T, or key == T and it
+// is among the first q such elements in index order.  emit(i, rank, kept,
+// word, base) is called for every i, with rank = kept elements before i,
+// word = the 64-bit kept mask of [base, base + 64).  Returns the kept count.
+// Each wave walks a contiguous segment, so one barrier pair suffices.
+template <int NT, class GetKey, class Emit>
+DSA_DEV uint32_t wg_select_compact(int n, uint32_t T, uint32_t q, GetKey getk,
+                                   Emit emit, Smem& sm) {
+  constexpr int NW = NT / 64;
+  const int w = wave(), l = lane();
+  const int seg = (((n + NW - 1) / NW) + 63) & ~63;
+  const int lo = min(n, w * seg), hi = min(n, lo + seg);
+  uint32_t cgt = 0, ceq = 0;
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + l;
+    const bool v = i < hi;
+    const uint32_t k = v ? getk(i) : 0u;
+    cgt += popc(ballot(v && k > T));
+    ceq += popc(ballot(v && k == T));
+  }
+  if (l == 0) {
+    sm.wv[w] = cgt;
+    sm.wv[NW + w] = ceq;
+  }
+  __syncthreads();
+  uint32_t selb = 0, eqb = 0, my_sel = 0, my_eq = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    if (x == w) {
+      my_sel = selb;
+      my_eq = eqb;
+    }
+    const uint32_t g = sm.wv[x], e = sm.wv[NW + x];
+    const uint32_t take = q > eqb ? min(e, q - eqb) : 0u;
+    selb += g + take;
+    eqb += e;
+  }
+  __syncthreads();
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + l;
+    const bool v = i < hi;
+    const uint32_t k = v ? getk(i) : 0u;
+    const bool gt = v && k > T;
+    const bool eq = v && k == T;
+    const uint64_t meq = ballot(eq);
+    const bool kept = gt || (eq && (my_eq + mbcnt(meq)) < q);
+    const uint64_t mk = ballot(kept);
+    if (v) emit(i, my_sel + mbcnt(mk), kept, mk, base);
+    my_sel += popc(mk);
+    my_eq += popc(meq);
+  }
+  return selb;
+}
+
+// Ordered compaction of [0, n) by a predicate: emit(i, rank) for pred(i).
+template <int NT, class Pred, class Emit>
+DSA_DEV uint32_t wg_compact(int n, Pred pred, Emit emit, Smem& sm) {
+  constexpr int NW = NT / 64;
+  const int w = wave(), l = lane();
+  const int seg = (((n + NW - 1) / NW) + 63) & ~63;
+  const int lo = min(n, w * seg), hi = min(n, lo + seg);
+  uint32_t c = 0;
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + l;
+    c += popc(ballot(i < hi && pred(i)));
+  }
+  if (l == 0) sm.wv[w] = c;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    const uint32_t v = sm.wv[x];
+    off += (x < w) ? v : 0u;
+    tot += v;
+  }
+  __syncthreads();
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + l;
+    const bool p = i < hi && pred(i);
+    const uint64_t m = ballot(p);
+    if (p) emit(i, off + mbcnt(m));
+    off += popc(m);
+  }
+  return tot;
+}
+
+}  // namespace dsa

@@ -1,0 +1,170 @@
+"""Helpers for the GPU parity tests: move seeded cases to the device, run the
+library through its binding, and compare with the oracle row by row."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+from sparse_attention_indexer_start_amd import binding
+from sparse_attention_indexer_start_amd import workloads as wl
+
+NEG_INF_BITS = 0xFF800000
+SCORE_FILL_BITS = 0x7FC0FEED      # pre-fill of the scores buffer (never produced)
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class DevCase:
+    """A workload case on the device, with its pristine copy."""
+
+    def __init__(self, case: wl.Case, device="cuda"):
+        import torch
+        self.case = case
+        self.sh = case.shape
+        self.buf = torch.from_numpy(case.buf).to(device)
+        self.pristine = self.buf.clone()
+        self.starts = None if case.starts is None else torch.from_numpy(case.starts).to(device)
+        self.ends = torch.from_numpy(case.ends).to(device)
+
+    @property
+    def logits(self):
+        return self.buf[:, :: self.sh.col_stride]
+
+    def restore(self):
+        self.buf.copy_(self.pristine)
+
+    def context(self) -> binding.Context:
+        sh = self.sh
+        return binding.Context(sh.rows, sh.width, sh.block_size, sh.k_blocks, sh.k_tokens,
+                               row_stride=sh.row_stride, col_stride=sh.col_stride,
+                               starts_repeat=sh.starts_repeat, ends_repeat=sh.ends_repeat)
+
+    def outputs(self):
+        import torch
+        sh = self.sh
+        dev = self.buf.device
+        bids = torch.full((sh.rows, sh.k_blocks), 12345, dtype=torch.int32, device=dev)
+        tids = torch.full((sh.rows, sh.k_tokens), 12345, dtype=torch.int32, device=dev)
+        scores = torch.full((sh.rows, sh.nblocks), SCORE_FILL_BITS, dtype=torch.int32, device=dev)
+        return bids, tids, scores.view(torch.float32)
+
+    def run_fused(self, ctx=None, write_mask=True, with_scores=True):
+        import torch
+        own = ctx is None
+        ctx = ctx or self.context()
+        bids, tids, scores = self.outputs()
+        ctx.select_fused(self.logits, self.starts, self.ends, bids, tids,
+                         scores if with_scores else None, write_mask)
+        torch.cuda.synchronize()
+        if own:
+            ctx.close()
+        return bids, tids, scores
+
+
+def oracle_row(case: wl.Case, r: int):
+    """(s, e, L, scores, blocks, masked_live, tokens_abs) from the oracle."""
+    sh = case.shape
+    s, e, L = oracle.row_bounds(r, case.starts, case.ends, sh.width, sh.starts_repeat,
+                                sh.ends_repeat)
+    if L == 0:
+        z = np.zeros(0, dtype=np.int64)
+        return s, e, 0, np.zeros(0, np.float32), z, np.zeros(0, np.float32), z
+    live = np.array(case.logits[r, s:e], dtype=np.float32)
+    sc, bl, mk, tk = oracle.select_row(live, sh.block_size, sh.k_blocks, sh.k_tokens)
+    return s, e, L, sc, bl, mk, tk + s
+
+
+def row_bits(t_row) -> np.ndarray:
+    return t_row.detach().cpu().numpy().view(np.uint32)
+
+
+def check_rows_against_oracle(dc: DevCase, rows, bids, tids, scores, masked=True,
+                              check_scores=True):
+    """Bit-exact comparison of the listed rows with the oracle."""
+    case, sh = dc.case, dc.sh
+    b_np = bids.cpu().numpy()
+    t_np = tids.cpu().numpy()
+    for r in rows:
+        s, e, L, sc, bl, mk, tk = oracle_row(case, r)
+        want_b = np.full(sh.k_blocks, -1, np.int32)
+        want_b[: bl.size] = bl
+        want_t = np.full(sh.k_tokens, -1, np.int32)
+        want_t[: tk.size] = tk
+        assert np.array_equal(b_np[r], want_b), (
+            f"row {r} (s={s}, e={e}, L={L}) block ids differ at "
+            f"{np.nonzero(b_np[r] != want_b)[0][:8]}")
+        assert np.array_equal(t_np[r], want_t), (
+            f"row {r} (s={s}, e={e}, L={L}) token ids differ at "
+            f"{np.nonzero(t_np[r] != want_t)[0][:8]}")
+        if check_scores and scores is not None:
+            got = row_bits(scores[r])
+            nlb = sc.size
+            assert np.array_equal(got[:nlb], sc.view(np.uint32)), f"row {r} scores differ"
+            assert np.all(got[nlb:] == SCORE_FILL_BITS), f"row {r} scores written past nlb"
+        # the whole underlying row (live span, head, tail, gaps)
+        want_row = np.array(case.buf[r], dtype=np.float32, copy=True)
+        if masked and L:
+            want_row[s * sh.col_stride: e * sh.col_stride: sh.col_stride] = mk
+        got_row = row_bits(dc.buf[r])
+        diff = np.nonzero(got_row != want_row.view(np.uint32))[0]
+        assert diff.size == 0, f"row {r} buffer differs at underlying columns {diff[:8]}"
+
+
+def check_whole_buffer(dc: DevCase, write_mask=True, chunk_rows=256):
+    """On the device, every row: only live columns of the view changed, only to
+    -inf, and exactly B * max(nlb - K_blk, 0) of them (or none without mask)."""
+    import torch
+    sh, case = dc.sh, dc.case
+    B, K = sh.block_size, sh.k_blocks
+    want = np.zeros(sh.rows, np.int64)
+    lo = np.zeros(sh.rows, np.int64)
+    hi = np.zeros(sh.rows, np.int64)
+    for r in range(sh.rows):
+        s, e, L = oracle.row_bounds(r, case.starts, case.ends, sh.width, sh.starts_repeat,
+                                    sh.ends_repeat)
+        nlb = -(-L // B) if L else 0
+        want[r] = B * max(nlb - K, 0) if write_mask else 0
+        lo[r], hi[r] = s * sh.col_stride, max(s, e) * sh.col_stride
+    ncol = dc.buf.shape[1]
+    cols = torch.arange(ncol, device=dc.buf.device)
+    for r0 in range(0, sh.rows, chunk_rows):
+        r1 = min(sh.rows, r0 + chunk_rows)
+        a = dc.buf[r0:r1].view(torch.int32)
+        b = dc.pristine[r0:r1].view(torch.int32)
+        changed = a != b
+        cnt = changed.sum(1).cpu().numpy()
+        assert np.array_equal(cnt, want[r0:r1]), (
+            f"rows {r0}..{r1}: changed counts {cnt[:8]} != {want[r0:r1][:8]}")
+        bad_val = (changed & (a != torch.tensor(NEG_INF_BITS - (1 << 32), dtype=torch.int32,
+                                                device=a.device))).any().item()
+        assert not bad_val, "a changed element is not -inf"
+        lo_t = torch.from_numpy(lo[r0:r1]).to(a.device)[:, None]
+        hi_t = torch.from_numpy(hi[r0:r1]).to(a.device)[:, None]
+        outside = changed & ((cols[None, :] < lo_t) | (cols[None, :] >= hi_t))
+        assert not outside.any().item(), "an element outside [start, end) changed"
+        if sh.col_stride > 1:
+            gap = changed & ((cols[None, :] % sh.col_stride) != 0)
+            assert not gap.any().item(), "an interleaved element changed"
+
+
+def check_invariants_all_rows(dc: DevCase, bids, tids):
+    """Ids in range, ascending, exact counts, newest block kept (all rows)."""
+    case, sh = dc.case, dc.sh
+    b_np = bids.cpu().numpy()
+    t_np = tids.cpu().numpy()
+    for r in range(sh.rows):
+        s, e, L = oracle.row_bounds(r, case.starts, case.ends, sh.width, sh.starts_repeat,
+                                    sh.ends_repeat)
+        nlb = -(-L // sh.block_size) if L else 0
+        kb, kt = min(sh.k_blocks, nlb), min(sh.k_tokens, L)
+        bb, tt = b_np[r], t_np[r]
+        assert np.all(bb[kb:] == -1) and np.all(tt[kt:] == -1), f"row {r} padding"
+        assert np.all(np.diff(bb[:kb]) > 0) and np.all(np.diff(tt[:kt]) > 0), f"row {r} order"
+        if L:
+            assert bb[0] >= 0 and bb[kb - 1] == nlb - 1, f"row {r}: newest block not kept"
+            assert tt[0] >= s and tt[kt - 1] < e, f"row {r}: token outside [start, end)"

@@ -1,0 +1,367 @@
+"""Parity of the HIP library with the CPU oracle (needs an MI355X).
+
+Every comparison is bit-exact: indices, scores and the masked buffer
+(including the tail past end, the head before start and the interleaved
+elements of a strided view).  Small cases are compared row by row in full;
+the full-size workloads are compared on sampled rows with the oracle and on
+every row through properties checked on the device.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_indexer_start_amd import binding
+from sparse_attention_indexer_start_amd import workloads as wl
+from tests import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load()          # raises if the library is missing: no fallback
+    yield
+    torch.cuda.synchronize()
+
+
+def _full_check(dc, bids, tids, scores, write_mask=True):
+    gh.check_rows_against_oracle(dc, range(dc.sh.rows), bids, tids, scores, masked=write_mask)
+    gh.check_whole_buffer(dc, write_mask)
+    gh.check_invariants_all_rows(dc, bids, tids)
+
+
+# ---------------------------------------------------------------------------
+# Small cases, every row
+# ---------------------------------------------------------------------------
+
+def test_fused_tiny_config():
+    dc = gh.DevCase(wl.make_config("tiny"))
+    gh.log(f"tiny: ends={dc.case.ends.tolist()}")
+    bids, tids, scores = dc.run_fused()
+    _full_check(dc, bids, tids, scores)
+
+
+def _fuzz_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    R = int(rng.integers(1, 8))
+    B = int(rng.choice([1, 2, 3, 4, 5, 8, 16, 32, 64, 128]))
+    W = int(rng.integers(1, 6000 if B > 2 else 9000))
+    nb = -(-W // B)
+    kb = int(rng.choice([1, 2, 7, max(1, nb // 3), nb, nb + 5, 64, 256]))
+    kt = int(rng.choice([1, 3, 100, max(1, W // 5), W, W + 3, 2048]))
+    cs = int(rng.choice([1, 2]))
+    ends = rng.integers(0, W + 40, size=R)
+    ends[rng.random(R) < 0.3] = W
+    starts = None
+    if rng.random() < 0.6:
+        starts = rng.integers(0, max(1, W // 2), size=R)
+    return wl.make_custom(R, W, B, kb, kt, ends, starts=starts, col_stride=cs,
+                          seed=seed, dup_frac=0.1)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_fused_fuzz(seed):
+    case = _fuzz_case(seed)
+    sh = case.shape
+    gh.log(f"fuzz seed={seed} R={sh.rows} W={sh.width} B={sh.block_size} "
+           f"kb={sh.k_blocks} kt={sh.k_tokens} cs={sh.col_stride} ends={case.ends.tolist()} "
+           f"starts={None if case.starts is None else case.starts.tolist()}")
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused()
+    _full_check(dc, bids, tids, scores)
+
+
+@pytest.mark.parametrize("B,W,ends,kb,kt", [
+    (8, 65536, [65536, 40000, 16385], 16, 100),
+    (8, 65536, [65536, 40000, 16385], 1000, 2048),
+    (8, 65536, [65536, 40001, 16399], 3000, 9000),
+    (1, 12000, [12000, 4097, 2049, 11999], 50, 70),
+    (2, 30000, [30000, 20001, 4097], 2047, 5000),
+    (16, 140000, [140000, 70000, 32769], 128, 2048),
+])
+def test_fused_long_rows(B, W, ends, kb, kt):
+    """Rows longer than one workgroup's LDS share: the two-pass path."""
+    case = wl.make_custom(len(ends), W, B, kb, kt, ends, seed=B * 7 + kb, dup_frac=0.02,
+                          outlier_frac=0.01)
+    gh.log(f"long rows B={B} W={W} ends={ends} kb={kb} kt={kt}")
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused()
+    _full_check(dc, bids, tids, scores)
+
+
+def test_fused_long_rows_with_start_and_stride():
+    case = wl.make_custom(4, 50000, 8, 300, 2048, [50000, 49999, 30000, 45000],
+                          starts=[0, 7, 1001, 44990], col_stride=2, seed=77, dup_frac=0.05)
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused()
+    _full_check(dc, bids, tids, scores)
+
+
+def test_fused_without_mask_leaves_buffer():
+    case = wl.make_custom(4, 40000, 8, 64, 500, [40000, 100, 20000, 3], seed=5)
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused(write_mask=False)
+    _full_check(dc, bids, tids, scores, write_mask=False)
+
+
+def test_fused_repeatable():
+    case = wl.make_custom(3, 70000, 8, 500, 3000, [70000, 33000, 9000], seed=9, dup_frac=0.05)
+    dc = gh.DevCase(case)
+    ctx = dc.context()
+    first = None
+    for i in range(4):
+        dc.restore()
+        out = [t.cpu().numpy().copy() for t in dc.run_fused(ctx)[:2]]
+        if first is None:
+            first = out
+        else:
+            assert all(np.array_equal(a, b) for a, b in zip(first, out)), f"run {i} differs"
+    ctx.close()
+
+
+# ---------------------------------------------------------------------------
+# The four steps one by one
+# ---------------------------------------------------------------------------
+
+def _run_steps(dc):
+    import torch
+    sh = dc.sh
+    ctx = dc.context()
+    dev = dc.buf.device
+    scores = torch.full((sh.rows, sh.nblocks), gh.SCORE_FILL_BITS, dtype=torch.int32,
+                        device=dev).view(torch.float32)
+    ctx.block_scores(dc.logits, dc.starts, dc.ends, scores)
+    bids = torch.full((sh.rows, sh.k_blocks), 777, dtype=torch.int32, device=dev)
+    ctx.topk_blocks(scores, dc.starts, dc.ends, bids)
+    tids_virtual = torch.full((sh.rows, sh.k_tokens), 777, dtype=torch.int32, device=dev)
+    ctx.topk_tokens(dc.logits, dc.starts, dc.ends, bids, tids_virtual)
+    ctx.candidate_mask(dc.logits, dc.starts, dc.ends, bids)
+    tids_plain = torch.full((sh.rows, sh.k_tokens), 777, dtype=torch.int32, device=dev)
+    ctx.topk_tokens(dc.logits, dc.starts, dc.ends, None, tids_plain)
+    torch.cuda.synchronize()
+    ctx.close()
+    return scores, bids, tids_virtual, tids_plain
+
+
+@pytest.mark.parametrize("which", ["tiny", "fuzz3", "fuzz8", "long"])
+def test_steps_match_oracle(which):
+    if which == "tiny":
+        case = wl.make_config("tiny")
+    elif which == "long":
+        case = wl.make_custom(3, 65536, 8, 700, 2500, [65536, 30001, 17000], seed=4,
+                              dup_frac=0.03)
+    else:
+        case = _fuzz_case(int(which[4:]))
+    dc = gh.DevCase(case)
+    scores, bids, tv, tp = _run_steps(dc)
+    # scores/ids/mask/tokens equal the fused chain's, which the oracle defines
+    gh.check_rows_against_oracle(dc, range(dc.sh.rows), bids, tv, scores)
+    gh.check_rows_against_oracle(dc, range(dc.sh.rows), bids, tp, scores)
+    gh.check_whole_buffer(dc)
+
+
+def test_plain_row_topk_matches_oracle():
+    case = wl.make_custom(5, 20000, 8, 1, 1500, [20000, 1, 1499, 1501, 12345],
+                          starts=[0, 0, 3, 0, 10], seed=12, dup_frac=0.1)
+    dc = gh.DevCase(case)
+    import torch
+    ctx = dc.context()
+    out = torch.empty((5, 1500), dtype=torch.int32, device=dc.buf.device)
+    ctx.topk_tokens(dc.logits, dc.starts, dc.ends, None, out)
+    torch.cuda.synchronize()
+    ctx.close()
+    want = oracle.topk_tokens(case.logits, case.starts, case.ends, 8, 1500)
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_mask_with_unsorted_and_invalid_ids():
+    """The mask takes ids in any order; -1 and out-of-range ids are ignored."""
+    import torch
+    case = wl.make_custom(2, 5000, 8, 6, 10, [5000, 333], seed=2)
+    dc = gh.DevCase(case)
+    ids = np.array([[600, 3, -1, 624, 10**6, 3], [41, 0, -7, 2, 1, 50]], dtype=np.int32)
+    ctx = dc.context()
+    ctx.candidate_mask(dc.logits, dc.starts, dc.ends, torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    ctx.close()
+    want = oracle.candidate_mask(case.logits, case.starts, case.ends, 8, ids)
+    got = dc.logits.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# The pages' edge lists (report on vllm PR #56628, test code)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("width", [8192, 262144])
+@pytest.mark.parametrize("col_stride", [1, 2])
+@pytest.mark.parametrize("B", [8, 16])
+def test_page_ragged_ends(width, col_stride, B):
+    ends = [0, 1, 1023, 1024, 1025, width - 1, width, width // 2]
+    case = wl.make_custom(len(ends), width, B, 64, 1024, ends, col_stride=col_stride,
+                          seed=width + B + col_stride)
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused()
+    _full_check(dc, bids, tids, scores)
+
+
+def test_page_sentinel_tail_untouched():
+    """Buffer filled with 1.5: every value ties; the tail past end stays 1.5."""
+    import torch
+    W = 262144
+    ends = [0, 1, 1025, W // 2]
+    case = wl.make_custom(len(ends), W, 8, 64, 1024, ends, seed=3)
+    case.buf[:] = np.float32(1.5)
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused()
+    _full_check(dc, bids, tids, scores)
+    buf = dc.buf.cpu().numpy()
+    for r, e in enumerate(ends):
+        assert np.all(buf[r, e:] == np.float32(1.5))
+
+
+def test_graph_replay_tracks_changing_ends():
+    """Capture once at one set of ends, replay with others (wide width)."""
+    import torch
+    W = 262144
+    captured = [1024, 4096, 8192, 2048]
+    replays = [[1, 131072, W, 0], [W, 1025, 3, 65536], [5000, 0, 262143, 70001]]
+    full = wl.make_custom(4, W, 8, 256, 2048, [W] * 4, seed=21, dup_frac=0.01)
+    dc = gh.DevCase(full)
+    dc.ends.copy_(torch.tensor(captured, dtype=torch.int32))
+    ctx = dc.context()
+    bids, tids, scores = dc.outputs()
+    # first call outside the graph
+    ctx.select_fused(dc.logits, dc.starts, dc.ends, bids, tids, scores, True)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ctx.select_fused(dc.logits, dc.starts, dc.ends, bids, tids, scores, True)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for ends in replays:
+            gh.log(f"replay {rep} ends={ends}")
+            dc.restore()
+            dc.ends.copy_(torch.tensor(ends, dtype=torch.int32))
+            scores.view(torch.int32).fill_(gh.SCORE_FILL_BITS)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            case = wl.Case("replay", full.shape, full.buf, None, np.array(ends, np.int32), 21)
+            dcv = gh.DevCase.__new__(gh.DevCase)
+            dcv.case, dcv.sh, dcv.buf, dcv.pristine = case, case.shape, dc.buf, dc.pristine
+            dcv.starts, dcv.ends = None, dc.ends
+            _full_check(dcv, bids, tids, scores)
+    ctx.close()
+
+
+def test_negative_start_is_flagged_and_empty():
+    import torch
+    case = wl.make_custom(3, 1000, 8, 4, 16, [500, 900, 300], starts=[-3, 0, 10], seed=1)
+    dc = gh.DevCase(case)
+    ctx = dc.context()
+    bids, tids, scores = dc.outputs()
+    ctx.select_fused(dc.logits, dc.starts, dc.ends, bids, tids, scores, True)
+    torch.cuda.synchronize()
+    assert ctx.read_status() & 1
+    assert np.all(bids.cpu().numpy()[0] == -1) and np.all(tids.cpu().numpy()[0] == -1)
+    gh.check_rows_against_oracle(dc, [1, 2], bids, tids, scores)
+    ctx.reset_workspace()
+    torch.cuda.synchronize()
+    assert ctx.read_status() == 0
+    ctx.close()
+
+
+def test_empty_shapes_are_noops():
+    import torch
+    for rows, width in ((0, 100), (3, 0)):
+        ctx = binding.Context(rows, width, 8, 4, 4)
+        lg = torch.zeros((rows, width), dtype=torch.float32, device="cuda")
+        e = torch.zeros((max(rows, 1),), dtype=torch.int32, device="cuda")
+        b = torch.zeros((rows, 4), dtype=torch.int32, device="cuda")
+        t = torch.zeros((rows, 4), dtype=torch.int32, device="cuda")
+        ctx.select_fused(lg, None, e, b, t)
+        ctx.close()
+    torch.cuda.synchronize()
+
+
+def test_binding_rejects_mismatched_tensors():
+    import torch
+    ctx = binding.Context(4, 100, 8, 4, 4)
+    lg = torch.zeros((4, 100), dtype=torch.float32, device="cuda")
+    e = torch.zeros((4,), dtype=torch.int32, device="cuda")
+    b = torch.zeros((4, 4), dtype=torch.int32, device="cuda")
+    t = torch.zeros((4, 4), dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        ctx.select_fused(lg.double(), None, e, b, t)
+    with pytest.raises(ValueError):
+        ctx.select_fused(lg, None, e.long(), b, t)
+    with pytest.raises(ValueError):
+        ctx.select_fused(lg[:, :50], None, e, b, t)
+    with pytest.raises(ValueError):
+        ctx.select_fused(lg, None, e, b[:, :2].contiguous(), t)
+    ctx.close()
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size (the launch configuration bench.py times)
+# ---------------------------------------------------------------------------
+
+def _sample_rows(case, n_random=6, seed=0):
+    sh = case.shape
+    L = np.array([oracle.row_bounds(r, case.starts, case.ends, sh.width, sh.starts_repeat,
+                                    sh.ends_repeat)[2] for r in range(sh.rows)])
+    rows = {0, sh.rows - 1, int(L.argmax()), int(L.argmin())}
+    rng = np.random.default_rng(seed)
+    rows.update(int(x) for x in rng.choice(sh.rows, size=min(n_random, sh.rows), replace=False))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["short_decode", "mtp_ragged", "long_decode", "prefill_chunk"])
+def test_full_size_workload(name):
+    gh.log(f"workload {name}: generating")
+    case = wl.make_config(name)
+    dc = gh.DevCase(case)
+    gh.log(f"workload {name}: running")
+    bids, tids, scores = dc.run_fused()
+    gh.log(f"workload {name}: whole-buffer checks")
+    gh.check_whole_buffer(dc)
+    gh.check_invariants_all_rows(dc, bids, tids)
+    rows = _sample_rows(case, n_random=8 if name != "long_decode" else 4)
+    if name == "mtp_ragged":
+        rows = sorted(set(rows) | set(range(16)))   # the edge requests 1023/1024/1025/width
+    gh.log(f"workload {name}: oracle rows {rows}")
+    gh.check_rows_against_oracle(dc, rows, bids, tids, scores)
+
+
+def test_prefill_graph_replay_new_ends():
+    """Prefill-chunk shape: capture once, replay with the +100/+200 end sets."""
+    import torch
+    base = wl.make_config("prefill_chunk")
+    dc = gh.DevCase(base)
+    ctx = dc.context()
+    bids, tids, scores = dc.outputs()
+    ctx.select_fused(dc.logits, dc.starts, dc.ends, bids, tids, scores, True)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ctx.select_fused(dc.logits, dc.starts, dc.ends, bids, tids, scores, True)
+    torch.cuda.synchronize()
+    for off in (100, 200):
+        case = wl.make_config("prefill_chunk", seed_offset=off)
+        gh.log(f"prefill replay seed offset {off}")
+        dc.buf.copy_(torch.from_numpy(case.buf))
+        dc.pristine.copy_(dc.buf)
+        dc.ends.copy_(torch.from_numpy(case.ends))
+        scores.view(torch.int32).fill_(gh.SCORE_FILL_BITS)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        dc.case = case
+        gh.check_whole_buffer(dc)
+        gh.check_invariants_all_rows(dc, bids, tids)
+        gh.check_rows_against_oracle(dc, _sample_rows(case, 6, seed=off), bids, tids, scores)
+    ctx.close()
