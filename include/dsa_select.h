@@ -57,7 +57,11 @@ typedef enum dsa_status {
 } dsa_status;
 
 enum { DSA_TOPK_BLOCKS = 0, DSA_TOPK_TOKENS = 1 };
-enum { DSA_WRITE_MASK = 1u };
+enum {
+  DSA_WRITE_MASK = 1u,    /* dsa_select_fused: write the mask into logits */
+  DSA_TWO_LAUNCHES = 2u   /* dsa_select_fused: run long rows' second pass as a
+                             second launch instead of waiting in the first */
+};
 
 typedef struct dsa_shape {
   int32_t rows;          /* >= 0 */
@@ -145,8 +149,10 @@ int dsa_candidate_mask(dsa_ctx* ctx, float* logits, const int32_t* starts,
  *   block_ids [rows, k_blocks] int32 (relative to s), token_ids [rows,
  *   k_tokens] int32 (absolute), scores (nullable) as dsa_block_scores.
  * flags & DSA_WRITE_MASK: write the mask into logits in place; otherwise
- * logits is only read.  Uses the context workspace (calls on one context must
- * not overlap).
+ * logits is only read.  flags & DSA_TWO_LAUNCHES: for rows too long for one
+ * workgroup, launch the second pass separately instead of having its
+ * workgroups wait (time-bounded) in the same launch; results are identical.
+ * Uses the context workspace (calls on one context must not overlap).
  */
 int dsa_select_fused(dsa_ctx* ctx, float* logits, const int32_t* starts,
                      const int32_t* ends, int32_t* block_ids, int32_t* token_ids,
@@ -155,7 +161,8 @@ int dsa_select_fused(dsa_ctx* ctx, float* logits, const int32_t* starts,
 /*
  * dsa_read_status -- copy the context's device status word to *out after
  * synchronizing the context's device.  Bit 0: a row had start < 0 (treated as
- * empty).  Bit 2: a fused call found its workspace inconsistent, which only a
+ * empty).  Bit 1: a second-pass wait gave up after its time limit (the row's
+ * outputs are then incomplete).  Bit 2: a fused call found its workspace inconsistent, which only a
  * call cut short can leave behind (dsa_reset_workspace clears it).  0 means no
  * contract violation since init or the last reset.
  */

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(PKG, "libdsa_select.so")
 DSA_TOPK_BLOCKS = 0
 DSA_TOPK_TOKENS = 1
 DSA_WRITE_MASK = 1
+DSA_TWO_LAUNCHES = 2
 
 STATUS_NAMES = {
     0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_UNSUPPORTED",
@@ -117,7 +118,7 @@ class Context:
                  starts_repeat: int = 1, ends_repeat: int = 1, device: int = 0):
         lib = load()
         self.shape = Shape(rows, block_size, k_blocks, k_tokens, width,
-                           width * col_stride if row_stride is None else row_stride,
+                           max(1, width * col_stride) if row_stride is None else row_stride,
                            col_stride, starts_repeat, ends_repeat)
         self.device = device
         self.nblocks = -(-width // block_size) if width else 0
@@ -225,7 +226,7 @@ class Context:
                                          _ptr(block_ids), self._stream(stream)))
 
     def select_fused(self, logits, starts, ends, block_ids, token_ids, scores=None,
-                     write_mask: bool = True, stream=None):
+                     write_mask: bool = True, stream=None, two_launches: bool = False):
         import torch
         self._check_logits(logits)
         self._check_bounds(starts, ends)
@@ -236,7 +237,8 @@ class Context:
             raise ValueError("scores must be contiguous float32 [rows, nblocks]")
         _check(load().dsa_select_fused(self.handle, _ptr(logits), _ptr(starts), _ptr(ends),
                                        _ptr(block_ids), _ptr(token_ids), _ptr(scores),
-                                       DSA_WRITE_MASK if write_mask else 0,
+                                       (DSA_WRITE_MASK if write_mask else 0)
+                                       | (DSA_TWO_LAUNCHES if two_launches else 0),
                                        self._stream(stream)))
 
     def read_status(self) -> int:

@@ -29,6 +29,28 @@ DSA_DEV float key2f(uint32_t k) {
 }
 
 // ---------------------------------------------------------------------------
+// Workspace words shared between workgroups of one launch.  Agent-scope
+// relaxed atomics compile to coherent (sc1) loads and stores on gfx950, so no
+// L2 write-back or invalidate is needed; vm_drain() waits until this wave's
+// stores and atomics have completed before a ticket is taken.
+// ---------------------------------------------------------------------------
+DSA_DEV uint32_t ld_shared(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DSA_DEV void st_shared(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DSA_DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+DSA_DEV void store_ninf4(float* p) {   // 16-byte aligned, streaming
+  const f4v v = {__uint_as_float(NEG_INF_BITS), __uint_as_float(NEG_INF_BITS),
+                 __uint_as_float(NEG_INF_BITS), __uint_as_float(NEG_INF_BITS)};
+  __builtin_nontemporal_store(v, reinterpret_cast<f4v*>(p));
+}
+DSA_DEV void store_ninf(float* p) { __builtin_nontemporal_store(__uint_as_float(NEG_INF_BITS), p); }
+
+// ---------------------------------------------------------------------------
 // Wavefront helpers (wave64)
 // ---------------------------------------------------------------------------
 DSA_DEV int lane() { return threadIdx.x & 63; }
@@ -57,42 +79,45 @@ DSA_DEV uint32_t group_max(uint32_t x) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes: row_shr 1/2/4/8 within each row of
+// 16 lanes, then row_bcast 15 and 31 carry row totals into the rows above.
 DSA_DEV uint32_t wave_incl_scan(uint32_t x) {
-  const int l = lane();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d, 64);
-    if (l >= d) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);
   return x;
 }
 
 // ---------------------------------------------------------------------------
-// Shared memory of one workgroup.
+// Shared memory of one workgroup (about 73 KB: two workgroups per CU).
 // ---------------------------------------------------------------------------
 constexpr int HIST_WORDS = 4096;       // 12-bit digit histogram, or a 131072-bit bitmap
-constexpr int KEY_CAP = 2048;          // block keys of a small row / list of the final stage
+constexpr int LIST_CAP = 4096;         // block keys / listed blocks / token columns
 constexpr int SEL_CAP = 2048;          // kept block ids
-constexpr int TK_CAP = 4096;           // token-domain keys
-constexpr int DB_CAP = 2 * KEY_CAP;    // token-domain blocks (aliases keys+ids)
+constexpr int TK_CAP = 4096;           // token keys
+constexpr int DB_CAP = 2 * LIST_CAP;   // token-domain blocks (aliases kid)
 constexpr int BITMAP_BITS = HIST_WORDS * 32;
+constexpr int CHUNK_CAP = LIST_CAP;    // blocks per sub-chunk in the mask pass
 
 struct __align__(16) Smem {
   uint32_t hist[HIST_WORDS];
-  uint32_t kid[2 * KEY_CAP];  // [0, KEY_CAP): keys, [KEY_CAP, 2*KEY_CAP): ids;
-                              // later the token-domain block list (DB_CAP)
+  uint32_t kid[2 * LIST_CAP];   // [0, LIST_CAP): keys, [LIST_CAP, 2*LIST_CAP): ids
   uint32_t sel[SEL_CAP];
   uint32_t tkey[TK_CAP];
-  uint32_t selbits[KEY_CAP / 32];
+  uint32_t bits[CHUNK_CAP / 32];
   uint32_t wv[64];
   uint32_t misc[16];
   DSA_DEV uint32_t* keys() { return kid; }
-  DSA_DEV uint32_t* ids() { return kid + KEY_CAP; }
+  DSA_DEV uint32_t* ids() { return kid + LIST_CAP; }
 };
 
 // Exclusive scan of one value per thread over the workgroup; also the total.
+// The caller must pass a barrier before wv is written again.
 template <int NT>
-DSA_DEV uint32_t wg_excl_scan(uint32_t x, uint32_t* wv, uint32_t& total) {
+DSA_DEV uint32_t wg_excl_scan_once(uint32_t x, uint32_t* wv, uint32_t& total) {
   constexpr int NW = NT / 64;
   const uint32_t inc = wave_incl_scan(x);
   if (lane() == 63) wv[wave()] = inc;
@@ -105,51 +130,72 @@ DSA_DEV uint32_t wg_excl_scan(uint32_t x, uint32_t* wv, uint32_t& total) {
     off += (i < w) ? v : 0u;
     tot += v;
   }
-  __syncthreads();
   total = tot;
   return off + inc - x;
 }
 
-// hist[0..nb): find d with count(bins > d) < krem <= count(bins >= d).
+template <int NT>
+DSA_DEV uint32_t wg_excl_scan(uint32_t x, uint32_t* wv, uint32_t& total) {
+  const uint32_t r = wg_excl_scan_once<NT>(x, wv, total);
+  __syncthreads();
+  return r;
+}
+
+// hist[0..nb) (nb a power of two, 256 <= nb <= 8 * NT): find d with
+// count(bins > d) < krem <= count(bins >= d); also count(bins > d) and hist[d].
+// Each thread holds its bins in registers; two barriers in all.
 template <int NT>
 DSA_DEV void find_bin(const uint32_t* hist, int nb, uint32_t krem, Smem& sm,
-                      uint32_t& d, uint32_t& above) {
+                      uint32_t& d, uint32_t& above, uint32_t& in_bin) {
   const int per = nb >= NT ? nb / NT : 1;
   const int lo = (int)threadIdx.x * per;
-  if (threadIdx.x == 0) {   // defined result even if the counts fall short
-    sm.misc[0] = 0;
-    sm.misc[1] = 0;
-  }
+  uint32_t h[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) h[j] = (j < per && lo + j < nb) ? hist[lo + j] : 0u;
   uint32_t c = 0;
-  if (lo < nb)
-    for (int j = 0; j < per; ++j) c += hist[lo + j];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c += h[j];
+  if (threadIdx.x == 0) {   // defined result even if the counts fall short; written
+    sm.misc[0] = 0;          // before the scan's barrier, so the finder's write wins
+    sm.misc[1] = 0;
+    sm.misc[5] = 0;
+  }
   uint32_t total;
-  const uint32_t excl = wg_excl_scan<NT>(c, sm.wv, total);
-  const uint32_t sfx = total - (excl + c);   // sum over threads above this one
-  if (lo < nb && sfx < krem && krem <= sfx + c) {
-    uint32_t acc = sfx;
-    for (int j = per - 1; j >= 0; --j) {
-      const uint32_t h = hist[lo + j];
-      if (acc + h >= krem) {
-        sm.misc[0] = (uint32_t)(lo + j);
-        sm.misc[1] = acc;
-        break;
+  const uint32_t excl = wg_excl_scan_once<NT>(c, sm.wv, total);
+  const uint32_t sfx = total - (excl + c);   // count in bins above this thread's bins
+  if (sfx < krem && krem <= sfx + c) {
+    uint32_t acc = sfx, dd = (uint32_t)lo, hh = 0;
+    bool done = false;
+#pragma unroll
+    for (int j = 7; j >= 0; --j) {
+      if (!done && j < per) {
+        if (acc + h[j] >= krem) {
+          dd = (uint32_t)(lo + j);
+          hh = h[j];
+          done = true;
+        } else {
+          acc += h[j];
+        }
       }
-      acc += h;
     }
+    sm.misc[0] = dd;
+    sm.misc[1] = acc;
+    sm.misc[5] = hh;
   }
   __syncthreads();
   d = sm.misc[0];
   above = sm.misc[1];
-  __syncthreads();
+  in_bin = sm.misc[5];
 }
 
-// K-th largest key among getk(0..n), 1 <= K <= n: T, and q = the number of
-// elements equal to T that belong to the top K (the lowest-index ones).
-// MSB-first radix select, digits of 12, 12 and 8 bits, LDS histograms.
-template <int NT, class GetKey>
-DSA_DEV void wg_radix_select(int n, uint32_t K, GetKey getk, Smem& sm,
-                             uint32_t& T, uint32_t& q) {
+// Top-K selection rule over getk(0..n), 1 <= K <= n: element i is kept iff
+// key > T, or key == T and it is among the first q such elements in index
+// order.  MSB-first radix select with digits of 12, 12 and 8 bits and LDS
+// histograms; it stops early once the digit bin holding the K-th key is kept
+// whole.  Loads are issued U at a time per thread.
+template <int NT, int U = 8, class GetKey>
+DSA_DEV void wg_radix_select(int n, uint32_t K, GetKey getk, Smem& sm, uint32_t& T,
+                             uint32_t& q) {
   uint32_t prefix = 0, krem = K;
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
@@ -159,40 +205,66 @@ DSA_DEV void wg_radix_select(int n, uint32_t K, GetKey getk, Smem& sm,
     const int hs = shift + bits;
     for (int j = threadIdx.x; j < nb; j += NT) sm.hist[j] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += NT) {
-      const uint32_t k = getk(i);
-      const bool match = (hs >= 32) || ((k >> hs) == (prefix >> hs));
-      if (match) atomicAdd(&sm.hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+    for (int i0 = threadIdx.x; i0 < n; i0 += NT * U) {
+      uint32_t k[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        k[u] = i < n ? getk(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        const bool match = (hs >= 32) || ((k[u] >> hs) == (prefix >> hs));
+        if (i < n && match) atomicAdd(&sm.hist[(k[u] >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
     }
     __syncthreads();
-    uint32_t d, above;
-    find_bin<NT>(sm.hist, nb, krem, sm, d, above);
+    uint32_t d, above, in_bin;
+    find_bin<NT>(sm.hist, nb, krem, sm, d, above, in_bin);
     prefix |= d << shift;
     krem -= above;
+    if (in_bin == krem) {            // the whole bin is kept: keys >= its lowest key
+      if (prefix == 0) {
+        T = 0;
+        q = 0xFFFFFFFFu;
+      } else {
+        T = prefix - 1;
+        q = 0;
+      }
+      return;
+    }
   }
   T = prefix;
   q = krem;
 }
 
-// Ordered pass over [0, n): element i is kept iff key > T, or key == T and it
-// is among the first q such elements in index order.  emit(i, rank, kept,
-// word, base) is called for every i, with rank = kept elements before i,
-// word = the 64-bit kept mask of [base, base + 64).  Returns the kept count.
-// Each wave walks a contiguous segment, so one barrier pair suffices.
+// Ordered pass over [0, n) applying the (T, q) rule above.  emit(i, rank,
+// kept, word, base) is called for every i, with rank = kept elements before
+// i and word = the 64-bit kept mask of [base, base + 64).  Returns the kept
+// count.  Each wave walks one contiguous segment, four 64-groups at a time.
 template <int NT, class GetKey, class Emit>
 DSA_DEV uint32_t wg_select_compact(int n, uint32_t T, uint32_t q, GetKey getk,
                                    Emit emit, Smem& sm) {
   constexpr int NW = NT / 64;
+  constexpr int G = 4;
   const int w = wave(), l = lane();
   const int seg = (((n + NW - 1) / NW) + 63) & ~63;
   const int lo = min(n, w * seg), hi = min(n, lo + seg);
   uint32_t cgt = 0, ceq = 0;
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + l;
-    const bool v = i < hi;
-    const uint32_t k = v ? getk(i) : 0u;
-    cgt += popc(ballot(v && k > T));
-    ceq += popc(ballot(v && k == T));
+  for (int b0 = lo; b0 < hi; b0 += 64 * G) {
+    uint32_t k[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int i = b0 + 64 * g + l;
+      k[g] = i < hi ? getk(i) : 0u;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const bool v = b0 + 64 * g + l < hi;
+      cgt += popc(ballot(v && k[g] > T));
+      ceq += popc(ballot(v && k[g] == T));
+    }
   }
   if (l == 0) {
     sm.wv[w] = cgt;
@@ -212,18 +284,28 @@ DSA_DEV uint32_t wg_select_compact(int n, uint32_t T, uint32_t q, GetKey getk,
     eqb += e;
   }
   __syncthreads();
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + l;
-    const bool v = i < hi;
-    const uint32_t k = v ? getk(i) : 0u;
-    const bool gt = v && k > T;
-    const bool eq = v && k == T;
-    const uint64_t meq = ballot(eq);
-    const bool kept = gt || (eq && (my_eq + mbcnt(meq)) < q);
-    const uint64_t mk = ballot(kept);
-    if (v) emit(i, my_sel + mbcnt(mk), kept, mk, base);
-    my_sel += popc(mk);
-    my_eq += popc(meq);
+  for (int b0 = lo; b0 < hi; b0 += 64 * G) {
+    uint32_t k[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int i = b0 + 64 * g + l;
+      k[g] = i < hi ? getk(i) : 0u;
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int base = b0 + 64 * g;
+      if (base >= hi) break;
+      const int i = base + l;
+      const bool v = i < hi;
+      const bool gt = v && k[g] > T;
+      const bool eq = v && k[g] == T;
+      const uint64_t meq = ballot(eq);
+      const bool kept = gt || (eq && (my_eq + mbcnt(meq)) < q);
+      const uint64_t mk = ballot(kept);
+      if (v) emit(i, my_sel + mbcnt(mk), kept, mk, base);
+      my_sel += popc(mk);
+      my_eq += popc(meq);
+    }
   }
   return selb;
 }

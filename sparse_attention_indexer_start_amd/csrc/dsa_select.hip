@@ -10,16 +10,21 @@
 //                  written at or past e' or before s;
 //   token top-k    the K_tok best columns of the masked row over [s, e').
 //
-// Launch shape: a grid of rows x P workgroups (P from the shape and CU count
-// only), remapped so that a row's workgroups share one XCD.  Trip counts follow
-// each row's live range, so the grid is fixed and the calls replay under HIP
-// graphs.  A row with at most KEY_CAP live blocks is handled end to end by one
-// workgroup from LDS; a longer row is split: pass 1 scores chunks of blocks
-// into the workspace and a 12-bit key-digit histogram; the last workgroup of
-// the row finds the digit holding the K_blk-th score; pass 2 masks every block
-// below that digit and lists the rest, and the last workgroup of pass 2 settles
-// the exact selection among the listed blocks, masks the rejected ones and runs
-// the token top-k.
+// Launch shape: P workgroups per row (P from the shape and CU count only),
+// ordered part-major so that the first workgroup of every row is dispatched
+// first.  Trip counts follow each row's live range, so the grid is fixed and
+// the calls replay under HIP graphs.
+//
+// A row with at most LIST_CAP live blocks is handled end to end by its first
+// workgroup from LDS.  A longer row is split over its P workgroups in two
+// passes of one launch: pass 1 scores a chunk of blocks into the workspace and
+// adds a 12-bit key-digit histogram; the last pass-1 workgroup of the row finds
+// the digit that holds the K_blk-th score and raises the row's ready flag.
+// Pass-2 workgroups (grid indices above every pass-1 workgroup) wait for that
+// flag, mask each block below the digit and list the others; the last of them
+// settles the exact selection among the listed blocks, masks the rejected ones
+// and runs the token top-k.  A pass-2 workgroup waits only for workgroups with
+// lower grid indices, which never wait, and its wait is time-bounded.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -37,8 +42,9 @@ namespace dsa {
 
 constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int UNROLL = 4;      // float4 loads in flight per lane in the score pass
-constexpr int ROW_STATE = 4;   // ticket1, ticket2, digit, spare
+constexpr int ROW_STATE = 4;   // pass-1 ticket, pass-2 ticket, digit, ready flag
 constexpr uint32_t KEPT_FLAG = 0x80000000u;
+constexpr uint64_t WAIT_LIMIT_TICKS = 200000000ull;   // 2 s of the 100 MHz clock
 
 struct Params {
   float* logits;
@@ -51,17 +57,18 @@ struct Params {
   float* scores;
   int64_t width, row_stride, col_stride;
   int32_t rows, B, k_blocks, k_tokens, starts_repeat, ends_repeat;
-  int32_t nblocks, P, G, small_blocks;
+  int32_t nblocks, P, G, small_blocks, phase_base;
   uint32_t flags;
-  uint32_t* ws_key;    // [rows][nblocks]
-  uint32_t* ws_list;   // [rows][nblocks]
-  uint32_t* ws_flat;   // [rows][nblocks]
+  uint32_t* ws_key;    // [rows][nblocks]  block keys of long rows
+  uint32_t* ws_list;   // [rows][nblocks]  listed blocks, per chunk
+  uint32_t* ws_flat;   // [rows][nblocks]  listed blocks, gathered (overflow)
   uint32_t* ws_hist;   // [rows][HIST_WORDS]
   uint32_t* ws_cnt;    // [rows][P]
   uint32_t* ws_row;    // [rows][ROW_STATE]
-  uint32_t* ws_sel;    // [rows][k_blocks]
-  uint32_t* ws_dblk;   // [rows][dblk_cap]
-  uint32_t* ws_tkey;   // [rows][tkey_cap]
+  uint32_t* ws_sel;    // [rows][k_blocks]   (overflow)
+  uint32_t* ws_dblk;   // [rows][dblk_cap]   (overflow)
+  uint32_t* ws_tkey;   // [rows][tkey_cap]   (overflow)
+  uint32_t* ws_tcol;   // [rows][tkey_cap]   (overflow)
   int64_t dblk_cap, tkey_cap;
   uint32_t* status;
 };
@@ -93,17 +100,10 @@ DSA_DEV bool vec_ok(const Params& p, const float* rowp) {
   return p.col_stride == 1 && ((reinterpret_cast<uintptr_t>(rowp) & 15u) == 0);
 }
 
-// Grid index -> (row, part).  gridDim.x is a multiple of 8; hardware places
-// workgroup g on XCD g % 8, so consecutive logical groups (one row) share an
-// XCD and its L2.
-DSA_DEV bool map_group(const Params& p, int& r, int& part) {
-  const int g = blockIdx.x;
-  const int per = gridDim.x >> 3;
-  const int logical = (g & 7) * per + (g >> 3);
-  if (logical >= p.G) return false;
-  r = logical / p.P;
-  part = logical - r * p.P;
-  return true;
+// Grid index -> (row, part), part-major: every row's part 0 comes first.
+DSA_DEV void part_of(const Params& p, int g, int& r, int& part) {
+  part = g / p.rows;
+  r = g - part * p.rows;
 }
 
 DSA_DEV void chunk_of(const Row& rb, int P, int part, int& b0, int& b1) {
@@ -116,6 +116,25 @@ template <int BS>
 DSA_DEV int div_b(int64_t x, int B) {
   if constexpr (BS > 0) return (int)(x / BS);
   else return (int)(x / B);
+}
+
+// Max key over columns [c, c + n) of a block (n <= B), loads issued together.
+template <int BS>
+DSA_DEV uint32_t block_max_key(const float* rowp, int64_t cs, bool vec, int64_t c, int n) {
+  uint32_t m = 0;
+  if constexpr (BS >= 4) {
+    if (vec && n == BS) {
+      f4v v[BS / 4];
+#pragma unroll
+      for (int j = 0; j < BS / 4; ++j) v[j] = *reinterpret_cast<const f4v*>(rowp + c + 4 * j);
+#pragma unroll
+      for (int j = 0; j < BS / 4; ++j)
+        m = max(m, max(max(f2key(v[j].x), f2key(v[j].y)), max(f2key(v[j].z), f2key(v[j].w))));
+      return m;
+    }
+  }
+  for (int j = 0; j < n; ++j) m = max(m, f2key(rowp[(c + j) * cs]));
+  return m;
 }
 
 // ---------------------------------------------------------------------------
@@ -131,23 +150,34 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
     const int64_t t4 = (int64_t)threadIdx.x * 4;
     const int64_t step = (int64_t)NT * 4 * UNROLL;
     const bool leader = (threadIdx.x % G) == 0;
-    int64_t c0 = cbeg;
-    for (; c0 + step <= cend; c0 += step) {
+    for (int64_t c0 = cbeg; c0 < cend; c0 += step) {
       uint32_t k[UNROLL];
       if (vec) {
-        float4 v[UNROLL];
+        f4v v[UNROLL];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-          v[u] = *reinterpret_cast<const float4*>(rowp + c0 + (int64_t)u * NT * 4 + t4);
+        for (int u = 0; u < UNROLL; ++u) {
+          const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
+          if (col + 4 <= cend) {
+            v[u] = *reinterpret_cast<const f4v*>(rowp + col);
+          } else {
+            const float z = __uint_as_float(0xFFFFFFFFu);    // key 0: below every float
+            v[u] = f4v{z, z, z, z};
+            for (int j = 0; j < 4; ++j)
+              if (col + j < cend) v[u][j] = rowp[col + j];
+          }
+        }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
           k[u] = max(max(f2key(v[u].x), f2key(v[u].y)), max(f2key(v[u].z), f2key(v[u].w)));
       } else {
         float v[UNROLL][4];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+        for (int u = 0; u < UNROLL; ++u) {
+          const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v[u][j] = rowp[(c0 + (int64_t)u * NT * 4 + t4 + j) * cs];
+          for (int j = 0; j < 4; ++j)
+            v[u][j] = (col + j < cend) ? rowp[(col + j) * cs] : __uint_as_float(0xFFFFFFFFu);
+        }
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
           k[u] = max(max(f2key(v[u][0]), f2key(v[u][1])), max(f2key(v[u][2]), f2key(v[u][3])));
@@ -155,48 +185,44 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
         const uint32_t m = group_max<G>(k[u]);
-        if (leader) {
-          const int b = (int)((c0 + (int64_t)u * NT * 4 + t4) / BS);
+        const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
+        if (leader && col < cend) {
+          const int b = (int)(col / BS);
           emit(b, b == nlb - 1 ? KEY_POS_INF : m);
         }
-      }
-    }
-    for (; c0 < cend; c0 += (int64_t)NT * 4) {
-      const int64_t col = c0 + t4;
-      uint32_t m = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (col + j < cend) m = max(m, f2key(rowp[(col + j) * cs]));
-      m = group_max<G>(m);
-      if (leader && col < cend) {
-        const int b = (int)(col / BS);
-        emit(b, b == nlb - 1 ? KEY_POS_INF : m);
       }
     }
   } else if constexpr (BS == 1 || BS == 2) {
     const int64_t cbeg = (int64_t)b0 * BS;
     const int64_t cend = min((int64_t)b1 * BS, (int64_t)L);
-    for (int64_t col = cbeg + (int64_t)threadIdx.x * 4; col < cend; col += (int64_t)NT * 4) {
-      uint32_t k[4];
+    for (int64_t c0 = cbeg + (int64_t)threadIdx.x * 4; c0 < cend; c0 += (int64_t)NT * 4 * UNROLL) {
+      uint32_t k[UNROLL][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) k[j] = (col + j < cend) ? f2key(rowp[(col + j) * cs]) : 0u;
+      for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; j += BS) {
-        if (col + j < cend) {
-          uint32_t m = k[j];
-          if constexpr (BS == 2) m = max(m, k[j + 1]);
-          const int b = (int)((col + j) / BS);
-          emit(b, b == nlb - 1 ? KEY_POS_INF : m);
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = c0 + (int64_t)u * NT * 4 + j;
+          k[u][j] = col < cend ? f2key(rowp[col * cs]) : 0u;
         }
-      }
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; j += BS) {
+          const int64_t col = c0 + (int64_t)u * NT * 4 + j;
+          if (col < cend) {
+            uint32_t m = k[u][j];
+            if constexpr (BS == 2) m = max(m, k[u][j + 1]);
+            const int b = (int)(col / BS);
+            emit(b, b == nlb - 1 ? KEY_POS_INF : m);
+          }
+        }
     }
   } else {
     // Any block size: one lane per block.
     for (int b = b0 + (int)threadIdx.x; b < b1; b += NT) {
       const int64_t c0 = (int64_t)b * B;
-      const int64_t c1 = min(c0 + B, (int64_t)L);
-      uint32_t m = 0;
-      for (int64_t c = c0; c < c1; ++c) m = max(m, f2key(rowp[c * cs]));
+      const int n = (int)min((int64_t)B, (int64_t)L - c0);
+      const uint32_t m = block_max_key<0>(rowp, cs, false, c0, n);
       emit(b, b == nlb - 1 ? KEY_POS_INF : m);
     }
   }
@@ -208,39 +234,111 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
 template <int BS, class IsMasked>
 DSA_DEV void mask_blocks(float* rowp, int64_t cs, int B, int L, int b0, int b1, bool vec,
                          IsMasked masked) {
-  const float ninf = __uint_as_float(NEG_INF_BITS);
   const int64_t cbeg = (int64_t)b0 * B;
   const int64_t cend = min((int64_t)b1 * B, (int64_t)L);
   if constexpr (BS >= 4) {
     for (int64_t col = cbeg + (int64_t)threadIdx.x * 4; col < cend; col += (int64_t)NT * 4) {
       if (!masked((int)(col / BS))) continue;
       if (vec && col + 4 <= cend) {
-        *reinterpret_cast<float4*>(rowp + col) = make_float4(ninf, ninf, ninf, ninf);
+        store_ninf4(rowp + col);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (col + j < cend) rowp[(col + j) * cs] = ninf;
+          if (col + j < cend) store_ninf(rowp + (col + j) * cs);
       }
     }
   } else {
     for (int64_t col = cbeg + (int64_t)threadIdx.x; col < cend; col += NT)
-      if (masked(div_b<BS>(col, B))) rowp[col * cs] = ninf;
+      if (masked(div_b<BS>(col, B))) store_ninf(rowp + col * cs);
+  }
+}
+
+// -inf over one whole block (called by one lane).
+DSA_DEV void mask_one_block(float* rowp, int64_t cs, int B, int L, uint32_t b) {
+  const int64_t c0 = (int64_t)b * B;
+  const int64_t c1 = min(c0 + B, (int64_t)L);
+  for (int64_t c = c0; c < c1; ++c) store_ninf(rowp + c * cs);
+}
+
+DSA_DEV void write_empty_row(const Params& p, int r) {
+  if (p.block_ids)
+    for (int i = threadIdx.x; i < p.k_blocks; i += NT) p.block_ids[(int64_t)r * p.k_blocks + i] = -1;
+  if (p.token_ids)
+    for (int i = threadIdx.x; i < p.k_tokens; i += NT) p.token_ids[(int64_t)r * p.k_tokens + i] = -1;
+}
+
+// Visit the live columns of kept blocks sel[j0..j1) in column order:
+// visit(column, key).  Loads of GB blocks are issued together.
+template <int BS, class Visit>
+DSA_DEV void gather_kept(const float* rowp, int64_t cs, int B, int L, bool vec,
+                         const uint32_t* sel, int j0, int j1, Visit visit) {
+  if constexpr (BS >= 4) {
+    constexpr int GB = (BS / 4) >= 8 ? 1 : 8 / (BS / 4);
+    for (int j = j0; j < j1; j += GB) {
+      uint32_t kk[GB][BS];
+      int64_t c0s[GB];
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        c0s[g] = -1;
+#pragma unroll
+        for (int e = 0; e < BS; ++e) kk[g][e] = 0u;
+        if (j + g < j1) {
+          const int64_t c0 = (int64_t)sel[j + g] * BS;
+          const int n = (int)min((int64_t)BS, (int64_t)L - c0);
+          c0s[g] = c0;
+          if (vec && n == BS) {
+#pragma unroll
+            for (int t = 0; t < BS / 4; ++t) {
+              const f4v v = *reinterpret_cast<const f4v*>(rowp + c0 + 4 * t);
+              kk[g][4 * t + 0] = f2key(v.x);
+              kk[g][4 * t + 1] = f2key(v.y);
+              kk[g][4 * t + 2] = f2key(v.z);
+              kk[g][4 * t + 3] = f2key(v.w);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < BS; ++e)
+              if (e < n) kk[g][e] = f2key(rowp[(c0 + e) * cs]);
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        if (c0s[g] < 0) continue;
+        const int n = (int)min((int64_t)BS, (int64_t)L - c0s[g]);
+#pragma unroll
+        for (int e = 0; e < BS; ++e)
+          if (e < n) visit(c0s[g] + e, kk[g][e]);
+      }
+    }
+  } else {
+    for (int j = j0; j < j1; ++j) {
+      const int64_t c0 = (int64_t)sel[j] * B;
+      const int n = (int)min((int64_t)B, (int64_t)L - c0);
+      for (int e = 0; e < n; ++e) visit(c0 + e, f2key(rowp[(c0 + e) * cs]));
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Token top-k of one row (one workgroup).  sel: ascending kept block ids (Kp of
-// them); nullptr means the row is ranked as it stands.  The ranked domain is
-// every kept block plus the F = ceil(Kt/B) lowest non-kept blocks, in block
-// order: a non-kept column ranks as -inf, and no -inf column beyond the first
-// Kt of them can enter the top Kt, so the result equals ranking the whole
-// masked row.
+// Token top-k of one row (one workgroup).
+//   sel     ascending kept block ids (Kp of them); nullptr: rank the row as is.
+//   tlo     a key no larger than the largest value of any kept block other
+//           than the newest (0 when unknown).
+// When the kept blocks hold at least Kt columns at or above some bound beta
+// (beta = tlo if enough columns reach it, else the smallest finite key), every
+// one of the Kt best columns reaches beta, so only kept columns >= beta are
+// ranked.  Otherwise the ranked domain is every kept block plus the
+// F = ceil(Kt/B) lowest non-kept blocks in block order: a non-kept column ranks
+// as -inf and no -inf column beyond the first Kt of them can enter the top Kt.
+// Either way the result equals ranking the whole masked row.
 // ---------------------------------------------------------------------------
 template <int BS>
 DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* rowp,
-                         const uint32_t* sel, int Kp, Smem& sm) {
+                         const uint32_t* sel, int Kp, uint32_t tlo, Smem& sm) {
   const int L = rb.L, nlb = rb.nlb, B = p.B;
   const int64_t cs = p.col_stride;
+  const bool vec = vec_ok(p, rowp);
   const int Kt = min(p.k_tokens, L);
   int32_t* tout = p.token_ids + (int64_t)r * p.k_tokens;
   if (L <= p.k_tokens) {
@@ -258,6 +356,48 @@ DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* row
     for (int i = Kt + threadIdx.x; i < p.k_tokens; i += NT) tout[i] = -1;
     return;
   }
+
+  if ((int64_t)Kp * B >= Kt) {
+    // ---- pre-filtered kept columns (thread-contiguous kept blocks) ----
+    const int bpt = (Kp + NT - 1) / NT;
+    const int j0 = min(Kp, (int)threadIdx.x * bpt), j1 = min(Kp, j0 + bpt);
+    uint32_t ca = 0, cf = 0;
+    gather_kept<BS>(rowp, cs, B, L, vec, sel, j0, j1, [&](int64_t, uint32_t k) {
+      ca += k >= tlo;
+      cf += k > KEY_NEG_INF;
+    });
+    uint32_t ta, tf;
+    const uint32_t oa = wg_excl_scan<NT>(ca, sm.wv, ta);
+    const uint32_t of = wg_excl_scan<NT>(cf, sm.wv, tf);
+    const bool use_a = tlo > KEY_NEG_INF && ta >= (uint32_t)Kt;
+    if (use_a || tf >= (uint32_t)Kt) {
+      const uint32_t bound = use_a ? tlo : KEY_NEG_INF + 1u;
+      const uint32_t m = use_a ? ta : tf;
+      uint32_t off = use_a ? oa : of;
+      const bool lds = m <= (uint32_t)TK_CAP;
+      uint32_t* fkey = lds ? sm.tkey : p.ws_tkey + (int64_t)r * p.tkey_cap;
+      uint32_t* fcol = lds ? sm.kid : p.ws_tcol + (int64_t)r * p.tkey_cap;
+      gather_kept<BS>(rowp, cs, B, L, vec, sel, j0, j1, [&](int64_t c, uint32_t k) {
+        if (k >= bound) {
+          fkey[off] = k;
+          fcol[off] = (uint32_t)c;
+          ++off;
+        }
+      });
+      __syncthreads();
+      uint32_t T = 0, q = 0xFFFFFFFFu;
+      auto getk = [&](int i) { return fkey[i]; };
+      if ((int)m > Kt) wg_radix_select<NT>((int)m, (uint32_t)Kt, getk, sm, T, q);
+      wg_select_compact<NT>((int)m, T, q, getk,
+          [&](int i, uint32_t rank, bool kept, uint64_t, int) {
+            if (kept) tout[rank] = (int32_t)(rb.s + fcol[i]);
+          }, sm);
+      for (int i = Kt + threadIdx.x; i < p.k_tokens; i += NT) tout[i] = -1;
+      return;
+    }
+  }
+
+  // ---- kept blocks plus the lowest F non-kept blocks ----
   const int F = (Kt + B - 1) / B;
   const int nlow = min(nlb, Kp + F);
   uint32_t* lowbits = sm.hist;
@@ -270,13 +410,11 @@ DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* row
   __syncthreads();
   const bool db_lds = (nlow + Kp) <= DB_CAP;
   uint32_t* dblk = db_lds ? sm.kid : p.ws_dblk + (int64_t)r * p.dblk_cap;
-  // Part 1: blocks below nlow, kept ones and the first F others.
   auto lowkey = [&](int b) -> uint32_t { return ((lowbits[b >> 5] >> (b & 31)) & 1u) ? 2u : 1u; };
   const uint32_t n1 = wg_select_compact<NT>(nlow, 1u, (uint32_t)F, lowkey,
       [&](int b, uint32_t rank, bool kept, uint64_t, int) {
         if (kept) dblk[rank] = (uint32_t)b | (lowkey(b) == 2u ? KEPT_FLAG : 0u);
       }, sm);
-  // Part 2: kept blocks at or above nlow, in order.
   const uint32_t n2 = wg_compact<NT>(Kp, [&](int j) { return sel[j] >= (uint32_t)nlow; },
       [&](int j, uint32_t rank) { dblk[n1 + rank] = sel[j] | KEPT_FLAG; }, sm);
   __syncthreads();
@@ -284,16 +422,42 @@ DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* row
   const int last = (int)(dblk[nd - 1] & ~KEPT_FLAG);
   const int nc = (nd - 1) * B + min(B, L - last * B);
   uint32_t* tkey = nc <= TK_CAP ? sm.tkey : p.ws_tkey + (int64_t)r * p.tkey_cap;
-  for (int i = threadIdx.x; i < nc; i += NT) {
-    const int d = div_b<BS>(i, B);
-    const uint32_t e = dblk[d];
-    const int64_t c = (int64_t)(e & ~KEPT_FLAG) * B + (i - d * B);
-    tkey[i] = ((e & KEPT_FLAG) && c < L) ? f2key(rowp[c * cs]) : KEY_NEG_INF;
+  constexpr int U = 8;
+  uint32_t cgt = 0, cge = 0;
+  for (int i0 = threadIdx.x; i0 < nc; i0 += NT * U) {
+    uint32_t k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * NT;
+      k[u] = KEY_NEG_INF;
+      if (i < nc) {
+        const int d = div_b<BS>(i, B);
+        const uint32_t e = dblk[d];
+        const int64_t c = (int64_t)(e & ~KEPT_FLAG) * B + (i - d * B);
+        if ((e & KEPT_FLAG) && c < L) k[u] = f2key(rowp[c * cs]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i0 + u * NT < nc) {
+        tkey[i0 + u * NT] = k[u];
+        cgt += k[u] > KEY_NEG_INF;
+        cge += k[u] >= KEY_NEG_INF;
+      }
+    }
   }
-  __syncthreads();
+  uint32_t tgt, tge;
+  (void)wg_excl_scan<NT>(cgt, sm.wv, tgt);
+  (void)wg_excl_scan<NT>(cge, sm.wv, tge);
   uint32_t T = 0, q = 0xFFFFFFFFu;
   auto getk = [&](int i) { return tkey[i]; };
-  if (nc > Kt) wg_radix_select<NT>(nc, (uint32_t)Kt, getk, sm, T, q);
+  if (tgt <= (uint32_t)Kt && (uint32_t)Kt <= tge) {
+    // All columns above -inf, then the lowest-index -inf columns.
+    T = KEY_NEG_INF;
+    q = (uint32_t)Kt - tgt;
+  } else if (nc > Kt) {
+    wg_radix_select<NT>(nc, (uint32_t)Kt, getk, sm, T, q);
+  }
   wg_select_compact<NT>(nc, T, q, getk,
       [&](int i, uint32_t rank, bool kept, uint64_t, int) {
         if (kept) {
@@ -304,15 +468,8 @@ DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* row
   for (int i = Kt + threadIdx.x; i < p.k_tokens; i += NT) tout[i] = -1;
 }
 
-DSA_DEV void write_empty_row(const Params& p, int r) {
-  if (p.block_ids)
-    for (int i = threadIdx.x; i < p.k_blocks; i += NT) p.block_ids[(int64_t)r * p.k_blocks + i] = -1;
-  if (p.token_ids)
-    for (int i = threadIdx.x; i < p.k_tokens; i += NT) p.token_ids[(int64_t)r * p.k_tokens + i] = -1;
-}
-
 // ---------------------------------------------------------------------------
-// A row with nlb <= KEY_CAP: the whole chain in one workgroup, keys in LDS.
+// A row with nlb <= LIST_CAP: the whole chain in one workgroup, keys in LDS.
 // ---------------------------------------------------------------------------
 template <int BS>
 DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
@@ -323,19 +480,20 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
   int32_t* bout = p.block_ids + (int64_t)r * p.k_blocks;
   uint32_t* sel = Kp <= SEL_CAP ? sm.sel : p.ws_sel + (int64_t)r * p.k_blocks;
   const bool need_keys = nlb > p.k_blocks || p.scores != nullptr;
+  uint32_t T = 0, q = 0xFFFFFFFFu;
   if (!need_keys) {
     // Every live block is kept; the result follows from the bounds.
     for (int i = threadIdx.x; i < p.k_blocks; i += NT) bout[i] = i < nlb ? i : -1;
     for (int i = threadIdx.x; i < nlb; i += NT) sel[i] = (uint32_t)i;
   } else {
     float* sc = p.scores ? p.scores + (int64_t)r * p.nblocks : nullptr;
+    uint32_t* keys = sm.keys();
     score_blocks<BS>(rowp, p.col_stride, B, L, 0, nlb, nlb, vec, [&](int b, uint32_t k) {
-      sm.keys()[b] = k;
+      keys[b] = k;
       if (sc) sc[b] = key2f(k);
     });
     __syncthreads();
-    uint32_t T = 0, q = 0xFFFFFFFFu;
-    auto getk = [&](int i) { return sm.keys()[i]; };
+    auto getk = [&](int i) { return keys[i]; };
     if (nlb > Kp) wg_radix_select<NT>(nlb, (uint32_t)Kp, getk, sm, T, q);
     wg_select_compact<NT>(nlb, T, q, getk,
         [&](int i, uint32_t rank, bool kept, uint64_t word, int base) {
@@ -344,53 +502,36 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
             sel[rank] = (uint32_t)i;
           }
           if (i == base) {
-            sm.selbits[base >> 5] = (uint32_t)word;
-            sm.selbits[(base >> 5) + 1] = (uint32_t)(word >> 32);
+            sm.bits[base >> 5] = (uint32_t)word;
+            sm.bits[(base >> 5) + 1] = (uint32_t)(word >> 32);
           }
         }, sm);
     for (int i = Kp + threadIdx.x; i < p.k_blocks; i += NT) bout[i] = -1;
     __syncthreads();
     if ((p.flags & DSA_WRITE_MASK) && nlb > Kp)
       mask_blocks<BS>(rowp, p.col_stride, B, L, 0, nlb, vec,
-                      [&](int b) { return ((sm.selbits[b >> 5] >> (b & 31)) & 1u) == 0u; });
+                      [&](int b) { return ((sm.bits[b >> 5] >> (b & 31)) & 1u) == 0u; });
   }
   __syncthreads();
-  token_stage<BS>(p, r, rb, rowp, sel, Kp, sm);
+  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, sm);
 }
 
-// Workgroup-wide ticket: returns true in the last of `total` arrivals.  Every
-// thread fences its own global writes before the barrier; after a true return
-// every thread has acquired the other workgroups' writes.
+// Workgroup-wide ticket on a workspace counter: true in the last of `total`
+// arrivals.  Each wave first drains its own stores and atomics.
 DSA_DEV bool arrive_last(uint32_t* ticket, uint32_t total, Smem& sm) {
-  __threadfence();
+  vm_drain();
   __syncthreads();
   if (threadIdx.x == 0) sm.misc[2] = atomicAdd(ticket, 1u);
   __syncthreads();
-  const bool last = sm.misc[2] == total - 1;
-  if (last) __threadfence();
-  return last;
+  return sm.misc[2] == total - 1;
 }
 
 // ---------------------------------------------------------------------------
-// Fused pass 1: small rows end to end; long rows: chunk scores + histogram,
-// and the last workgroup of the row finds the digit of the K_blk-th score.
+// Pass 1 of a long row: scores of one chunk, digit histogram, and in the last
+// workgroup of the row the digit of the K_blk-th score.
 // ---------------------------------------------------------------------------
 template <int BS>
-__global__ __launch_bounds__(NT) void k_fused_p1(Params p) {
-  __shared__ Smem sm;
-  int r, part;
-  if (!map_group(p, r, part)) return;
-  const Row rb = row_bounds(p, r);
-  if (rb.nlb <= p.small_blocks) {
-    if (part != 0) return;
-    if (rb.bad && threadIdx.x == 0) atomicOr(p.status, 1u);
-    if (rb.L == 0) {
-      write_empty_row(p, r);
-      return;
-    }
-    small_row<BS>(p, r, rb, sm);
-    return;
-  }
+DSA_DEV void long_pass1(const Params& p, int r, int part, const Row& rb, Smem& sm) {
   float* rowp = row_ptr(p, r, rb);
   const bool vec = vec_ok(p, rowp);
   int b0, b1;
@@ -400,7 +541,7 @@ __global__ __launch_bounds__(NT) void k_fused_p1(Params p) {
   uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   float* sc = p.scores ? p.scores + (int64_t)r * p.nblocks : nullptr;
   score_blocks<BS>(rowp, p.col_stride, p.B, rb.L, b0, b1, rb.nlb, vec, [&](int b, uint32_t k) {
-    wk[b] = k;
+    st_shared(&wk[b], k);
     if (sc) sc[b] = key2f(k);
     atomicAdd(&sm.hist[k >> 20], 1u);
   });
@@ -412,22 +553,29 @@ __global__ __launch_bounds__(NT) void k_fused_p1(Params p) {
   }
   uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
   if (!arrive_last(&st[0], (uint32_t)p.P, sm)) return;
-  for (int j = threadIdx.x; j < HIST_WORDS; j += NT) {
-    sm.hist[j] = gh[j];
-    gh[j] = 0;                        // clean for the next call
+  constexpr int PER = HIST_WORDS / NT;
+  uint32_t h[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) h[u] = ld_shared(&gh[threadIdx.x + u * NT]);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    sm.hist[threadIdx.x + u * NT] = h[u];
+    if (h[u]) st_shared(&gh[threadIdx.x + u * NT], 0u);   // clean for the next call
   }
   __syncthreads();
-  uint32_t d, above;
-  find_bin<NT>(sm.hist, HIST_WORDS, (uint32_t)min(p.k_blocks, rb.nlb), sm, d, above);
+  uint32_t d, above, in_bin;
+  find_bin<NT>(sm.hist, HIST_WORDS, (uint32_t)min(p.k_blocks, rb.nlb), sm, d, above, in_bin);
   if (threadIdx.x == 0) {
-    st[2] = d;
-    st[0] = 0;                        // reset the ticket for the next call
+    st_shared(&st[2], d);
+    st_shared(&st[0], 0u);
+    vm_drain();
+    st_shared(&st[3], 1u);            // the row's digit is ready
   }
 }
 
 // ---------------------------------------------------------------------------
-// Fused pass 2 (long rows): mask blocks below the digit, list the others; the
-// last workgroup of the row finishes the row.
+// Last workgroup of pass 2: exact selection among the listed blocks, masks of
+// the rejected ones, outputs, token top-k.
 // ---------------------------------------------------------------------------
 template <int BS>
 DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
@@ -435,28 +583,61 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
   const int nlb = rb.nlb, B = p.B, P = p.P;
   const int64_t cs = p.col_stride;
   const int cb = (nlb + P - 1) / P;
-  const uint32_t* cnt = p.ws_cnt + (int64_t)r * P;
   const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   const uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
   // Exclusive prefix of the per-chunk list lengths (P <= NT).
-  const uint32_t c = (int)threadIdx.x < P ? cnt[threadIdx.x] : 0u;
+  const uint32_t c = (int)threadIdx.x < P ? ld_shared(&p.ws_cnt[(int64_t)r * P + threadIdx.x]) : 0u;
   uint32_t n_list;
   const uint32_t off = wg_excl_scan<NT>(c, sm.wv, n_list);
-  if ((int)threadIdx.x < P) sm.hist[threadIdx.x] = off;
+  if ((int)threadIdx.x < P) {
+    sm.hist[threadIdx.x] = off;
+    sm.hist[NT + threadIdx.x] = c;
+  }
   __syncthreads();
-  const bool in_lds = n_list <= (uint32_t)KEY_CAP;
+  const bool in_lds = n_list <= (uint32_t)LIST_CAP;
   uint32_t* lid = in_lds ? sm.ids() : p.ws_flat + (int64_t)r * p.nblocks;
-  for (int t = 0; t < P; ++t) {
-    const uint32_t ct = cnt[t], ot = sm.hist[t];
-    const int b0 = min(nlb, t * cb);
-    for (int j = threadIdx.x; j < (int)ct; j += NT) lid[ot + j] = wl[b0 + j];
+  {
+    // Gather the per-chunk lists into one ascending list; entry i belongs to
+    // the last chunk whose offset is <= i (binary search over P offsets).
+    constexpr int U = 8;
+    for (int i0 = threadIdx.x; i0 < (int)n_list; i0 += NT * U) {
+      uint32_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        v[u] = 0;
+        if (i < (int)n_list) {
+          int lo = 0, hi = P - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sm.hist[mid] <= (uint32_t)i) lo = mid;
+            else hi = mid - 1;
+          }
+          v[u] = ld_shared(&wl[min(nlb, lo * cb) + (i - (int)sm.hist[lo])]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + u * NT < (int)n_list) lid[i0 + u * NT] = v[u];
+    }
   }
   __syncthreads();
   if (in_lds) {
-    for (int i = threadIdx.x; i < (int)n_list; i += NT) sm.keys()[i] = wk[lid[i]];
+    constexpr int U = 8;
+    for (int i0 = threadIdx.x; i0 < (int)n_list; i0 += NT * U) {
+      uint32_t k[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        k[u] = i < (int)n_list ? ld_shared(&wk[lid[i]]) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + u * NT < (int)n_list) sm.keys()[i0 + u * NT] = k[u];
+    }
     __syncthreads();
   }
-  auto getk = [&](int i) { return in_lds ? sm.keys()[i] : wk[lid[i]]; };
+  auto getk = [&](int i) { return in_lds ? sm.keys()[i] : ld_shared(&wk[lid[i]]); };
   int Kp = min(p.k_blocks, nlb);
   if ((int)n_list < Kp) {
     // Only after a call was cut short (stale workspace): keep the list.
@@ -468,7 +649,6 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
   int32_t* bout = p.block_ids + (int64_t)r * p.k_blocks;
   uint32_t* sel = Kp <= SEL_CAP ? sm.sel : p.ws_sel + (int64_t)r * p.k_blocks;
   const bool write_mask = (p.flags & DSA_WRITE_MASK) != 0;
-  const float ninf = __uint_as_float(NEG_INF_BITS);
   wg_select_compact<NT>((int)n_list, T, q, getk,
       [&](int i, uint32_t rank, bool kept, uint64_t, int) {
         const uint32_t b = lid[i];
@@ -476,40 +656,119 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
           bout[rank] = (int32_t)b;
           sel[rank] = b;
         } else if (write_mask) {
-          const int64_t c0 = (int64_t)b * B;
-          const int64_t c1 = min(c0 + B, (int64_t)rb.L);
-          for (int64_t col = c0; col < c1; ++col) rowp[col * cs] = ninf;
+          mask_one_block(rowp, cs, B, rb.L, b);
         }
       }, sm);
   for (int i = Kp + threadIdx.x; i < p.k_blocks; i += NT) bout[i] = -1;
   __syncthreads();
-  token_stage<BS>(p, r, rb, rowp, sel, Kp, sm);
+  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, sm);
 }
 
+// Thread 0 waits (time-bounded) for the row's ready flag.  Returns false if
+// the wait gave up (status bit 1).
+DSA_DEV bool wait_ready(const Params& p, const uint32_t* flag, Smem& sm) {
+  if (threadIdx.x == 0) {
+    uint32_t ok = 1;
+    if (ld_shared(flag) == 0u) {
+      const uint64_t t0 = wall_clock64();
+      while (ld_shared(flag) == 0u) {
+        __builtin_amdgcn_s_sleep(2);
+        if (wall_clock64() - t0 > WAIT_LIMIT_TICKS) {
+          atomicOr(p.status, 2u);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    sm.misc[3] = ok;
+  }
+  __syncthreads();
+  return sm.misc[3] != 0u;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2 of a long row: mask blocks below the digit, list the others; the
+// last workgroup of the row finishes it.
+// ---------------------------------------------------------------------------
 template <int BS>
-__global__ __launch_bounds__(NT) void k_fused_p2(Params p) {
-  __shared__ Smem sm;
-  int r, part;
-  if (!map_group(p, r, part)) return;
-  const Row rb = row_bounds(p, r);
-  if (rb.nlb <= p.small_blocks) return;
+DSA_DEV void long_pass2(const Params& p, int r, int part, const Row& rb, Smem& sm) {
+  uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
+  if (!wait_ready(p, &st[3], sm)) return;
   float* rowp = row_ptr(p, r, rb);
   const bool vec = vec_ok(p, rowp);
   int b0, b1;
   chunk_of(rb, p.P, part, b0, b1);
-  uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
-  const uint32_t digit = st[2];
+  const uint32_t digit = ld_shared(&st[2]);
   const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
-  const uint32_t n = wg_compact<NT>(b1 - b0, [&](int i) { return (wk[b0 + i] >> 20) >= digit; },
-                                    [&](int i, uint32_t rank) { wl[b0 + rank] = (uint32_t)(b0 + i); }, sm);
-  if (threadIdx.x == 0) p.ws_cnt[(int64_t)r * p.P + part] = n;
-  if (p.flags & DSA_WRITE_MASK)
-    mask_blocks<BS>(rowp, p.col_stride, p.B, rb.L, b0, b1, vec,
-                    [&](int b) { return (wk[b] >> 20) < digit; });
+  uint32_t* keys = sm.keys();
+  uint32_t cnt = 0;
+  for (int s0 = b0; s0 < b1; s0 += CHUNK_CAP) {
+    const int n = min(b1 - s0, CHUNK_CAP);
+    constexpr int U = CHUNK_CAP / NT;
+    uint32_t k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = (int)threadIdx.x + u * NT;
+      k[u] = i < n ? ld_shared(&wk[s0 + i]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) keys[threadIdx.x + u * NT] = k[u];
+    __syncthreads();
+    for (int w = threadIdx.x; w < (n + 31) / 32; w += NT) {
+      uint32_t word = 0;
+      for (int j = 0; j < 32; ++j) {
+        const int i = w * 32 + j;
+        if (i < n && (keys[i] >> 20) >= digit) word |= 1u << j;
+      }
+      sm.bits[w] = word;
+    }
+    const uint32_t base = cnt;
+    cnt += wg_compact<NT>(n, [&](int i) { return (keys[i] >> 20) >= digit; },
+                          [&](int i, uint32_t rank) { st_shared(&wl[b0 + base + rank], (uint32_t)(s0 + i)); },
+                          sm);
+    __syncthreads();
+    if (p.flags & DSA_WRITE_MASK)
+      mask_blocks<BS>(rowp, p.col_stride, p.B, rb.L, s0, s0 + n, vec, [&](int b) {
+        const int i = b - s0;
+        return ((sm.bits[i >> 5] >> (i & 31)) & 1u) == 0u;
+      });
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) st_shared(&p.ws_cnt[(int64_t)r * p.P + part], cnt);
   if (!arrive_last(&st[1], (uint32_t)p.P, sm)) return;
   final_row<BS>(p, r, rb, sm);
-  if (threadIdx.x == 0) st[1] = 0;
+  if (threadIdx.x == 0) {
+    st_shared(&st[1], 0u);
+    st_shared(&st[3], 0u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The fused kernel.  Grid index g + phase_base < G: pass 1 (and the whole of
+// a short row); otherwise pass 2.
+// ---------------------------------------------------------------------------
+template <int BS>
+__global__ __launch_bounds__(NT) void k_fused(Params p) {
+  __shared__ Smem sm;
+  int g = (int)blockIdx.x + p.phase_base;
+  const bool pass2 = g >= p.G;
+  if (pass2) g -= p.G;
+  int r, part;
+  part_of(p, g, r, part);
+  const Row rb = row_bounds(p, r);
+  if (rb.nlb <= p.small_blocks) {
+    if (pass2 || part != 0) return;
+    if (rb.bad && threadIdx.x == 0) atomicOr(p.status, 1u);
+    if (rb.L == 0) {
+      write_empty_row(p, r);
+      return;
+    }
+    small_row<BS>(p, r, rb, sm);
+    return;
+  }
+  if (!pass2) long_pass1<BS>(p, r, part, rb, sm);
+  else long_pass2<BS>(p, r, part, rb, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -518,7 +777,7 @@ __global__ __launch_bounds__(NT) void k_fused_p2(Params p) {
 template <int BS>
 __global__ __launch_bounds__(NT) void k_scores(Params p) {
   int r, part;
-  if (!map_group(p, r, part)) return;
+  part_of(p, (int)blockIdx.x, r, part);
   const Row rb = row_bounds(p, r);
   if (rb.L == 0) return;
   const float* rowp = row_ptr(p, r, rb);
@@ -533,7 +792,7 @@ template <int BS>
 __global__ __launch_bounds__(NT) void k_mask(Params p) {
   __shared__ uint32_t bits[HIST_WORDS];
   int r, part;
-  if (!map_group(p, r, part)) return;
+  part_of(p, (int)blockIdx.x, r, part);
   const Row rb = row_bounds(p, r);
   if (rb.L == 0) return;
   float* rowp = row_ptr(p, r, rb);
@@ -587,7 +846,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(Params p) {
   }
   const float* rowp = row_ptr(p, r, rb);
   if (p.in_ids == nullptr) {
-    token_stage<BS>(p, r, rb, rowp, nullptr, 0, sm);
+    token_stage<BS>(p, r, rb, rowp, nullptr, 0, 0u, sm);
     return;
   }
   const int32_t* ids = p.in_ids + (int64_t)r * p.k_blocks;
@@ -596,7 +855,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(Params p) {
   const uint32_t kp = wg_compact<NT>(p.k_blocks, [&](int j) { return ids[j] >= 0 && ids[j] < nlb; },
                                      [&](int j, uint32_t rank) { sel[rank] = (uint32_t)ids[j]; }, sm);
   __syncthreads();
-  token_stage<BS>(p, r, rb, rowp, sel, (int)kp, sm);
+  token_stage<BS>(p, r, rb, rowp, sel, (int)kp, 0u, sm);
 }
 
 }  // namespace dsa
@@ -610,12 +869,12 @@ struct dsa_ctx {
   dsa_shape sh;
   int device;
   int cus;
-  int32_t nblocks, P, G, Gpad, small_blocks;
+  int32_t nblocks, P, G, small_blocks;
   int64_t dblk_cap, tkey_cap;
   void* ws;
   size_t ws_bytes;
   uint32_t *ws_key, *ws_list, *ws_flat, *ws_hist, *ws_cnt, *ws_row, *ws_sel, *ws_dblk, *ws_tkey,
-      *status;
+      *ws_tcol, *status;
   uint32_t magic;
 };
 
@@ -689,6 +948,7 @@ Params base_params(const dsa_ctx* c) {
   p.ws_sel = c->ws_sel;
   p.ws_dblk = c->ws_dblk;
   p.ws_tkey = c->ws_tkey;
+  p.ws_tcol = c->ws_tcol;
   p.dblk_cap = c->dblk_cap;
   p.tkey_cap = c->tkey_cap;
   p.status = c->status;
@@ -740,16 +1000,17 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
   c->magic = CTX_MAGIC;
   const int64_t nb = s->width > 0 ? (s->width + s->block_size - 1) / s->block_size : 0;
   c->nblocks = (int32_t)nb;
-  c->small_blocks = KEY_CAP;
+  c->small_blocks = LIST_CAP;
 
   int rc = on_device(device, [&]() -> int {
     hipDeviceProp_t prop;
     hipError_t e = hipGetDeviceProperties(&prop, device);
     if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
     c->cus = prop.multiProcessorCount;
-    // Workgroups per row: enough groups to cover the CUs several times over,
-    // no more than one per 256 blocks of the buffer, and at most NT.
-    const int64_t target = (int64_t)c->cus * 8;
+    // Workgroups per row: about two per CU in all (one resident round at two
+    // workgroups per CU), no more than one per 256 blocks of the buffer, and
+    // at most NT.
+    const int64_t target = (int64_t)c->cus * 2;
     int64_t P = s->rows > 0 ? (target + s->rows - 1) / s->rows : 1;
     const int64_t pmax = std::max<int64_t>(1, (nb + 255) / 256);
     P = std::max<int64_t>(1, std::min<int64_t>({P, pmax, (int64_t)NT}));
@@ -757,7 +1018,6 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     const int64_t G = P * s->rows;
     if (G > (int64_t)1 << 30) return fail(DSA_ERR_UNSUPPORTED, "too many rows");
     c->G = (int32_t)G;
-    c->Gpad = (int32_t)((G + 7) / 8 * 8);
     const int64_t F = (s->k_tokens + s->block_size - 1) / s->block_size;
     // Token domain of a row: at most nlow + Kp <= 2*K_blk + F blocks (also
     // with repeated ids given to the standalone token top-k).
@@ -770,7 +1030,8 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     const int64_t n_hist = long_rows ? R * HIST_WORDS : 0;
     const int64_t n_cnt = long_rows ? R * P : 0;
     const int64_t words[] = {n_key, n_key, n_key, n_hist, n_cnt, R * ROW_STATE,
-                             R * s->k_blocks, R * c->dblk_cap, R * c->tkey_cap, 64};
+                             R * s->k_blocks, R * c->dblk_cap, R * c->tkey_cap,
+                             R * c->tkey_cap, 64};
     int64_t total = 0;
     for (int64_t w : words) total += (w + 63) / 64 * 64;
     c->ws_bytes = (size_t)total * 4;
@@ -782,9 +1043,10 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
     uint32_t* base = static_cast<uint32_t*>(c->ws);
     uint32_t** slots[] = {&c->ws_key, &c->ws_list, &c->ws_flat, &c->ws_hist, &c->ws_cnt,
-                          &c->ws_row, &c->ws_sel, &c->ws_dblk, &c->ws_tkey, &c->status};
+                          &c->ws_row, &c->ws_sel, &c->ws_dblk, &c->ws_tkey, &c->ws_tcol,
+                          &c->status};
     int64_t pos = 0;
-    for (int i = 0; i < 10; ++i) {
+    for (int i = 0; i < 11; ++i) {
       *slots[i] = words[i] ? base + pos : nullptr;
       pos += (words[i] + 63) / 64 * 64;
     }
@@ -819,10 +1081,10 @@ int dsa_select_query(const dsa_ctx* c, dsa_launch_info* info) {
   if (!info) return fail(DSA_ERR_INVALID_ARG, "info is null");
   info->programs_per_row = c->P;
   info->threads_per_group = NT;
-  info->grid_groups = c->Gpad;
+  info->grid_groups = c->G;
   info->small_row_blocks = c->small_blocks;
   info->workspace_bytes = (int64_t)c->ws_bytes;
-  info->fused_launches = c->nblocks > c->small_blocks ? 2 : 1;
+  info->fused_launches = 1;
   return DSA_OK;
 }
 
@@ -839,7 +1101,7 @@ int dsa_block_scores(dsa_ctx* c, const float* logits, const int32_t* starts, con
     p.ends = ends;
     p.scores = scores;
     with_bs(p.B, [&](auto bs) {
-      hipLaunchKernelGGL((k_scores<decltype(bs)::value>), dim3(c->Gpad), dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL((k_scores<decltype(bs)::value>), dim3(c->G), dim3(NT), 0, stream, p);
     });
     return launch_check("k_scores launch");
   });
@@ -886,7 +1148,7 @@ int dsa_candidate_mask(dsa_ctx* c, float* logits, const int32_t* starts, const i
     p.ends = ends;
     p.in_ids = block_ids;
     with_bs(p.B, [&](auto bs) {
-      hipLaunchKernelGGL((k_mask<decltype(bs)::value>), dim3(c->Gpad), dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL((k_mask<decltype(bs)::value>), dim3(c->G), dim3(NT), 0, stream, p);
     });
     return launch_check("k_mask launch");
   });
@@ -897,7 +1159,8 @@ int dsa_select_fused(dsa_ctx* c, float* logits, const int32_t* starts, const int
                      hipStream_t stream) {
   int rc = check_ctx(c);
   if (rc != DSA_OK) return rc;
-  if (flags & ~(uint32_t)DSA_WRITE_MASK) return fail(DSA_ERR_INVALID_ARG, "unknown flags %#x", flags);
+  if (flags & ~(uint32_t)(DSA_WRITE_MASK | DSA_TWO_LAUNCHES))
+    return fail(DSA_ERR_INVALID_ARG, "unknown flags %#x", flags);
   if (empty_shape(c)) return DSA_OK;
   if (!logits || !ends || !block_ids || !token_ids)
     return fail(DSA_ERR_INVALID_ARG, "logits, ends, block_ids and token_ids must be non-null");
@@ -909,16 +1172,22 @@ int dsa_select_fused(dsa_ctx* c, float* logits, const int32_t* starts, const int
     p.block_ids = block_ids;
     p.token_ids = token_ids;
     p.scores = scores;
-    p.flags = flags;
-    const bool two = c->nblocks > c->small_blocks;
+    p.flags = flags & DSA_WRITE_MASK;
+    // Long rows need the second pass: in the same launch (its workgroups wait
+    // for their row's first pass) or, on request, in a second launch.
+    const bool long_rows = c->nblocks > c->small_blocks;
+    const bool two = long_rows && (flags & DSA_TWO_LAUNCHES);
+    const int grid = long_rows && !two ? 2 * c->G : c->G;
     int r2 = DSA_OK;
     with_bs(p.B, [&](auto bs) {
       constexpr int BS = decltype(bs)::value;
-      hipLaunchKernelGGL((k_fused_p1<BS>), dim3(c->Gpad), dim3(NT), 0, stream, p);
-      if ((r2 = launch_check("k_fused_p1 launch")) != DSA_OK) return;
+      p.phase_base = 0;
+      hipLaunchKernelGGL((k_fused<BS>), dim3(grid), dim3(NT), 0, stream, p);
+      if ((r2 = launch_check("k_fused launch")) != DSA_OK) return;
       if (two) {
-        hipLaunchKernelGGL((k_fused_p2<BS>), dim3(c->Gpad), dim3(NT), 0, stream, p);
-        r2 = launch_check("k_fused_p2 launch");
+        p.phase_base = c->G;
+        hipLaunchKernelGGL((k_fused<BS>), dim3(c->G), dim3(NT), 0, stream, p);
+        r2 = launch_check("k_fused (second pass) launch");
       }
     });
     return r2;

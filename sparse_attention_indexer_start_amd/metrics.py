@@ -1,0 +1,48 @@
+"""Algorithmic byte counts of one fused selection call (host-side, from bounds).
+
+Per row with live length L, nlb = ceil(L / B) live blocks:
+
+* reads   ``4 * L`` when the values can change the result, i.e. when some block
+          must be dropped (``nlb > K_blk``) or some column must be dropped
+          (``L > K_tok``), or when block scores are requested; otherwise every
+          live block and column is kept and the outputs follow from the bounds;
+* stores  ``4 * B * max(nlb - K_blk, 0)`` bytes of -inf (only the newest block
+          can be partial, and it is always kept), when the mask is written;
+* stores  ``4 * (K_blk + K_tok)`` bytes of indices, padding included, plus
+          ``4 * nlb`` of scores when requested;
+* reads   the row's bounds: 4 bytes of end, 4 of start when starts are given.
+
+Workspace traffic (block keys, histograms, lists) is an intermediate and is not
+counted.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def row_lengths(starts, ends, rows: int, width: int, starts_repeat: int = 1,
+                ends_repeat: int = 1) -> np.ndarray:
+    r = np.arange(rows)
+    e = np.minimum(np.asarray(ends, dtype=np.int64)[r // ends_repeat], width)
+    if starts is None:
+        s = np.zeros(rows, dtype=np.int64)
+    else:
+        s = np.asarray(starts, dtype=np.int64)[r // starts_repeat]
+    L = np.where(s < 0, 0, np.maximum(e - s, 0))
+    return L
+
+
+def fused_bytes(starts, ends, rows: int, width: int, block_size: int, k_blocks: int,
+                k_tokens: int, starts_repeat: int = 1, ends_repeat: int = 1,
+                write_mask: bool = True, with_scores: bool = False) -> dict:
+    L = row_lengths(starts, ends, rows, width, starts_repeat, ends_repeat)
+    nlb = -(-L // block_size)
+    need = (nlb > k_blocks) | (L > k_tokens) | with_scores
+    reads = int((4 * L * need).sum())
+    mask = int((4 * block_size * np.maximum(nlb - k_blocks, 0)).sum()) if write_mask else 0
+    idx = rows * 4 * (k_blocks + k_tokens)
+    sc = int((4 * nlb).sum()) if with_scores else 0
+    bounds = rows * (4 + (4 if starts is not None else 0))
+    total = reads + mask + idx + sc + bounds
+    return dict(read_bytes=reads + bounds, mask_bytes=mask, index_bytes=idx,
+                score_bytes=sc, total_bytes=total, live_columns=int(L.sum()))

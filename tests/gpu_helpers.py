@@ -53,13 +53,14 @@ class DevCase:
         scores = torch.full((sh.rows, sh.nblocks), SCORE_FILL_BITS, dtype=torch.int32, device=dev)
         return bids, tids, scores.view(torch.float32)
 
-    def run_fused(self, ctx=None, write_mask=True, with_scores=True):
+    def run_fused(self, ctx=None, write_mask=True, with_scores=True, two_launches=False):
         import torch
         own = ctx is None
         ctx = ctx or self.context()
         bids, tids, scores = self.outputs()
         ctx.select_fused(self.logits, self.starts, self.ends, bids, tids,
-                         scores if with_scores else None, write_mask)
+                         scores if with_scores else None, write_mask,
+                         two_launches=two_launches)
         torch.cuda.synchronize()
         if own:
             ctx.close()

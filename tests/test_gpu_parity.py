@@ -74,6 +74,7 @@ def test_fused_fuzz(seed):
     _full_check(dc, bids, tids, scores)
 
 
+@pytest.mark.parametrize("two", [False, True], ids=["one_launch", "two_launches"])
 @pytest.mark.parametrize("B,W,ends,kb,kt", [
     (8, 65536, [65536, 40000, 16385], 16, 100),
     (8, 65536, [65536, 40000, 16385], 1000, 2048),
@@ -81,14 +82,16 @@ def test_fused_fuzz(seed):
     (1, 12000, [12000, 4097, 2049, 11999], 50, 70),
     (2, 30000, [30000, 20001, 4097], 2047, 5000),
     (16, 140000, [140000, 70000, 32769], 128, 2048),
+    (8, 300000, [300000, 299999, 150001, 65537], 2048, 2048),
+    (4, 200000, [200000, 100003], 600, 5000),
 ])
-def test_fused_long_rows(B, W, ends, kb, kt):
+def test_fused_long_rows(B, W, ends, kb, kt, two):
     """Rows longer than one workgroup's LDS share: the two-pass path."""
     case = wl.make_custom(len(ends), W, B, kb, kt, ends, seed=B * 7 + kb, dup_frac=0.02,
                           outlier_frac=0.01)
-    gh.log(f"long rows B={B} W={W} ends={ends} kb={kb} kt={kt}")
+    gh.log(f"long rows B={B} W={W} ends={ends} kb={kb} kt={kt} two_launches={two}")
     dc = gh.DevCase(case)
-    bids, tids, scores = dc.run_fused()
+    bids, tids, scores = dc.run_fused(two_launches=two)
     _full_check(dc, bids, tids, scores)
 
 
@@ -320,13 +323,15 @@ def _sample_rows(case, n_random=6, seed=0):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", ["short_decode", "mtp_ragged", "long_decode", "prefill_chunk"])
-def test_full_size_workload(name):
+@pytest.mark.parametrize("name,two", [
+    ("short_decode", False), ("mtp_ragged", False), ("mtp_ragged", True),
+    ("long_decode", False), ("long_decode", True), ("prefill_chunk", False)])
+def test_full_size_workload(name, two):
     gh.log(f"workload {name}: generating")
     case = wl.make_config(name)
     dc = gh.DevCase(case)
-    gh.log(f"workload {name}: running")
-    bids, tids, scores = dc.run_fused()
+    gh.log(f"workload {name}: running (two_launches={two})")
+    bids, tids, scores = dc.run_fused(two_launches=two)
     gh.log(f"workload {name}: whole-buffer checks")
     gh.check_whole_buffer(dc)
     gh.check_invariants_all_rows(dc, bids, tids)
