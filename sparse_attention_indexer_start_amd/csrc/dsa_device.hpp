@@ -190,7 +190,7 @@ DSA_DEV void find_bin(const uint32_t* hist, int nb, uint32_t krem, Smem& sm,
 
 // Top-K selection rule over getk(0..n), 1 <= K <= n: element i is kept iff
 // key > T, or key == T and it is among the first q such elements in index
-// order.  MSB-first radix select with digits of 12, 12 and 8 bits and LDS
+// order.  MSB-first radix select with digits of 11, 11 and 10 bits and LDS
 // histograms; it stops early once the digit bin holding the K-th key is kept
 // whole.  Loads are issued U at a time per thread.
 template <int NT, int U = 8, class GetKey>
@@ -199,8 +199,8 @@ DSA_DEV void wg_radix_select(int n, uint32_t K, GetKey getk, Smem& sm, uint32_t&
   uint32_t prefix = 0, krem = K;
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-    const int bits = pass == 2 ? 8 : 12;
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int bits = pass == 2 ? 10 : 11;
     const int nb = 1 << bits;
     const int hs = shift + bits;
     for (int j = threadIdx.x; j < nb; j += NT) sm.hist[j] = 0;

@@ -42,7 +42,11 @@ namespace dsa {
 
 constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int UNROLL = 4;      // float4 loads in flight per lane in the score pass
-constexpr int ROW_STATE = 4;   // pass-1 ticket, pass-2 ticket, digit, ready flag
+constexpr int ROW_STATE = 8;   // pass-1 ticket, pass-2 ticket, digit, ready flag, low flag
+constexpr int UNROLL_STRIDED = 8;   // scalar loads in flight per lane: 4 * this
+// One workgroup reads at most a few tens of GB/s, so a row longer than this is
+// split over its P workgroups even when its block keys would fit in LDS.
+constexpr int SMALL_COLS = 16384;
 constexpr uint32_t KEPT_FLAG = 0x80000000u;
 constexpr uint64_t WAIT_LIMIT_TICKS = 200000000ull;   // 2 s of the 100 MHz clock
 
@@ -58,6 +62,12 @@ struct Params {
   int64_t width, row_stride, col_stride;
   int32_t rows, B, k_blocks, k_tokens, starts_repeat, ends_repeat;
   int32_t nblocks, P, G, small_blocks, phase_base;
+
+  // A row is handled by one workgroup when its keys fit in LDS and it is short
+  // (or the shape gives each row a single workgroup anyway).
+  __device__ bool one_group(int32_t nlb, int32_t L) const {
+    return nlb <= small_blocks && (L <= SMALL_COLS || P == 1);
+  }
   uint32_t flags;
   uint32_t* ws_key;    // [rows][nblocks]  block keys of long rows
   uint32_t* ws_list;   // [rows][nblocks]  listed blocks, per chunk
@@ -140,35 +150,75 @@ DSA_DEV uint32_t block_max_key(const float* rowp, int64_t cs, bool vec, int64_t 
 // ---------------------------------------------------------------------------
 // Block scores of blocks [b0, b1): emit(b, key) once per block.
 // ---------------------------------------------------------------------------
+// `low` is set when some live value of the range ranks at or below -inf.
 template <int BS, class Emit>
 DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, int b1,
-                          int nlb, bool vec, Emit emit) {
+                          int nlb, bool vec, Emit emit, bool& low) {
   if constexpr (BS >= 4) {
     constexpr int G = BS / 4;          // lanes per block, 4 columns per lane
     const int64_t cbeg = (int64_t)b0 * BS;
     const int64_t cend = min((int64_t)b1 * BS, (int64_t)L);
     const int64_t t4 = (int64_t)threadIdx.x * 4;
-    const int64_t step = (int64_t)NT * 4 * UNROLL;
     const bool leader = (threadIdx.x % G) == 0;
+    if (!vec) {
+      // Strided or unaligned: scalar loads, UNROLL_STRIDED groups in flight.
+      const int64_t sstep = (int64_t)NT * 4 * UNROLL_STRIDED;
+      for (int64_t c0 = cbeg; c0 < cend; c0 += sstep) {
+        float v[UNROLL_STRIDED][4];
+#pragma unroll
+        for (int u = 0; u < UNROLL_STRIDED; ++u) {
+          const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            v[u][j] = (col + j < cend) ? rowp[(col + j) * cs] : __uint_as_float(0xFFFFFFFFu);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL_STRIDED; ++u) {
+          const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
+          uint32_t m = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t kk = f2key(v[u][j]);
+            m = max(m, kk);
+            low |= (col + j < cend) && kk <= KEY_NEG_INF;
+          }
+          m = group_max<G>(m);
+          if (leader && col < cend) {
+            const int b = (int)(col / BS);
+            emit(b, b == nlb - 1 ? KEY_POS_INF : m);
+          }
+        }
+      }
+      return;
+    }
+    const int64_t step = (int64_t)NT * 4 * UNROLL;
     for (int64_t c0 = cbeg; c0 < cend; c0 += step) {
       uint32_t k[UNROLL];
       if (vec) {
+        // Whole vectors first, so that all UNROLL loads are in flight together;
+        // the one partial vector at the end of the range is filled afterwards.
+        const float z = __uint_as_float(0xFFFFFFFFu);    // key 0: below every float
         f4v v[UNROLL];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
-          if (col + 4 <= cend) {
-            v[u] = *reinterpret_cast<const f4v*>(rowp + col);
-          } else {
-            const float z = __uint_as_float(0xFFFFFFFFu);    // key 0: below every float
-            v[u] = f4v{z, z, z, z};
-            for (int j = 0; j < 4; ++j)
-              if (col + j < cend) v[u][j] = rowp[col + j];
-          }
+          v[u] = col + 4 <= cend ? *reinterpret_cast<const f4v*>(rowp + col) : f4v{z, z, z, z};
         }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+        for (int u = 0; u < UNROLL; ++u) {
+          const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
+          if (col < cend && col + 4 > cend)
+            for (int j = 0; j < 4; ++j)
+              if (col + j < cend) v[u][j] = rowp[col + j];
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
           k[u] = max(max(f2key(v[u].x), f2key(v[u].y)), max(f2key(v[u].z), f2key(v[u].w)));
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            low |= (col + j < cend) && f2key(v[u][j]) <= KEY_NEG_INF;
+        }
       } else {
         float v[UNROLL][4];
 #pragma unroll
@@ -179,8 +229,13 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
             v[u][j] = (col + j < cend) ? rowp[(col + j) * cs] : __uint_as_float(0xFFFFFFFFu);
         }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+        for (int u = 0; u < UNROLL; ++u) {
+          const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
           k[u] = max(max(f2key(v[u][0]), f2key(v[u][1])), max(f2key(v[u][2]), f2key(v[u][3])));
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            low |= (col + j < cend) && f2key(v[u][j]) <= KEY_NEG_INF;
+        }
       }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u) {
@@ -203,6 +258,7 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
         for (int j = 0; j < 4; ++j) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + j;
           k[u][j] = col < cend ? f2key(rowp[col * cs]) : 0u;
+          low |= col < cend && k[u][j] <= KEY_NEG_INF;
         }
 #pragma unroll
       for (int u = 0; u < UNROLL; ++u)
@@ -223,6 +279,9 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
       const int64_t c0 = (int64_t)b * B;
       const int n = (int)min((int64_t)B, (int64_t)L - c0);
       const uint32_t m = block_max_key<0>(rowp, cs, false, c0, n);
+      uint32_t mn = 0xFFFFFFFFu;
+      for (int j = 0; j < n; ++j) mn = min(mn, f2key(rowp[(c0 + j) * cs]));
+      low |= mn <= KEY_NEG_INF;
       emit(b, b == nlb - 1 ? KEY_POS_INF : m);
     }
   }
@@ -277,29 +336,37 @@ DSA_DEV void gather_kept(const float* rowp, int64_t cs, int B, int L, bool vec,
     for (int j = j0; j < j1; j += GB) {
       uint32_t kk[GB][BS];
       int64_t c0s[GB];
+      bool full[GB];
 #pragma unroll
       for (int g = 0; g < GB; ++g) {
         c0s[g] = -1;
-#pragma unroll
-        for (int e = 0; e < BS; ++e) kk[g][e] = 0u;
+        full[g] = false;
         if (j + g < j1) {
-          const int64_t c0 = (int64_t)sel[j + g] * BS;
-          const int n = (int)min((int64_t)BS, (int64_t)L - c0);
-          c0s[g] = c0;
-          if (vec && n == BS) {
+          c0s[g] = (int64_t)sel[j + g] * BS;
+          full[g] = vec && c0s[g] + BS <= L;
+        }
+      }
+      // Whole blocks by vector loads, all issued before any is used.
+      f4v v[GB][BS / 4];
 #pragma unroll
-            for (int t = 0; t < BS / 4; ++t) {
-              const f4v v = *reinterpret_cast<const f4v*>(rowp + c0 + 4 * t);
-              kk[g][4 * t + 0] = f2key(v.x);
-              kk[g][4 * t + 1] = f2key(v.y);
-              kk[g][4 * t + 2] = f2key(v.z);
-              kk[g][4 * t + 3] = f2key(v.w);
-            }
-          } else {
+      for (int g = 0; g < GB; ++g)
 #pragma unroll
-            for (int e = 0; e < BS; ++e)
-              if (e < n) kk[g][e] = f2key(rowp[(c0 + e) * cs]);
-          }
+        for (int t = 0; t < BS / 4; ++t)
+          v[g][t] = full[g] ? *reinterpret_cast<const f4v*>(rowp + c0s[g] + 4 * t) : f4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < GB; ++g)
+#pragma unroll
+        for (int t = 0; t < BS / 4; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kk[g][4 * t + e] = full[g] ? f2key(v[g][t][e]) : 0u;
+      // Strided, unaligned or the partial newest block: scalar loads.
+#pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        if (c0s[g] >= 0 && !full[g]) {
+          const int n = (int)min((int64_t)BS, (int64_t)L - c0s[g]);
+#pragma unroll
+          for (int e = 0; e < BS; ++e)
+            if (e < n) kk[g][e] = f2key(rowp[(c0s[g] + e) * cs]);
         }
       }
 #pragma unroll
@@ -335,7 +402,8 @@ DSA_DEV void gather_kept(const float* rowp, int64_t cs, int B, int L, bool vec,
 // ---------------------------------------------------------------------------
 template <int BS>
 DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* rowp,
-                         const uint32_t* sel, int Kp, uint32_t tlo, Smem& sm) {
+                         const uint32_t* sel, int Kp, uint32_t tlo, bool canonical,
+                         bool no_low, Smem& sm) {
   const int L = rb.L, nlb = rb.nlb, B = p.B;
   const int64_t cs = p.col_stride;
   const bool vec = vec_ok(p, rowp);
@@ -355,6 +423,56 @@ DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* row
         }, sm);
     for (int i = Kt + threadIdx.x; i < p.k_tokens; i += NT) tout[i] = -1;
     return;
+  }
+
+  // Kept columns: every kept block is whole except the newest (the row's last).
+  const bool newest_kept = canonical && Kp > 0 && sel[Kp - 1] == (uint32_t)(nlb - 1);
+  const int64_t C = newest_kept ? (int64_t)(Kp - 1) * B + (L - (int64_t)(nlb - 1) * B) : -1;
+  if (C >= 0 && C <= Kt) {
+    // ---- closed form: all kept columns, then the lowest non-kept columns ----
+    // Valid when every kept column ranks above -inf (checked here): then the
+    // Kt best columns are the C kept ones and the first q = Kt - C of the
+    // non-kept (-inf) columns in column order.
+    // (no_low: the scores pass saw no live value at or below -inf.)
+    uint32_t tf = (uint32_t)C;
+    if (!no_low) {
+      const int bpt = (Kp + NT - 1) / NT;
+      const int j0 = min(Kp, (int)threadIdx.x * bpt), j1 = min(Kp, j0 + bpt);
+      uint32_t cf = 0;
+      gather_kept<BS>(rowp, cs, B, L, vec, sel, j0, j1, [&](int64_t, uint32_t k) { cf += k > KEY_NEG_INF; });
+      (void)wg_excl_scan<NT>(cf, sm.wv, tf);
+    }
+    if ((int64_t)tf == C) {
+      const int q = Kt - (int)C;
+      for (int idx = threadIdx.x; idx < Kt; idx += NT) {
+        int64_t col;
+        int rank;
+        if (idx < (int)C) {
+          const int j = div_b<BS>(idx, B);
+          const int e = idx - j * B;
+          const int64_t b = sel[j];
+          col = b * B + e;
+          rank = idx + (int)min((int64_t)q, (b - j) * B);
+        } else {
+          const int f = idx - (int)C;
+          const int i = div_b<BS>(f, B);
+          const int e = f - i * B;
+          // number of kept blocks below the i-th non-kept block: the first j
+          // with sel[j] - j > i (sel[j] - j counts non-kept blocks below sel[j])
+          int lo = 0, hi = Kp;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if ((int64_t)sel[mid] - mid > i) hi = mid;
+            else lo = mid + 1;
+          }
+          col = (int64_t)(i + lo) * B + e;
+          rank = f + lo * B;
+        }
+        tout[rank] = (int32_t)(rb.s + col);
+      }
+      for (int i = Kt + threadIdx.x; i < p.k_tokens; i += NT) tout[i] = -1;
+      return;
+    }
   }
 
   if ((int64_t)Kp * B >= Kt) {
@@ -481,6 +599,7 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
   uint32_t* sel = Kp <= SEL_CAP ? sm.sel : p.ws_sel + (int64_t)r * p.k_blocks;
   const bool need_keys = nlb > p.k_blocks || p.scores != nullptr;
   uint32_t T = 0, q = 0xFFFFFFFFu;
+  bool no_low = false;
   if (!need_keys) {
     // Every live block is kept; the result follows from the bounds.
     for (int i = threadIdx.x; i < p.k_blocks; i += NT) bout[i] = i < nlb ? i : -1;
@@ -488,11 +607,12 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
   } else {
     float* sc = p.scores ? p.scores + (int64_t)r * p.nblocks : nullptr;
     uint32_t* keys = sm.keys();
+    bool low = false;
     score_blocks<BS>(rowp, p.col_stride, B, L, 0, nlb, nlb, vec, [&](int b, uint32_t k) {
       keys[b] = k;
       if (sc) sc[b] = key2f(k);
-    });
-    __syncthreads();
+    }, low);
+    no_low = __syncthreads_or(low) == 0;
     auto getk = [&](int i) { return keys[i]; };
     if (nlb > Kp) wg_radix_select<NT>(nlb, (uint32_t)Kp, getk, sm, T, q);
     wg_select_compact<NT>(nlb, T, q, getk,
@@ -513,7 +633,7 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
                       [&](int b) { return ((sm.bits[b >> 5] >> (b & 31)) & 1u) == 0u; });
   }
   __syncthreads();
-  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, sm);
+  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, true, no_low, sm);
 }
 
 // Workgroup-wide ticket on a workspace counter: true in the last of `total`
@@ -540,18 +660,19 @@ DSA_DEV void long_pass1(const Params& p, int r, int part, const Row& rb, Smem& s
   __syncthreads();
   uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   float* sc = p.scores ? p.scores + (int64_t)r * p.nblocks : nullptr;
+  bool low = false;
   score_blocks<BS>(rowp, p.col_stride, p.B, rb.L, b0, b1, rb.nlb, vec, [&](int b, uint32_t k) {
     st_shared(&wk[b], k);
     if (sc) sc[b] = key2f(k);
     atomicAdd(&sm.hist[k >> 20], 1u);
-  });
-  __syncthreads();
+  }, low);
+  uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
+  if (__syncthreads_or(low) && threadIdx.x == 0) atomicOr(&st[4], 1u);
   uint32_t* gh = p.ws_hist + (int64_t)r * HIST_WORDS;
   for (int j = threadIdx.x; j < HIST_WORDS; j += NT) {
     const uint32_t c = sm.hist[j];
     if (c) atomicAdd(&gh[j], c);
   }
-  uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
   if (!arrive_last(&st[0], (uint32_t)p.P, sm)) return;
   constexpr int PER = HIST_WORDS / NT;
   uint32_t h[PER];
@@ -661,7 +782,8 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
       }, sm);
   for (int i = Kp + threadIdx.x; i < p.k_blocks; i += NT) bout[i] = -1;
   __syncthreads();
-  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, sm);
+  const bool no_low = ld_shared(&p.ws_row[(int64_t)r * ROW_STATE + 4]) == 0u;
+  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, true, no_low, sm);
 }
 
 // Thread 0 waits (time-bounded) for the row's ready flag.  Returns false if
@@ -741,6 +863,7 @@ DSA_DEV void long_pass2(const Params& p, int r, int part, const Row& rb, Smem& s
   if (threadIdx.x == 0) {
     st_shared(&st[1], 0u);
     st_shared(&st[3], 0u);
+    st_shared(&st[4], 0u);
   }
 }
 
@@ -757,7 +880,7 @@ __global__ __launch_bounds__(NT) void k_fused(Params p) {
   int r, part;
   part_of(p, g, r, part);
   const Row rb = row_bounds(p, r);
-  if (rb.nlb <= p.small_blocks) {
+  if (p.one_group(rb.nlb, rb.L)) {
     if (pass2 || part != 0) return;
     if (rb.bad && threadIdx.x == 0) atomicOr(p.status, 1u);
     if (rb.L == 0) {
@@ -784,8 +907,9 @@ __global__ __launch_bounds__(NT) void k_scores(Params p) {
   int b0, b1;
   chunk_of(rb, p.P, part, b0, b1);
   float* sc = p.scores + (int64_t)r * p.nblocks;
+  bool low = false;
   score_blocks<BS>(rowp, p.col_stride, p.B, rb.L, b0, b1, rb.nlb, vec_ok(p, rowp),
-                   [&](int b, uint32_t k) { sc[b] = key2f(k); });
+                   [&](int b, uint32_t k) { sc[b] = key2f(k); }, low);
 }
 
 template <int BS>
@@ -846,7 +970,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(Params p) {
   }
   const float* rowp = row_ptr(p, r, rb);
   if (p.in_ids == nullptr) {
-    token_stage<BS>(p, r, rb, rowp, nullptr, 0, 0u, sm);
+    token_stage<BS>(p, r, rb, rowp, nullptr, 0, 0u, false, false, sm);
     return;
   }
   const int32_t* ids = p.in_ids + (int64_t)r * p.k_blocks;
@@ -855,7 +979,7 @@ __global__ __launch_bounds__(NT) void k_topk_tokens(Params p) {
   const uint32_t kp = wg_compact<NT>(p.k_blocks, [&](int j) { return ids[j] >= 0 && ids[j] < nlb; },
                                      [&](int j, uint32_t rank) { sel[rank] = (uint32_t)ids[j]; }, sm);
   __syncthreads();
-  token_stage<BS>(p, r, rb, rowp, sel, (int)kp, 0u, sm);
+  token_stage<BS>(p, r, rb, rowp, sel, (int)kp, 0u, false, false, sm);
 }
 
 }  // namespace dsa
@@ -963,6 +1087,12 @@ int check_ctx(const dsa_ctx* c) {
 
 bool empty_shape(const dsa_ctx* c) { return c->sh.rows == 0 || c->sh.width == 0; }
 
+// Whether some row of this shape can be split over its P workgroups (the
+// device-side rule of Params::one_group, taken at the widest row).
+bool may_split(const dsa_ctx* c) {
+  return c->nblocks > c->small_blocks || (c->sh.width > SMALL_COLS && c->P > 1);
+}
+
 int launch_check(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, what);
@@ -1024,7 +1154,7 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     c->dblk_cap = 2 * (int64_t)s->k_blocks + F + 1;
     c->tkey_cap = c->dblk_cap * s->block_size;
     if (empty_shape(c)) return DSA_OK;
-    const bool long_rows = nb > c->small_blocks;
+    const bool long_rows = may_split(c);
     const int64_t R = s->rows;
     const int64_t n_key = long_rows ? R * nb : 0;
     const int64_t n_hist = long_rows ? R * HIST_WORDS : 0;
@@ -1175,7 +1305,7 @@ int dsa_select_fused(dsa_ctx* c, float* logits, const int32_t* starts, const int
     p.flags = flags & DSA_WRITE_MASK;
     // Long rows need the second pass: in the same launch (its workgroups wait
     // for their row's first pass) or, on request, in a second launch.
-    const bool long_rows = c->nblocks > c->small_blocks;
+    const bool long_rows = may_split(c);
     const bool two = long_rows && (flags & DSA_TWO_LAUNCHES);
     const int grid = long_rows && !two ? 2 * c->G : c->G;
     int r2 = DSA_OK;

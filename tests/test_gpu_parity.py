@@ -83,6 +83,8 @@ def test_fused_fuzz(seed):
     (2, 30000, [30000, 20001, 4097], 2047, 5000),
     (16, 140000, [140000, 70000, 32769], 128, 2048),
     (8, 300000, [300000, 299999, 150001, 65537], 2048, 2048),
+    (16, 65536, [65536, 30000, 16385, 16384], 128, 2048),   # medium rows: split
+    (8, 32768, [32768, 16385, 16384, 20001], 300, 3000),
     (4, 200000, [200000, 100003], 600, 5000),
 ])
 def test_fused_long_rows(B, W, ends, kb, kt, two):
@@ -101,6 +103,28 @@ def test_fused_long_rows_with_start_and_stride():
     dc = gh.DevCase(case)
     bids, tids, scores = dc.run_fused()
     _full_check(dc, bids, tids, scores)
+
+
+@pytest.mark.parametrize("W,B,kb,kt", [(3000, 8, 40, 300), (5000, 4, 300, 2048),
+                                       (70000, 8, 600, 2048), (40000, 16, 64, 4000)])
+def test_fused_special_values(W, B, kb, kt):
+    """-inf, +inf, -0 and NaN bit patterns inside the live span.
+
+    They are outside the input contract, but the order key still defines the
+    result (NaNs rank by their bits; +inf blocks can tie with the pinned one),
+    and the library must reproduce the oracle exactly."""
+    ends = [W, W - 7, W // 2 + 3, W // 3]
+    case = wl.make_custom(len(ends), W, B, kb, kt, ends, seed=W + B, dup_frac=0.05)
+    rng = np.random.default_rng(W)
+    specials = np.array([0xFF800000, 0x7F800000, 0x80000000, 0x7FC00000, 0xFFC00001],
+                        dtype=np.uint32)
+    u = case.buf.view(np.uint32)
+    for r, e in enumerate(ends):
+        pos = rng.choice(min(e, W), size=max(1, min(e, W) // 50), replace=False)
+        u[r, pos] = rng.choice(specials, size=pos.size)
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused()
+    gh.check_rows_against_oracle(dc, range(dc.sh.rows), bids, tids, scores)
 
 
 def test_fused_without_mask_leaves_buffer():
