@@ -18,7 +18,6 @@ Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one GPU.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -34,16 +33,6 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
-
-
-def source_sha() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_attention_indexer_start_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, sha: str):
@@ -130,7 +119,7 @@ def main() -> int:
     nbytes = case.buf.nbytes
     need = args.steps + args.warmup
     nbuf = int(max(1, min(need, (args.buffer_budget_gb * 2**30) // nbytes)))
-    log(f"{nbuf} device copies of {nbytes / 2**20:.1f} MiB")
+    log(f"{nbuf} device copies of {nbytes / 2**20:.1f} MiB ({nbytes} bytes each)")
     base = torch.from_numpy(case.buf).to(dev)
     ring = [base.clone() for _ in range(nbuf)]
     starts = None if case.starts is None else torch.from_numpy(case.starts).to(dev)
@@ -216,7 +205,7 @@ def main() -> int:
     value = sh.rows * steps / (region_ms * 1e-3)
     live_gbps = per_call / (ms_per_step * 1e-3) / 1e9
     achieved = per_call / (call_ms * 1e-3) / 1e9
-    sha = source_sha()
+    sha = metrics.source_sha()
     traffic = measured_traffic(args.workload, sha)
 
     cpu = None
@@ -256,6 +245,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "source_sha": sha,
+        "buffer_bytes": nbytes,
     }
     print(json.dumps(out), flush=True)
     ctx.close()

@@ -17,7 +17,22 @@ counted.
 """
 from __future__ import annotations
 
+import hashlib
+import os
+
 import numpy as np
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def source_sha() -> str:
+    """Short hash of the kernel sources (ties a counter profile to the code)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def row_lengths(starts, ends, rows: int, width: int, starts_repeat: int = 1,
