@@ -188,23 +188,145 @@ DSA_DEV void find_bin(const uint32_t* hist, int nb, uint32_t krem, Smem& sm,
   in_bin = sm.misc[5];
 }
 
+// hist[0..NB) (NB a power of two, 256 <= NB <= 8 * NT): find d with
+// count(bins > d) < krem <= count(bins >= d), count(bins > d) and hist[d],
+// and leave hist[0..NB) zero.  Bins are read with 16-byte LDS loads; two
+// barriers.
+template <int NT, int NB>
+DSA_DEV void find_bin_zero(uint32_t* hist, uint32_t krem, Smem& sm, uint32_t& d,
+                           uint32_t& above, uint32_t& in_bin) {
+  constexpr int PER = NB >= NT ? NB / NT : 1;
+  constexpr int ACT = NB / PER;              // threads holding bins
+  static_assert(PER == 1 || PER == 2 || PER % 4 == 0, "bins per thread");
+  const int t = (int)threadIdx.x;
+  uint32_t h[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) h[j] = 0u;
+  if (t < ACT) {
+    uint32_t* hp = hist + t * PER;
+    if constexpr (PER % 4 == 0) {
+#pragma unroll
+      for (int j = 0; j < PER; j += 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(hp + j);
+        h[j] = v.x; h[j + 1] = v.y; h[j + 2] = v.z; h[j + 3] = v.w;
+      }
+#pragma unroll
+      for (int j = 0; j < PER; j += 4) *reinterpret_cast<uint4*>(hp + j) = make_uint4(0u, 0u, 0u, 0u);
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) h[j] = hp[j];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) hp[j] = 0u;
+    }
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) c += h[j];
+  if (t == 0) {   // defined result even if the counts fall short; written
+    sm.misc[0] = 0;   // before the scan's barrier, so the finder's write wins
+    sm.misc[1] = 0;
+    sm.misc[5] = 0;
+  }
+  uint32_t total;
+  const uint32_t excl = wg_excl_scan_once<NT>(c, sm.wv, total);
+  const uint32_t sfx = total - (excl + c);   // count in bins above this thread's
+  if (sfx < krem && krem <= sfx + c) {
+    uint32_t acc = sfx, dd = 0, ab = 0, hb = 0;
+    bool found = false;
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {
+      const bool hit = !found && acc + h[j] >= krem;
+      dd = hit ? (uint32_t)j : dd;
+      ab = hit ? acc : ab;
+      hb = hit ? h[j] : hb;
+      found = found || hit;
+      acc += h[j];
+    }
+    sm.misc[0] = (uint32_t)(t * PER) + dd;
+    sm.misc[1] = ab;
+    sm.misc[5] = hb;
+  }
+  __syncthreads();
+  d = sm.misc[0];
+  above = sm.misc[1];
+  in_bin = sm.misc[5];
+}
+
+// Radix passes of the top-K rule below over keys visited by
+// for_keys(f) (f(key) once per element).  Digits of 12, 12 and 8 bits over
+// the 4096-word histogram, which must be zero on entry and is zero on return.
+template <int NT, class ForKeys>
+DSA_DEV void radix_passes(ForKeys for_keys, uint32_t K, Smem& sm, uint32_t& T, uint32_t& q) {
+  uint32_t d, above, in_bin, krem = K;
+  auto done = [&](uint32_t lo) {   // the bin starting at key `lo` is kept whole
+    if (lo == 0) {
+      T = 0;
+      q = 0xFFFFFFFFu;
+    } else {
+      T = lo - 1;
+      q = 0;
+    }
+  };
+  for_keys([&](uint32_t k) { atomicAdd(&sm.hist[k >> 20], 1u); });
+  __syncthreads();
+  find_bin_zero<NT, 4096>(sm.hist, krem, sm, d, above, in_bin);
+  uint32_t prefix = d << 20;
+  krem -= above;
+  if (in_bin == krem) return done(prefix);
+  const uint32_t p20 = prefix >> 20;
+  for_keys([&](uint32_t k) {
+    if ((k >> 20) == p20) atomicAdd(&sm.hist[(k >> 8) & 0xFFFu], 1u);
+  });
+  __syncthreads();
+  find_bin_zero<NT, 4096>(sm.hist, krem, sm, d, above, in_bin);
+  prefix |= d << 8;
+  krem -= above;
+  if (in_bin == krem) return done(prefix);
+  const uint32_t p8 = prefix >> 8;
+  for_keys([&](uint32_t k) {
+    if ((k >> 8) == p8) atomicAdd(&sm.hist[k & 0xFFu], 1u);
+  });
+  __syncthreads();
+  find_bin_zero<NT, 256>(sm.hist, krem, sm, d, above, in_bin);
+  T = prefix | d;
+  q = krem - above;
+}
+
+template <int NT, int U, class GetKey>
+DSA_DEV void radix_select_regs(int n, uint32_t K, GetKey getk, Smem& sm, uint32_t& T,
+                               uint32_t& q) {
+  uint32_t k[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = (int)threadIdx.x + u * NT;
+    k[u] = i < n ? getk(i) : 0u;
+  }
+  radix_passes<NT>([&](auto f) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if ((int)threadIdx.x + u * NT < n) f(k[u]);
+  }, K, sm, T, q);
+}
+
 // Top-K selection rule over getk(0..n), 1 <= K <= n: element i is kept iff
 // key > T, or key == T and it is among the first q such elements in index
-// order.  MSB-first radix select with digits of 11, 11 and 10 bits and LDS
+// order.  MSB-first radix select (digits of 12, 12 and 8 bits) with LDS
 // histograms; it stops early once the digit bin holding the K-th key is kept
-// whole.  Loads are issued U at a time per thread.
+// whole.  Up to 8 * NT keys are held in registers across the passes; longer
+// inputs are re-read each pass, U loads at a time per thread.
+// hist_zero: the caller guarantees sm.hist[0..4096) is zero.  On return it is.
 template <int NT, int U = 8, class GetKey>
 DSA_DEV void wg_radix_select(int n, uint32_t K, GetKey getk, Smem& sm, uint32_t& T,
-                             uint32_t& q) {
-  uint32_t prefix = 0, krem = K;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int bits = pass == 2 ? 10 : 11;
-    const int nb = 1 << bits;
-    const int hs = shift + bits;
-    for (int j = threadIdx.x; j < nb; j += NT) sm.hist[j] = 0;
+                             uint32_t& q, bool hist_zero = false) {
+  if (!hist_zero) {
+    for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
     __syncthreads();
+  }
+  if (n <= NT) return radix_select_regs<NT, 1>(n, K, getk, sm, T, q);
+  if (n <= 2 * NT) return radix_select_regs<NT, 2>(n, K, getk, sm, T, q);
+  if (n <= 4 * NT) return radix_select_regs<NT, 4>(n, K, getk, sm, T, q);
+  if (n <= 8 * NT) return radix_select_regs<NT, 8>(n, K, getk, sm, T, q);
+  radix_passes<NT>([&](auto f) {
     for (int i0 = threadIdx.x; i0 < n; i0 += NT * U) {
       uint32_t k[U];
 #pragma unroll
@@ -213,30 +335,68 @@ DSA_DEV void wg_radix_select(int n, uint32_t K, GetKey getk, Smem& sm, uint32_t&
         k[u] = i < n ? getk(i) : 0u;
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NT;
-        const bool match = (hs >= 32) || ((k[u] >> hs) == (prefix >> hs));
-        if (i < n && match) atomicAdd(&sm.hist[(k[u] >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
+      for (int u = 0; u < U; ++u)
+        if (i0 + u * NT < n) f(k[u]);
     }
-    __syncthreads();
-    uint32_t d, above, in_bin;
-    find_bin<NT>(sm.hist, nb, krem, sm, d, above, in_bin);
-    prefix |= d << shift;
-    krem -= above;
-    if (in_bin == krem) {            // the whole bin is kept: keys >= its lowest key
-      if (prefix == 0) {
-        T = 0;
-        q = 0xFFFFFFFFu;
-      } else {
-        T = prefix - 1;
-        q = 0;
-      }
-      return;
-    }
+  }, K, sm, T, q);
+}
+
+// Ordered application of the (T, q) rule to [0, n), n <= 8 * NT, keys held in
+// registers (element i = threadIdx.x + u * NT): emit(i, rank, kept) for every
+// i, rank = kept elements before i.  Returns the kept count.  One barrier; the
+// caller must pass a barrier before sm.wv is written again.
+template <int NT, int U, class GetKey, class Emit>
+DSA_DEV uint32_t rule_emit_regs(int n, uint32_t T, uint32_t q, GetKey getk, Emit emit,
+                                Smem& sm) {
+  constexpr int NW = NT / 64;
+  static_assert(U * NW <= 64, "one lane per (batch, wave) pair");
+  const int w = wave(), l = lane();
+  uint64_t mg[U], me[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = (int)threadIdx.x + u * NT;
+    const bool v = i < n;
+    const uint32_t k = v ? getk(i) : 0u;
+    mg[u] = ballot(v && k > T);
+    me[u] = ballot(v && k == T);
   }
-  T = prefix;
-  q = krem;
+  if (l == 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) sm.wv[u * NW + w] = popc(mg[u]) | (popc(me[u]) << 16);
+  }
+  __syncthreads();
+  // Lane j of every wave holds pair j = (batch, wave) in index order.
+  const uint32_t cj = l < U * NW ? sm.wv[l] : 0u;
+  const uint32_t gj = cj & 0xFFFFu, ej = cj >> 16;
+  const uint32_t eqx = wave_incl_scan(ej) - ej;
+  const uint32_t take = q > eqx ? min(ej, q - eqx) : 0u;
+  const uint32_t kj = gj + take;
+  const uint32_t kinc = wave_incl_scan(kj);
+  const uint32_t kx = kinc - kj;
+  const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)kinc, 63);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int pair = u * NW + w;
+    const uint32_t base = (uint32_t)__builtin_amdgcn_ds_bpermute(pair << 2, (int)kx);
+    const uint32_t eqb = (uint32_t)__builtin_amdgcn_ds_bpermute(pair << 2, (int)eqx);
+    const int i = (int)threadIdx.x + u * NT;
+    const bool gt = (mg[u] >> l) & 1u;
+    const bool eq = (me[u] >> l) & 1u;
+    const bool kept = gt || (eq && eqb + mbcnt(me[u]) < q);
+    const uint64_t km = ballot(kept);
+    if (i < n) emit(i, base + mbcnt(km), kept);
+  }
+  return total;
+}
+
+// The (T, q) rule applied in index order over getk(0..n) for n <= 8 * NT;
+// see rule_emit_regs.
+template <int NT, class GetKey, class Emit>
+DSA_DEV uint32_t wg_rule_emit(int n, uint32_t T, uint32_t q, GetKey getk, Emit emit, Smem& sm) {
+  if (n <= NT) return rule_emit_regs<NT, 1>(n, T, q, getk, emit, sm);
+  if (n <= 2 * NT) return rule_emit_regs<NT, 2>(n, T, q, getk, emit, sm);
+  if (n <= 4 * NT) return rule_emit_regs<NT, 4>(n, T, q, getk, emit, sm);
+  return rule_emit_regs<NT, 8>(n, T, q, getk, emit, sm);
 }
 
 // Ordered pass over [0, n) applying the (T, q) rule above.  emit(i, rank,

@@ -204,13 +204,24 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
           v[u] = col + 4 <= cend ? *reinterpret_cast<const f4v*>(rowp + col) : f4v{z, z, z, z};
         }
+        // The partial vector's scalars go into registers of their own, so
+        // their loads are in flight together with the vector loads.
+        int tu = -1;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
-          if (col < cend && col + 4 > cend)
-            for (int j = 0; j < 4; ++j)
-              if (col + j < cend) v[u][j] = rowp[col + j];
+          if (col < cend && col + 4 > cend) tu = u;
         }
+        float t0 = z, t1 = z, t2 = z;
+        if (tu >= 0) {
+          const int64_t col = c0 + (int64_t)tu * NT * 4 + t4;
+          t0 = rowp[col];
+          if (col + 1 < cend) t1 = rowp[col + 1];
+          if (col + 2 < cend) t2 = rowp[col + 2];
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+          if (u == tu) v[u] = f4v{t0, t1, t2, z};
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
@@ -312,6 +323,22 @@ DSA_DEV void mask_blocks(float* rowp, int64_t cs, int B, int L, int b0, int b1, 
   }
 }
 
+// -inf over the live columns of block b, by one lane (vector stores when the
+// block is whole and aligned).
+template <int BS>
+DSA_DEV void mask_block_lane(float* rowp, int64_t cs, int B, int L, bool vec, int64_t b) {
+  const int64_t c0 = b * B;
+  const int n = (int)min((int64_t)B, (int64_t)L - c0);
+  if constexpr (BS >= 4) {
+    if (vec && n == BS) {
+#pragma unroll
+      for (int t = 0; t < BS / 4; ++t) store_ninf4(rowp + c0 + 4 * t);
+      return;
+    }
+  }
+  for (int e = 0; e < n; ++e) store_ninf(rowp + (c0 + e) * cs);
+}
+
 // -inf over one whole block (called by one lane).
 DSA_DEV void mask_one_block(float* rowp, int64_t cs, int B, int L, uint32_t b) {
   const int64_t c0 = (int64_t)b * B;
@@ -346,29 +373,29 @@ DSA_DEV void gather_kept(const float* rowp, int64_t cs, int B, int L, bool vec,
           full[g] = vec && c0s[g] + BS <= L;
         }
       }
-      // Whole blocks by vector loads, all issued before any is used.
+      // Whole blocks by vector loads; strided, unaligned or partial (newest)
+      // blocks by scalar loads into registers of their own.  All loads are
+      // issued before any value is used.
       f4v v[GB][BS / 4];
+      float sv[GB][BS];
 #pragma unroll
       for (int g = 0; g < GB; ++g)
 #pragma unroll
         for (int t = 0; t < BS / 4; ++t)
           v[g][t] = full[g] ? *reinterpret_cast<const f4v*>(rowp + c0s[g] + 4 * t) : f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
+      for (int g = 0; g < GB; ++g) {
+        const int n = (c0s[g] >= 0 && !full[g]) ? (int)min((int64_t)BS, (int64_t)L - c0s[g]) : 0;
+#pragma unroll
+        for (int e = 0; e < BS; ++e) sv[g][e] = e < n ? rowp[(c0s[g] + e) * cs] : 0.f;
+      }
+#pragma unroll
       for (int g = 0; g < GB; ++g)
 #pragma unroll
         for (int t = 0; t < BS / 4; ++t)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) kk[g][4 * t + e] = full[g] ? f2key(v[g][t][e]) : 0u;
-      // Strided, unaligned or the partial newest block: scalar loads.
-#pragma unroll
-      for (int g = 0; g < GB; ++g) {
-        if (c0s[g] >= 0 && !full[g]) {
-          const int n = (int)min((int64_t)BS, (int64_t)L - c0s[g]);
-#pragma unroll
-          for (int e = 0; e < BS; ++e)
-            if (e < n) kk[g][e] = f2key(rowp[(c0s[g] + e) * cs]);
-        }
-      }
+          for (int e = 0; e < 4; ++e)
+            kk[g][4 * t + e] = full[g] ? f2key(v[g][t][e]) : f2key(sv[g][4 * t + e]);
 #pragma unroll
       for (int g = 0; g < GB; ++g) {
         if (c0s[g] < 0) continue;
@@ -403,7 +430,8 @@ DSA_DEV void gather_kept(const float* rowp, int64_t cs, int B, int L, bool vec,
 template <int BS>
 DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* rowp,
                          const uint32_t* sel, int Kp, uint32_t tlo, bool canonical,
-                         bool no_low, Smem& sm) {
+                         bool no_low, Smem& sm, const uint32_t* nonkept = nullptr,
+                         int n_nonkept = 0) {
   const int L = rb.L, nlb = rb.nlb, B = p.B;
   const int64_t cs = p.col_stride;
   const bool vec = vec_ok(p, rowp);
@@ -457,16 +485,23 @@ DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* row
           const int f = idx - (int)C;
           const int i = div_b<BS>(f, B);
           const int e = f - i * B;
-          // number of kept blocks below the i-th non-kept block: the first j
-          // with sel[j] - j > i (sel[j] - j counts non-kept blocks below sel[j])
-          int lo = 0, hi = Kp;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if ((int64_t)sel[mid] - mid > i) hi = mid;
-            else lo = mid + 1;
+          // the i-th non-kept block, from the list when it holds it; else the
+          // number of kept blocks below it is the first j with sel[j] - j > i
+          // (sel[j] - j counts non-kept blocks below sel[j])
+          int64_t bnk;
+          if (i < n_nonkept) {
+            bnk = nonkept[i];
+          } else {
+            int lo = 0, hi = Kp;
+            while (lo < hi) {
+              const int mid = (lo + hi) >> 1;
+              if ((int64_t)sel[mid] - mid > i) hi = mid;
+              else lo = mid + 1;
+            }
+            bnk = i + lo;
           }
-          col = (int64_t)(i + lo) * B + e;
-          rank = f + lo * B;
+          col = bnk * B + e;
+          rank = f + (int)(bnk - i) * B;
         }
         tout[rank] = (int32_t)(rb.s + col);
       }
@@ -600,6 +635,7 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
   const bool need_keys = nlb > p.k_blocks || p.scores != nullptr;
   uint32_t T = 0, q = 0xFFFFFFFFu;
   bool no_low = false;
+  int n_nonkept = 0;
   if (!need_keys) {
     // Every live block is kept; the result follows from the bounds.
     for (int i = threadIdx.x; i < p.k_blocks; i += NT) bout[i] = i < nlb ? i : -1;
@@ -607,6 +643,8 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
   } else {
     float* sc = p.scores ? p.scores + (int64_t)r * p.nblocks : nullptr;
     uint32_t* keys = sm.keys();
+    // The select's histogram starts from zero; cleared while the loads fly.
+    for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
     bool low = false;
     score_blocks<BS>(rowp, p.col_stride, B, L, 0, nlb, nlb, vec, [&](int b, uint32_t k) {
       keys[b] = k;
@@ -614,26 +652,26 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
     }, low);
     no_low = __syncthreads_or(low) == 0;
     auto getk = [&](int i) { return keys[i]; };
-    if (nlb > Kp) wg_radix_select<NT>(nlb, (uint32_t)Kp, getk, sm, T, q);
-    wg_select_compact<NT>(nlb, T, q, getk,
-        [&](int i, uint32_t rank, bool kept, uint64_t word, int base) {
-          if (kept) {
-            bout[rank] = i;
-            sel[rank] = (uint32_t)i;
-          }
-          if (i == base) {
-            sm.bits[base >> 5] = (uint32_t)word;
-            sm.bits[(base >> 5) + 1] = (uint32_t)(word >> 32);
-          }
-        }, sm);
+    if (nlb > Kp) wg_radix_select<NT>(nlb, (uint32_t)Kp, getk, sm, T, q, true);
+    // One ordered pass: kept ids out, the lowest non-kept ids listed (for the
+    // token fill), and each non-kept block masked by the lane that owns it.
+    const bool do_mask = (p.flags & DSA_WRITE_MASK) && nlb > Kp;
+    uint32_t* nonkept = sm.tkey;
+    wg_rule_emit<NT>(nlb, T, q, getk, [&](int i, uint32_t rank, bool kept) {
+      if (kept) {
+        bout[rank] = i;
+        sel[rank] = (uint32_t)i;
+      } else {
+        const uint32_t nk = (uint32_t)i - rank;
+        if (nk < (uint32_t)TK_CAP) nonkept[nk] = (uint32_t)i;
+        if (do_mask) mask_block_lane<BS>(rowp, p.col_stride, B, L, vec, i);
+      }
+    }, sm);
+    n_nonkept = min(nlb - Kp, TK_CAP);
     for (int i = Kp + threadIdx.x; i < p.k_blocks; i += NT) bout[i] = -1;
-    __syncthreads();
-    if ((p.flags & DSA_WRITE_MASK) && nlb > Kp)
-      mask_blocks<BS>(rowp, p.col_stride, B, L, 0, nlb, vec,
-                      [&](int b) { return ((sm.bits[b >> 5] >> (b & 31)) & 1u) == 0u; });
   }
   __syncthreads();
-  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, true, no_low, sm);
+  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, true, no_low, sm, sm.tkey, n_nonkept);
 }
 
 // Workgroup-wide ticket on a workspace counter: true in the last of `total`
