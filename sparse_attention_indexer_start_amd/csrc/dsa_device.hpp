@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #define DSA_DEV __device__ __forceinline__
 
 namespace dsa {
@@ -110,6 +112,7 @@ struct __align__(16) Smem {
   uint32_t bits[CHUNK_CAP / 32];
   uint32_t wv[64];
   uint32_t misc[16];
+  uint64_t pfx[514];            // long-row block prefix over rows, then the chunk
   DSA_DEV uint32_t* keys() { return kid; }
   DSA_DEV uint32_t* ids() { return kid + LIST_CAP; }
 };
@@ -252,27 +255,25 @@ DSA_DEV void find_bin_zero(uint32_t* hist, uint32_t krem, Smem& sm, uint32_t& d,
   in_bin = sm.misc[5];
 }
 
-// Radix passes of the top-K rule below over keys visited by
-// for_keys(f) (f(key) once per element).  Digits of 12, 12 and 8 bits over
-// the 4096-word histogram, which must be zero on entry and is zero on return.
+// The bin starting at key `lo` (and everything above it) is kept whole.
+DSA_DEV void keep_from(uint32_t lo, uint32_t& T, uint32_t& q) {
+  if (lo == 0) {
+    T = 0;
+    q = 0xFFFFFFFFu;
+  } else {
+    T = lo - 1;
+    q = 0;
+  }
+}
+
+// Radix passes 2 and 3 (bits 19..8, then 7..0) of the top-K rule below, among
+// the keys whose top 12 bits equal those of `prefix`, krem of which are still
+// to be taken.  The 4096-word histogram must be zero on entry and is zero on
+// return.
 template <int NT, class ForKeys>
-DSA_DEV void radix_passes(ForKeys for_keys, uint32_t K, Smem& sm, uint32_t& T, uint32_t& q) {
-  uint32_t d, above, in_bin, krem = K;
-  auto done = [&](uint32_t lo) {   // the bin starting at key `lo` is kept whole
-    if (lo == 0) {
-      T = 0;
-      q = 0xFFFFFFFFu;
-    } else {
-      T = lo - 1;
-      q = 0;
-    }
-  };
-  for_keys([&](uint32_t k) { atomicAdd(&sm.hist[k >> 20], 1u); });
-  __syncthreads();
-  find_bin_zero<NT, 4096>(sm.hist, krem, sm, d, above, in_bin);
-  uint32_t prefix = d << 20;
-  krem -= above;
-  if (in_bin == krem) return done(prefix);
+DSA_DEV void radix_low_passes(ForKeys for_keys, uint32_t prefix, uint32_t krem, Smem& sm,
+                              uint32_t& T, uint32_t& q) {
+  uint32_t d, above, in_bin;
   const uint32_t p20 = prefix >> 20;
   for_keys([&](uint32_t k) {
     if ((k >> 20) == p20) atomicAdd(&sm.hist[(k >> 8) & 0xFFFu], 1u);
@@ -281,7 +282,7 @@ DSA_DEV void radix_passes(ForKeys for_keys, uint32_t K, Smem& sm, uint32_t& T, u
   find_bin_zero<NT, 4096>(sm.hist, krem, sm, d, above, in_bin);
   prefix |= d << 8;
   krem -= above;
-  if (in_bin == krem) return done(prefix);
+  if (in_bin == krem) return keep_from(prefix, T, q);
   const uint32_t p8 = prefix >> 8;
   for_keys([&](uint32_t k) {
     if ((k >> 8) == p8) atomicAdd(&sm.hist[k & 0xFFu], 1u);
@@ -290,6 +291,20 @@ DSA_DEV void radix_passes(ForKeys for_keys, uint32_t K, Smem& sm, uint32_t& T, u
   find_bin_zero<NT, 256>(sm.hist, krem, sm, d, above, in_bin);
   T = prefix | d;
   q = krem - above;
+}
+
+// Radix passes of the top-K rule below over keys visited by
+// for_keys(f) (f(key) once per element).  Digits of 12, 12 and 8 bits over
+// the 4096-word histogram, which must be zero on entry and is zero on return.
+template <int NT, class ForKeys>
+DSA_DEV void radix_passes(ForKeys for_keys, uint32_t K, Smem& sm, uint32_t& T, uint32_t& q) {
+  uint32_t d, above, in_bin;
+  for_keys([&](uint32_t k) { atomicAdd(&sm.hist[k >> 20], 1u); });
+  __syncthreads();
+  find_bin_zero<NT, 4096>(sm.hist, K, sm, d, above, in_bin);
+  const uint32_t krem = K - above;
+  if (in_bin == krem) return keep_from(d << 20, T, q);
+  radix_low_passes<NT>(for_keys, d << 20, krem, sm, T, q);
 }
 
 template <int NT, int U, class GetKey>
@@ -306,6 +321,34 @@ DSA_DEV void radix_select_regs(int n, uint32_t K, GetKey getk, Smem& sm, uint32_
     for (int u = 0; u < U; ++u)
       if ((int)threadIdx.x + u * NT < n) f(k[u]);
   }, K, sm, T, q);
+}
+
+// The (T, q) rule for the top K of getk(0..n), n <= 8 * NT, when the top
+// 12-bit digit of the K-th key is known to be d20 and `above` keys have a
+// larger top digit (so krem = K - above are taken from digit d20).
+template <int NT, class GetKey>
+DSA_DEV void wg_radix_select_low(int n, uint32_t d20, uint32_t krem, GetKey getk, Smem& sm,
+                                 uint32_t& T, uint32_t& q) {
+  for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
+  __syncthreads();
+  auto run = [&](auto u_tag) {
+    constexpr int U = decltype(u_tag)::value;
+    uint32_t k[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = (int)threadIdx.x + u * NT;
+      k[u] = i < n ? getk(i) : 0u;
+    }
+    radix_low_passes<NT>([&](auto f) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if ((int)threadIdx.x + u * NT < n) f(k[u]);
+    }, d20 << 20, krem, sm, T, q);
+  };
+  if (n <= NT) run(std::integral_constant<int, 1>{});
+  else if (n <= 2 * NT) run(std::integral_constant<int, 2>{});
+  else if (n <= 4 * NT) run(std::integral_constant<int, 4>{});
+  else run(std::integral_constant<int, 8>{});
 }
 
 // Top-K selection rule over getk(0..n), 1 <= K <= n: element i is kept iff

@@ -42,7 +42,8 @@ namespace dsa {
 
 constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int UNROLL = 4;      // float4 loads in flight per lane in the score pass
-constexpr int ROW_STATE = 8;   // pass-1 ticket, pass-2 ticket, digit, ready flag, low flag
+constexpr int ROW_STATE = 8;   // pass-1 ticket, pass-2 ticket, digit, ready flag, low flag,
+                               // keys above the digit
 constexpr int UNROLL_STRIDED = 8;   // scalar loads in flight per lane: 4 * this
 // One workgroup reads at most a few tens of GB/s, so a row longer than this is
 // split over its P workgroups even when its block keys would fit in LDS.
@@ -62,24 +63,32 @@ struct Params {
   int64_t width, row_stride, col_stride;
   int32_t rows, B, k_blocks, k_tokens, starts_repeat, ends_repeat;
   int32_t nblocks, P, G, small_blocks, phase_base;
+  // Balanced split (rows <= NT): workgroups [0, rows) own the short rows,
+  // then NQ pass-1 and NQ pass-2 workgroups share the long rows' blocks.
+  int32_t balanced, NQ, cnt_stride;
 
   // A row is handled by one workgroup when its keys fit in LDS and it is short
   // (or the shape gives each row a single workgroup anyway).
-  __device__ bool one_group(int32_t nlb, int32_t L) const {
-    return nlb <= small_blocks && (L <= SMALL_COLS || P == 1);
+  __device__ __forceinline__ bool one_group(int32_t nlb, int32_t L) const {
+    return nlb <= small_blocks && (L <= SMALL_COLS || (P == 1 && !balanced));
   }
   uint32_t flags;
   uint32_t* ws_key;    // [rows][nblocks]  block keys of long rows
   uint32_t* ws_list;   // [rows][nblocks]  listed blocks, per chunk
   uint32_t* ws_flat;   // [rows][nblocks]  listed blocks, gathered (overflow)
   uint32_t* ws_hist;   // [rows][HIST_WORDS]
-  uint32_t* ws_cnt;    // [rows][P]
+  uint32_t* ws_cnt;    // [rows][max(P, NQ)]  list length per piece
   uint32_t* ws_row;    // [rows][ROW_STATE]
   uint32_t* ws_sel;    // [rows][k_blocks]   (overflow)
   uint32_t* ws_dblk;   // [rows][dblk_cap]   (overflow)
   uint32_t* ws_tkey;   // [rows][tkey_cap]   (overflow)
   uint32_t* ws_tcol;   // [rows][tkey_cap]   (overflow)
+  uint32_t* ws_lkey;   // [rows][nblocks]  keys of the listed blocks (beside ws_list)
+  uint32_t* ws_ccol;   // [rows][2 * nblocks]  token candidates: column (row-relative)
+  uint32_t* ws_ckey;   // [rows][2 * nblocks]  token candidates: key
+  uint32_t* ws_ccnt;   // [rows][max(P, NQ)]  candidates per piece (~0u: overflow)
   int64_t dblk_cap, tkey_cap;
+  int32_t pregather;   // K_blk * B > K_tok and B in {4, 8, 16}
   uint32_t* status;
 };
 
@@ -120,6 +129,41 @@ DSA_DEV void chunk_of(const Row& rb, int P, int part, int& b0, int& b1) {
   const int cb = (rb.nlb + P - 1) / P;
   b0 = min(rb.nlb, part * cb);
   b1 = min(rb.nlb, b0 + cb);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced split.  The long rows' blocks are concatenated in row order
+// (sm.pfx[r] = blocks of long rows before r, sm.pfx[rows] = total T) and
+// worker w of a pass takes [w * C, (w + 1) * C) of them, C = ceil(T / NQ)
+// (sm.pfx[rows + 1]), so every worker streams the same number of blocks
+// whatever the row lengths.  The part of a row inside one worker's range is a
+// piece.
+// ---------------------------------------------------------------------------
+DSA_DEV uint64_t worker_lo(const Smem& sm, int rows, int w) {
+  const uint64_t T = sm.pfx[rows], C = sm.pfx[rows + 1];
+  const uint64_t lo = (uint64_t)w * C;
+  return lo < T ? lo : T;
+}
+// The worker whose range holds concatenated block x < T: floor(x / C), from a
+// double quotient corrected by one step either way (x < 2^53).
+DSA_DEV int worker_of(const Smem& sm, int rows, uint64_t x) {
+  const uint64_t C = sm.pfx[rows + 1];
+  uint64_t q = (uint64_t)((double)x / (double)C);
+  if (q * C > x) --q;
+  else if ((q + 1) * C <= x) ++q;
+  return (int)q;
+}
+
+// Pieces of long row r and the first block of piece j (row-relative).
+DSA_DEV int piece_count(const Params& p, const Smem& sm, const Row& rb, int r) {
+  if (!p.balanced) return p.P;
+  return worker_of(sm, p.rows, sm.pfx[r + 1] - 1) - worker_of(sm, p.rows, sm.pfx[r]) + 1;
+}
+DSA_DEV int piece_start(const Params& p, const Smem& sm, const Row& rb, int r, int j) {
+  if (!p.balanced) return min(rb.nlb, j * ((rb.nlb + p.P - 1) / p.P));
+  if (j == 0) return 0;
+  const int w = worker_of(sm, p.rows, sm.pfx[r]) + j;
+  return (int)(worker_lo(sm, p.rows, w) - sm.pfx[r]);
 }
 
 template <int BS>
@@ -689,11 +733,10 @@ DSA_DEV bool arrive_last(uint32_t* ticket, uint32_t total, Smem& sm) {
 // workgroup of the row the digit of the K_blk-th score.
 // ---------------------------------------------------------------------------
 template <int BS>
-DSA_DEV void long_pass1(const Params& p, int r, int part, const Row& rb, Smem& sm) {
+DSA_DEV void long_pass1(const Params& p, int r, int b0, int b1, int npieces, const Row& rb,
+                        Smem& sm) {
   float* rowp = row_ptr(p, r, rb);
   const bool vec = vec_ok(p, rowp);
-  int b0, b1;
-  chunk_of(rb, p.P, part, b0, b1);
   for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
   __syncthreads();
   uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
@@ -711,7 +754,7 @@ DSA_DEV void long_pass1(const Params& p, int r, int part, const Row& rb, Smem& s
     const uint32_t c = sm.hist[j];
     if (c) atomicAdd(&gh[j], c);
   }
-  if (!arrive_last(&st[0], (uint32_t)p.P, sm)) return;
+  if (!arrive_last(&st[0], (uint32_t)npieces, sm)) return;
   constexpr int PER = HIST_WORDS / NT;
   uint32_t h[PER];
 #pragma unroll
@@ -726,6 +769,7 @@ DSA_DEV void long_pass1(const Params& p, int r, int part, const Row& rb, Smem& s
   find_bin<NT>(sm.hist, HIST_WORDS, (uint32_t)min(p.k_blocks, rb.nlb), sm, d, above, in_bin);
   if (threadIdx.x == 0) {
     st_shared(&st[2], d);
+    st_shared(&st[5], above);
     st_shared(&st[0], 0u);
     vm_drain();
     st_shared(&st[3], 1u);            // the row's digit is ready
@@ -734,23 +778,27 @@ DSA_DEV void long_pass1(const Params& p, int r, int part, const Row& rb, Smem& s
 
 // ---------------------------------------------------------------------------
 // Last workgroup of pass 2: exact selection among the listed blocks, masks of
-// the rejected ones, outputs, token top-k.
+// the rejected ones, outputs, token top-k.  General form: the list is
+// gathered from the per-piece lists and the token top-k reads the kept
+// blocks' values back from the logits.
 // ---------------------------------------------------------------------------
 template <int BS>
-DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
+DSA_DEV void final_row_general(const Params& p, int r, const Row& rb, Smem& sm) {
   float* rowp = row_ptr(p, r, rb);
-  const int nlb = rb.nlb, B = p.B, P = p.P;
+  const int nlb = rb.nlb, B = p.B;
+  const int P = piece_count(p, sm, rb, r);   // <= NT
   const int64_t cs = p.col_stride;
-  const int cb = (nlb + P - 1) / P;
   const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   const uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
-  // Exclusive prefix of the per-chunk list lengths (P <= NT).
-  const uint32_t c = (int)threadIdx.x < P ? ld_shared(&p.ws_cnt[(int64_t)r * P + threadIdx.x]) : 0u;
+  // Exclusive prefix of the per-piece list lengths; piece j's list starts at
+  // its first block (sm.hist[2 * NT + j]).
+  const uint32_t c = (int)threadIdx.x < P ? ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + threadIdx.x]) : 0u;
   uint32_t n_list;
   const uint32_t off = wg_excl_scan<NT>(c, sm.wv, n_list);
   if ((int)threadIdx.x < P) {
     sm.hist[threadIdx.x] = off;
     sm.hist[NT + threadIdx.x] = c;
+    sm.hist[2 * NT + threadIdx.x] = (uint32_t)piece_start(p, sm, rb, r, threadIdx.x);
   }
   __syncthreads();
   const bool in_lds = n_list <= (uint32_t)LIST_CAP;
@@ -772,7 +820,7 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
             if (sm.hist[mid] <= (uint32_t)i) lo = mid;
             else hi = mid - 1;
           }
-          v[u] = ld_shared(&wl[min(nlb, lo * cb) + (i - (int)sm.hist[lo])]);
+          v[u] = ld_shared(&wl[sm.hist[2 * NT + lo] + (i - (int)sm.hist[lo])]);
         }
       }
 #pragma unroll
@@ -824,14 +872,189 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
   token_stage<BS>(p, r, rb, rowp, sel, Kp, T, true, no_low, sm);
 }
 
-// Thread 0 waits (time-bounded) for the row's ready flag.  Returns false if
-// the wait gave up (status bit 1).
-DSA_DEV bool wait_ready(const Params& p, const uint32_t* flag, Smem& sm) {
+// Largest j < P with offs[j] <= i (offs nondecreasing, offs[0] = 0).
+DSA_DEV int piece_of(const uint32_t* offs, int P, uint32_t i) {
+  int lo = 0, hi = P - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offs[mid] <= i) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Last workgroup of pass 2, with the token candidates gathered by pass 2.
+// The listed blocks (every block whose key's top digit reaches the digit d of
+// the K_blk-th score) come with their keys, so the block top-k only resolves
+// the ties inside d's bin.  When at least K_tok values of the kept blocks
+// reach beta = d << 20 (each kept block other than the newest has its maximum
+// there), the K_tok best columns of the masked row are among the candidates
+// (values >= beta of listed blocks) that lie in kept blocks: they are ranked
+// there.  Otherwise, and whenever the lists do not fit, the general form runs.
+template <int BS>
+DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
+  constexpr bool PG_OK = BS >= 4 && BS <= 16;
+  if constexpr (!PG_OK) {
+    final_row_general<BS>(p, r, rb, sm);
+  } else {
+    if (!p.pregather) return final_row_general<BS>(p, r, rb, sm);
+    const int nlb = rb.nlb, P = piece_count(p, sm, rb, r);
+    const int Kp = min(p.k_blocks, nlb), Kt = min(p.k_tokens, rb.L);
+    uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
+    const uint32_t digit = ld_shared(&st[2]), above = ld_shared(&st[5]);
+    const uint32_t beta = digit << 20;
+    const int t = (int)threadIdx.x;
+    const bool jt = t < P;
+    const uint32_t c = jt ? ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + t]) : 0u;
+    const uint32_t cc = jt ? ld_shared(&p.ws_ccnt[(int64_t)r * p.cnt_stride + t]) : 0u;
+    const bool ovf = __syncthreads_or(cc == 0xFFFFFFFFu) != 0;
+    uint32_t n_list, n_cand;
+    const uint32_t off = wg_excl_scan<NT>(c, sm.wv, n_list);
+    const uint32_t coff = wg_excl_scan<NT>(ovf ? 0u : cc, sm.wv, n_cand);
+    const bool fast = !ovf && beta > KEY_NEG_INF && rb.L > p.k_tokens &&
+                      n_list >= (uint32_t)Kp && n_list <= (uint32_t)LIST_CAP &&
+                      n_cand <= (uint32_t)TK_CAP && nlb <= BITMAP_BITS && Kp <= SEL_CAP;
+    if (!fast) return final_row_general<BS>(p, r, rb, sm);
+
+    float* rowp = row_ptr(p, r, rb);
+    const bool vec = vec_ok(p, rowp);
+    uint32_t* lkeys = sm.keys();
+    uint32_t* lids = sm.ids();
+    uint32_t* tk = sm.tkey;
+    // Piece tables (kept until the candidates are gathered; the selects
+    // below clear sm.hist): candidate offsets, first blocks, list offsets.
+    uint32_t* coffs = sm.sel;
+    uint32_t* pstart = sm.sel + NT;
+    uint32_t* loffs = sm.sel + 2 * NT;
+    if (jt) {
+      coffs[t] = coff;
+      pstart[t] = (uint32_t)piece_start(p, sm, rb, r, t);
+      loffs[t] = off;
+    }
+    __syncthreads();
+    // Gather the list (ids and keys) and the candidate keys in piece order.
+    const uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
+    const uint32_t* wlk = p.ws_lkey + (int64_t)r * p.nblocks;
+    const int64_t creg = (int64_t)r * 2 * p.nblocks;
+    constexpr int U = 8;
+    for (int i0 = t; i0 < (int)n_list; i0 += NT * U) {
+      uint32_t a[U], b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        a[u] = b[u] = 0;
+        if (i < (int)n_list) {
+          const int j = piece_of(loffs, P, (uint32_t)i);
+          const uint32_t src = pstart[j] + ((uint32_t)i - loffs[j]);
+          a[u] = ld_shared(&wl[src]);
+          b[u] = ld_shared(&wlk[src]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        if (i < (int)n_list) {
+          lids[i] = a[u];
+          lkeys[i] = b[u];
+        }
+      }
+    }
+    for (int i0 = t; i0 < (int)n_cand; i0 += NT * U) {
+      uint32_t a[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        a[u] = 0;
+        if (i < (int)n_cand) {
+          const int j = piece_of(coffs, P, (uint32_t)i);
+          a[u] = ld_shared(&p.ws_ckey[creg + 2 * (int64_t)pstart[j] + ((uint32_t)i - coffs[j])]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + u * NT < (int)n_cand) tk[i0 + u * NT] = a[u];
+    }
+    __syncthreads();
+
+    // Block top-k: the keys above d's bin are kept; the ties inside it are
+    // resolved on the lower 20 bits.  Leaves sm.hist zero.
+    uint32_t T = 0, q = 0xFFFFFFFFu;
+    auto getk = [&](int i) { return lkeys[i]; };
+    if ((int)n_list > Kp) {
+      wg_radix_select_low<NT>((int)n_list, digit, (uint32_t)Kp - above, getk, sm, T, q);
+    } else {
+      for (int j = t; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
+      __syncthreads();
+    }
+    const bool wm = (p.flags & DSA_WRITE_MASK) != 0;
+    int32_t* bout = p.block_ids + (int64_t)r * p.k_blocks;
+    wg_rule_emit<NT>((int)n_list, T, q, getk, [&](int i, uint32_t rank, bool kept) {
+      const uint32_t b = lids[i];
+      if (kept) {
+        bout[rank] = (int32_t)b;
+        atomicOr(&sm.hist[b >> 5], 1u << (b & 31));    // kept-block bitmap
+      } else if (wm) {
+        mask_block_lane<BS>(rowp, p.col_stride, BS, rb.L, vec, b);
+      }
+    }, sm);
+    for (int i = Kp + t; i < p.k_blocks; i += NT) bout[i] = -1;
+    __syncthreads();
+
+    // Candidate columns; a candidate outside the kept blocks ranks nowhere.
+    uint32_t* tc = sm.keys();
+    uint32_t nk = 0;
+    for (int i0 = t; i0 < (int)n_cand; i0 += NT * U) {
+      uint32_t a[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        a[u] = 0;
+        if (i < (int)n_cand) {
+          const int j = piece_of(coffs, P, (uint32_t)i);
+          a[u] = ld_shared(&p.ws_ccol[creg + 2 * (int64_t)pstart[j] + ((uint32_t)i - coffs[j])]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        if (i < (int)n_cand) {
+          const uint32_t b = a[u] / BS;
+          tc[i] = a[u];
+          if ((sm.hist[b >> 5] >> (b & 31)) & 1u) ++nk;
+          else tk[i] = 0u;
+        }
+      }
+    }
+    uint32_t n_keep;
+    (void)wg_excl_scan<NT>(nk, sm.wv, n_keep);
+    if ((int)n_keep < Kt) {
+      // Fewer kept values reach beta than tokens wanted: rank the kept
+      // blocks' columns from the logits.
+      for (int j = t; j < Kp; j += NT) sm.sel[j] = ld_shared(reinterpret_cast<const uint32_t*>(bout + j));
+      __syncthreads();
+      const bool no_low = ld_shared(&st[4]) == 0u;
+      token_stage<BS>(p, r, rb, rowp, sm.sel, Kp, T, true, no_low, sm);
+      return;
+    }
+    uint32_t T2 = 0, q2 = 0xFFFFFFFFu;
+    auto gk = [&](int i) { return tk[i]; };
+    if ((int)n_cand > Kt) wg_radix_select<NT>((int)n_cand, (uint32_t)Kt, gk, sm, T2, q2);
+    int32_t* tout = p.token_ids + (int64_t)r * p.k_tokens;
+    wg_rule_emit<NT>((int)n_cand, T2, q2, gk, [&](int i, uint32_t rank, bool kept) {
+      if (kept) tout[rank] = (int32_t)(rb.s + tc[i]);
+    }, sm);
+    for (int i = Kt + t; i < p.k_tokens; i += NT) tout[i] = -1;
+  }
+}
+
+// Thread 0 waits (time-bounded) until a row-state word reaches `target`.
+// Returns false if the wait gave up (status bit 1).
+DSA_DEV bool wait_at_least(const Params& p, const uint32_t* word, uint32_t target, Smem& sm) {
   if (threadIdx.x == 0) {
     uint32_t ok = 1;
-    if (ld_shared(flag) == 0u) {
+    if (ld_shared(word) < target) {
       const uint64_t t0 = wall_clock64();
-      while (ld_shared(flag) == 0u) {
+      while (ld_shared(word) < target) {
         __builtin_amdgcn_s_sleep(2);
         if (wall_clock64() - t0 > WAIT_LIMIT_TICKS) {
           atomicOr(p.status, 2u);
@@ -847,22 +1070,37 @@ DSA_DEV bool wait_ready(const Params& p, const uint32_t* flag, Smem& sm) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2 of a long row: mask blocks below the digit, list the others; the
-// last workgroup of the row finishes it.
+// Pass 2 of a long row, one piece: first the list of the piece's blocks whose
+// top digit reaches the row's digit (and their token candidates), published
+// with a count on the row's pass-2 ticket; then -inf over every other block of
+// the piece.  The row's final workgroup starts as soon as all lists are in.
 // ---------------------------------------------------------------------------
 template <int BS>
-DSA_DEV void long_pass2(const Params& p, int r, int part, const Row& rb, Smem& sm) {
+DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const Row& rb,
+                        Smem& sm) {
   uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
-  if (!wait_ready(p, &st[3], sm)) return;
+  if (!wait_at_least(p, &st[3], 1u, sm)) return;
   float* rowp = row_ptr(p, r, rb);
   const bool vec = vec_ok(p, rowp);
-  int b0, b1;
-  chunk_of(rb, p.P, part, b0, b1);
   const uint32_t digit = ld_shared(&st[2]);
   const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
+  uint32_t* wlk = p.ws_lkey + (int64_t)r * p.nblocks;
+  // Token candidates: every live value of a listed block whose key reaches
+  // the lower edge beta of the digit's bin, in column order, into this
+  // piece's region of 2 entries per block.
+  constexpr bool PG_OK = BS >= 4 && BS <= 16;
+  const uint32_t beta = digit << 20;
+  const bool pg = PG_OK && p.pregather && beta > KEY_NEG_INF;
+  const int64_t creg = (int64_t)r * 2 * p.nblocks + 2 * (int64_t)b0;
+  const uint32_t ccap = 2u * (uint32_t)(b1 - b0);
   uint32_t* keys = sm.keys();
-  uint32_t cnt = 0;
+  uint32_t* lids = sm.ids();
+  // Listed flags of the whole piece, kept for the masking phase when they fit.
+  const bool keep_bits = b1 - b0 <= BITMAP_BITS;
+  uint32_t* lbits = sm.hist;
+  uint32_t cnt = 0, ccnt = 0;
+  bool cover = false;
   for (int s0 = b0; s0 < b1; s0 += CHUNK_CAP) {
     const int n = min(b1 - s0, CHUNK_CAP);
     constexpr int U = CHUNK_CAP / NT;
@@ -882,21 +1120,98 @@ DSA_DEV void long_pass2(const Params& p, int r, int part, const Row& rb, Smem& s
         if (i < n && (keys[i] >> 20) >= digit) word |= 1u << j;
       }
       sm.bits[w] = word;
+      if (keep_bits) lbits[((s0 - b0) >> 5) + w] = word;
     }
     const uint32_t base = cnt;
-    cnt += wg_compact<NT>(n, [&](int i) { return (keys[i] >> 20) >= digit; },
-                          [&](int i, uint32_t rank) { st_shared(&wl[b0 + base + rank], (uint32_t)(s0 + i)); },
-                          sm);
+    const uint32_t nl = wg_compact<NT>(n, [&](int i) { return (keys[i] >> 20) >= digit; },
+        [&](int i, uint32_t rank) {
+          const uint32_t b = (uint32_t)(s0 + i);
+          st_shared(&wl[b0 + base + rank], b);
+          st_shared(&wlk[b0 + base + rank], keys[i]);
+          lids[rank] = b;
+        }, sm);
+    cnt += nl;
     __syncthreads();
-    if (p.flags & DSA_WRITE_MASK)
-      mask_blocks<BS>(rowp, p.col_stride, p.B, rb.L, s0, s0 + n, vec, [&](int b) {
-        const int i = b - s0;
-        return ((sm.bits[i >> 5] >> (i & 31)) & 1u) == 0u;
-      });
+    if constexpr (PG_OK) {
+      if (pg) {
+        // One listed block per thread per round: its values (loads issued
+        // together), the count at or above beta, then ordered stores.
+        for (int j0 = 0; j0 < (int)nl; j0 += NT) {
+          const int j = j0 + (int)threadIdx.x;
+          uint32_t kk[BS];
+          int64_t c0 = 0;
+          int nv = 0;
+          if (j < (int)nl) {
+            c0 = (int64_t)lids[j] * BS;
+            nv = (int)min((int64_t)BS, (int64_t)rb.L - c0);
+            if (vec && nv == BS) {
+              f4v v[BS / 4];
+#pragma unroll
+              for (int t = 0; t < BS / 4; ++t) v[t] = *reinterpret_cast<const f4v*>(rowp + c0 + 4 * t);
+#pragma unroll
+              for (int t = 0; t < BS / 4; ++t) {
+                kk[4 * t] = f2key(v[t].x);
+                kk[4 * t + 1] = f2key(v[t].y);
+                kk[4 * t + 2] = f2key(v[t].z);
+                kk[4 * t + 3] = f2key(v[t].w);
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < BS; ++e) kk[e] = e < nv ? f2key(rowp[(c0 + e) * p.col_stride]) : 0u;
+            }
+          }
+          uint32_t c = 0;
+#pragma unroll
+          for (int e = 0; e < BS; ++e) c += (e < nv && kk[e] >= beta) ? 1u : 0u;
+          uint32_t tot;
+          uint32_t o = wg_excl_scan<NT>(c, sm.wv, tot);
+          if (ccnt + tot > ccap) {
+            cover = true;
+          } else {
+#pragma unroll
+            for (int e = 0; e < BS; ++e) {
+              if (e < nv && kk[e] >= beta) {
+                st_shared(&p.ws_ccol[creg + ccnt + o], (uint32_t)(c0 + e));
+                st_shared(&p.ws_ckey[creg + ccnt + o], kk[e]);
+                ++o;
+              }
+            }
+            ccnt += tot;
+          }
+        }
+      }
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) st_shared(&p.ws_cnt[(int64_t)r * p.P + part], cnt);
-  if (!arrive_last(&st[1], (uint32_t)p.P, sm)) return;
+  if (threadIdx.x == 0) {
+    st_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + part], cnt);
+    st_shared(&p.ws_ccnt[(int64_t)r * p.cnt_stride + part], (pg && !cover) ? ccnt : 0xFFFFFFFFu);
+  }
+  (void)arrive_last(&st[1], 0u, sm);
+  if (!(p.flags & DSA_WRITE_MASK)) return;
+  if (keep_bits) {
+    mask_blocks<BS>(rowp, p.col_stride, p.B, rb.L, b0, b1, vec, [&](int b) {
+      const int i = b - b0;
+      return ((lbits[i >> 5] >> (i & 31)) & 1u) == 0u;
+    });
+    return;
+  }
+  for (int s0 = b0; s0 < b1; s0 += CHUNK_CAP) {
+    const int n = min(b1 - s0, CHUNK_CAP);
+    for (int i = threadIdx.x; i < n; i += NT) keys[i] = ld_shared(&wk[s0 + i]);
+    __syncthreads();
+    mask_blocks<BS>(rowp, p.col_stride, p.B, rb.L, s0, s0 + n, vec,
+                    [&](int b) { return (keys[b - s0] >> 20) < digit; });
+    __syncthreads();
+  }
+}
+
+// The final workgroup of a long row: waits until every pass-2 piece of the row
+// has published its list, then settles the row and resets its state.
+template <int BS>
+DSA_DEV void final_wg(const Params& p, int r, const Row& rb, int npieces, Smem& sm) {
+  uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
+  if (!wait_at_least(p, &st[1], (uint32_t)npieces, sm)) return;
   final_row<BS>(p, r, rb, sm);
   if (threadIdx.x == 0) {
     st_shared(&st[1], 0u);
@@ -910,26 +1225,143 @@ DSA_DEV void long_pass2(const Params& p, int r, int part, const Row& rb, Smem& s
 // a short row); otherwise pass 2.
 // ---------------------------------------------------------------------------
 template <int BS>
-__global__ __launch_bounds__(NT) void k_fused(Params p) {
+DSA_DEV void own_short_row(const Params& p, int r, const Row& rb, Smem& sm) {
+  if (rb.bad && threadIdx.x == 0) atomicOr(p.status, 1u);
+  if (rb.L == 0) {
+    write_empty_row(p, r);
+    return;
+  }
+  small_row<BS>(p, r, rb, sm);
+}
+
+// sm.pfx[0..rows]: blocks of long rows before each row (rows <= NT).
+DSA_DEV void build_plan(const Params& p, Smem& sm) {
+  const int t = (int)threadIdx.x;
+  uint32_t v = 0;
+  if (t < p.rows) {
+    const Row rb = row_bounds(p, t);
+    if (rb.L > 0 && !p.one_group(rb.nlb, rb.L)) v = (uint32_t)rb.nlb;
+  }
+  uint32_t total;
+  const uint32_t x = wg_excl_scan<NT>(v, sm.wv, total);
+  if (t < p.rows) sm.pfx[t] = x;
+  if (t == 0) {
+    sm.pfx[p.rows] = total;
+    sm.pfx[p.rows + 1] = ((uint64_t)total + (uint64_t)p.NQ - 1) / (uint64_t)p.NQ;
+  }
+  __syncthreads();
+}
+
+// Start of piece k of the balanced split, k in [0, NQ + rows - 1]: the pieces
+// are cut at every worker boundary min(w * C, T), w = 1..NQ-1, and at every
+// row boundary pfx[r], r = 1..rows-1 (empty pieces where two coincide or a
+// row is short).  Piece k starts at element k - 1 of the merged boundary list
+// (merge-path search; on ties worker boundaries come first), piece 0 at 0 and
+// the last piece ends at T.
+DSA_DEV uint64_t piece_bound(const Params& p, const Smem& sm, int k) {
+  const uint64_t T = sm.pfx[p.rows];
+  const int nA = p.NQ - 1, nB = p.rows - 1;
+  if (k <= 0) return 0;
+  if (k > nA + nB) return T;
+  const int m = k - 1;
+  auto A = [&](int i) { return worker_lo(sm, p.rows, i + 1); };
+  auto Bv = [&](int j) { return sm.pfx[j + 1]; };
+  int lo = max(0, m + 1 - nB), hi = min(m + 1, nA);
+  while (lo < hi) {
+    const int i = (lo + hi) >> 1;
+    if (A(i) <= Bv(m - i)) lo = i + 1;
+    else hi = i;
+  }
+  const int i = lo, j = m + 1 - lo;
+  const uint64_t a = i > 0 ? A(i - 1) : 0, b = j > 0 ? Bv(j - 1) : 0;
+  return a > b ? a : b;
+}
+
+// One piece of one pass of the balanced split (one workgroup per piece).
+template <int BS>
+DSA_DEV void balanced_piece(const Params& p, int k, bool pass2, Smem& sm) {
+  build_plan(p, sm);
+  const uint64_t T = sm.pfx[p.rows];
+  if (T == 0) return;
+  const uint64_t s0 = piece_bound(p, sm, k), s1 = piece_bound(p, sm, k + 1);
+  if (s0 >= s1) return;
+  int r;
+  {
+    int a = 0, b = p.rows - 1;   // largest r with pfx[r] <= s0: the long row holding s0
+    while (a < b) {
+      const int m = (a + b + 1) >> 1;
+      if (sm.pfx[m] <= s0) a = m;
+      else b = m - 1;
+    }
+    r = a;
+  }
+  const Row rb = row_bounds(p, r);
+  const uint64_t rs = sm.pfx[r], re = sm.pfx[r + 1];
+  const int w0 = worker_of(sm, p.rows, rs);
+  const int np = worker_of(sm, p.rows, re - 1) - w0 + 1;
+  const int part = worker_of(sm, p.rows, s0) - w0;
+  const int b0 = (int)(s0 - rs), b1 = (int)(s1 - rs);
+  if (!pass2) long_pass1<BS>(p, r, b0, b1, np, rb, sm);
+  else long_pass2<BS>(p, r, b0, b1, part, rb, sm);
+}
+
+// ---------------------------------------------------------------------------
+// The fused kernels.
+// k_fused (per-row split): grid index g + phase_base < G is pass 1 of part
+// g / rows of row g % rows (and the whole of a short row), [G, 2G) pass 2,
+// then one final workgroup per row.
+// k_fused_bal (balanced split): [0, rows) own the short rows, then one
+// workgroup per pass-1 piece, one per pass-2 piece (NQ + rows - 1 each), then
+// one final workgroup per row.  Every wait is on lower grid indices only.
+// ---------------------------------------------------------------------------
+template <int BS>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_fused(Params p) {
   __shared__ Smem sm;
   int g = (int)blockIdx.x + p.phase_base;
+  if (g >= 2 * p.G) {                 // final workgroups, one per row
+    const int r = g - 2 * p.G;
+    const Row rb = row_bounds(p, r);
+    if (p.one_group(rb.nlb, rb.L) || rb.L == 0) return;
+    final_wg<BS>(p, r, rb, p.P, sm);
+    return;
+  }
   const bool pass2 = g >= p.G;
   if (pass2) g -= p.G;
   int r, part;
   part_of(p, g, r, part);
   const Row rb = row_bounds(p, r);
-  if (p.one_group(rb.nlb, rb.L)) {
+  if (p.one_group(rb.nlb, rb.L) || rb.L == 0) {
     if (pass2 || part != 0) return;
-    if (rb.bad && threadIdx.x == 0) atomicOr(p.status, 1u);
-    if (rb.L == 0) {
-      write_empty_row(p, r);
-      return;
-    }
-    small_row<BS>(p, r, rb, sm);
+    own_short_row<BS>(p, r, rb, sm);
     return;
   }
-  if (!pass2) long_pass1<BS>(p, r, part, rb, sm);
-  else long_pass2<BS>(p, r, part, rb, sm);
+  int b0, b1;
+  chunk_of(rb, p.P, part, b0, b1);
+  if (!pass2) long_pass1<BS>(p, r, b0, b1, p.P, rb, sm);
+  else long_pass2<BS>(p, r, b0, b1, part, rb, sm);
+}
+
+template <int BS>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_fused_bal(Params p) {
+  __shared__ Smem sm;
+  int g = (int)blockIdx.x + p.phase_base;
+  if (g < p.rows) {
+    const Row rb = row_bounds(p, g);
+    if (p.one_group(rb.nlb, rb.L) || rb.L == 0) own_short_row<BS>(p, g, rb, sm);
+    return;
+  }
+  g -= p.rows;
+  const int npc = p.NQ + p.rows - 1;   // pieces per pass
+  if (g >= 2 * npc) {                  // final workgroups, one per row
+    const int r = g - 2 * npc;
+    build_plan(p, sm);
+    if (sm.pfx[r + 1] == sm.pfx[r]) return;   // not a long row
+    const Row rb = row_bounds(p, r);
+    final_wg<BS>(p, r, rb, piece_count(p, sm, rb, r), sm);
+    return;
+  }
+  const bool pass2 = g >= npc;
+  balanced_piece<BS>(p, pass2 ? g - npc : g, pass2, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1032,11 +1464,13 @@ struct dsa_ctx {
   int device;
   int cus;
   int32_t nblocks, P, G, small_blocks;
+  int32_t balanced, NQ, cnt_stride;
   int64_t dblk_cap, tkey_cap;
   void* ws;
   size_t ws_bytes;
   uint32_t *ws_key, *ws_list, *ws_flat, *ws_hist, *ws_cnt, *ws_row, *ws_sel, *ws_dblk, *ws_tkey,
-      *ws_tcol, *status;
+      *ws_tcol, *ws_lkey, *ws_ccol, *ws_ckey, *ws_ccnt, *status;
+  int32_t pregather;
   uint32_t magic;
 };
 
@@ -1100,6 +1534,9 @@ Params base_params(const dsa_ctx* c) {
   p.nblocks = c->nblocks;
   p.P = c->P;
   p.G = c->G;
+  p.balanced = c->balanced;
+  p.NQ = c->NQ;
+  p.cnt_stride = c->cnt_stride;
   p.small_blocks = c->small_blocks;
   p.ws_key = c->ws_key;
   p.ws_list = c->ws_list;
@@ -1111,6 +1548,11 @@ Params base_params(const dsa_ctx* c) {
   p.ws_dblk = c->ws_dblk;
   p.ws_tkey = c->ws_tkey;
   p.ws_tcol = c->ws_tcol;
+  p.ws_lkey = c->ws_lkey;
+  p.ws_ccol = c->ws_ccol;
+  p.ws_ckey = c->ws_ckey;
+  p.ws_ccnt = c->ws_ccnt;
+  p.pregather = c->pregather;
   p.dblk_cap = c->dblk_cap;
   p.tkey_cap = c->tkey_cap;
   p.status = c->status;
@@ -1128,7 +1570,15 @@ bool empty_shape(const dsa_ctx* c) { return c->sh.rows == 0 || c->sh.width == 0;
 // Whether some row of this shape can be split over its P workgroups (the
 // device-side rule of Params::one_group, taken at the widest row).
 bool may_split(const dsa_ctx* c) {
-  return c->nblocks > c->small_blocks || (c->sh.width > SMALL_COLS && c->P > 1);
+  return c->nblocks > c->small_blocks ||
+         (c->sh.width > SMALL_COLS && (c->P > 1 || c->balanced));
+}
+
+// Workgroups of the one-launch fused call.
+int fused_grid(const dsa_ctx* c) {
+  if (!may_split(c)) return c->G;
+  if (c->balanced) return 2 * c->sh.rows + 2 * (c->NQ + c->sh.rows - 1);
+  return 2 * c->G + c->sh.rows;
 }
 
 int launch_check(const char* what) {
@@ -1186,6 +1636,17 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     const int64_t G = P * s->rows;
     if (G > (int64_t)1 << 30) return fail(DSA_ERR_UNSUPPORTED, "too many rows");
     c->G = (int32_t)G;
+    // Balanced split of long rows when one workgroup can scan every row's
+    // bounds (rows <= CUs).  A pass has at most NQ + rows - 1 non-empty pieces
+    // (one per worker plus one per row boundary inside a worker's range);
+    // with the rows' owners that is one resident round at two workgroups per
+    // CU when NQ = 2 * CUs - rows + 1, less a reserve of slots for the rows'
+    // final workgroups, which run while the pass-2 pieces still store -inf.
+    const int64_t reserve = std::min<int64_t>(s->rows, 64);
+    c->NQ = (int32_t)std::max<int64_t>(
+        1, std::min<int64_t>((int64_t)c->cus * 2 - s->rows + 1 - reserve, NT));
+    c->balanced = (s->rows >= 1 && s->rows <= c->cus && s->rows <= NT) ? 1 : 0;
+    c->cnt_stride = std::max(c->P, c->NQ);
     const int64_t F = (s->k_tokens + s->block_size - 1) / s->block_size;
     // Token domain of a row: at most nlow + Kp <= 2*K_blk + F blocks (also
     // with repeated ids given to the standalone token top-k).
@@ -1196,10 +1657,15 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     const int64_t R = s->rows;
     const int64_t n_key = long_rows ? R * nb : 0;
     const int64_t n_hist = long_rows ? R * HIST_WORDS : 0;
-    const int64_t n_cnt = long_rows ? R * P : 0;
+    const int64_t n_cnt = long_rows ? R * c->cnt_stride : 0;
+    // Token candidates are gathered in pass 2 when the kept blocks hold more
+    // columns than the token top-k keeps (otherwise the closed form applies).
+    c->pregather = ((int64_t)s->k_blocks * s->block_size > s->k_tokens &&
+                    (s->block_size == 4 || s->block_size == 8 || s->block_size == 16)) ? 1 : 0;
+    const int64_t n_cand = long_rows && c->pregather ? 2 * R * nb : 0;
     const int64_t words[] = {n_key, n_key, n_key, n_hist, n_cnt, R * ROW_STATE,
                              R * s->k_blocks, R * c->dblk_cap, R * c->tkey_cap,
-                             R * c->tkey_cap, 64};
+                             R * c->tkey_cap, n_key, n_cand, n_cand, n_cnt, 64};
     int64_t total = 0;
     for (int64_t w : words) total += (w + 63) / 64 * 64;
     c->ws_bytes = (size_t)total * 4;
@@ -1212,9 +1678,10 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     uint32_t* base = static_cast<uint32_t*>(c->ws);
     uint32_t** slots[] = {&c->ws_key, &c->ws_list, &c->ws_flat, &c->ws_hist, &c->ws_cnt,
                           &c->ws_row, &c->ws_sel, &c->ws_dblk, &c->ws_tkey, &c->ws_tcol,
-                          &c->status};
+                          &c->ws_lkey, &c->ws_ccol, &c->ws_ckey, &c->ws_ccnt, &c->status};
+    static_assert(sizeof(slots) / sizeof(slots[0]) == sizeof(words) / sizeof(words[0]), "slots");
     int64_t pos = 0;
-    for (int i = 0; i < 11; ++i) {
+    for (int i = 0; i < (int)(sizeof(slots) / sizeof(slots[0])); ++i) {
       *slots[i] = words[i] ? base + pos : nullptr;
       pos += (words[i] + 63) / 64 * 64;
     }
@@ -1247,9 +1714,10 @@ int dsa_select_query(const dsa_ctx* c, dsa_launch_info* info) {
   int rc = check_ctx(c);
   if (rc != DSA_OK) return rc;
   if (!info) return fail(DSA_ERR_INVALID_ARG, "info is null");
-  info->programs_per_row = c->P;
+  const bool split = may_split(c) && c->balanced;
+  info->programs_per_row = split ? 0 : c->P;
   info->threads_per_group = NT;
-  info->grid_groups = c->G;
+  info->grid_groups = fused_grid(c);
   info->small_row_blocks = c->small_blocks;
   info->workspace_bytes = (int64_t)c->ws_bytes;
   info->fused_launches = 1;
@@ -1345,16 +1813,23 @@ int dsa_select_fused(dsa_ctx* c, float* logits, const int32_t* starts, const int
     // for their row's first pass) or, on request, in a second launch.
     const bool long_rows = may_split(c);
     const bool two = long_rows && (flags & DSA_TWO_LAUNCHES);
-    const int grid = long_rows && !two ? 2 * c->G : c->G;
+    p.balanced = long_rows && c->balanced;
+    // First launch: short rows and pass 1; pass 2 in the same launch or a
+    // second one.
+    const int npc = c->NQ + c->sh.rows - 1;
+    const int first = p.balanced ? c->sh.rows + npc : c->G;
+    const int second = p.balanced ? npc + c->sh.rows : c->G + c->sh.rows;
+    const int grid = fused_grid(c);
     int r2 = DSA_OK;
     with_bs(p.B, [&](auto bs) {
       constexpr int BS = decltype(bs)::value;
+      auto kern = p.balanced ? k_fused_bal<BS> : k_fused<BS>;
       p.phase_base = 0;
-      hipLaunchKernelGGL((k_fused<BS>), dim3(grid), dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL(kern, dim3(two ? first : grid), dim3(NT), 0, stream, p);
       if ((r2 = launch_check("k_fused launch")) != DSA_OK) return;
       if (two) {
-        p.phase_base = c->G;
-        hipLaunchKernelGGL((k_fused<BS>), dim3(c->G), dim3(NT), 0, stream, p);
+        p.phase_base = first;
+        hipLaunchKernelGGL(kern, dim3(second), dim3(NT), 0, stream, p);
         r2 = launch_check("k_fused (second pass) launch");
       }
     });

@@ -97,6 +97,21 @@ def test_fused_long_rows(B, W, ends, kb, kt, two):
     _full_check(dc, bids, tids, scores)
 
 
+@pytest.mark.parametrize("value", [1.5, -2.0])
+def test_fused_long_rows_all_ties(value):
+    """Long rows whose live values are all equal: every block ties, so every
+    block is listed and every value is a token candidate (the per-piece
+    candidate space overflows); ties go to the lower index."""
+    ends = [40000, 20000, 16385]
+    case = wl.make_custom(len(ends), 40000, 8, 300, 1000, ends, seed=91)
+    for r, e in enumerate(ends):
+        case.logits[r, :e] = np.float32(value)
+    gh.log(f"long rows all ties value={value}")
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused()
+    _full_check(dc, bids, tids, scores)
+
+
 def test_fused_long_rows_with_start_and_stride():
     case = wl.make_custom(4, 50000, 8, 300, 2048, [50000, 49999, 30000, 45000],
                           starts=[0, 7, 1001, 44990], col_stride=2, seed=77, dup_frac=0.05)
