@@ -113,6 +113,8 @@ struct __align__(16) Smem {
   uint32_t wv[64];
   uint32_t misc[16];
   uint64_t pfx[514];            // long-row block prefix over rows, then the chunk
+  uint32_t row_s[256];          // balanced split: each row's start and live length
+  uint32_t row_L[256];
   DSA_DEV uint32_t* keys() { return kid; }
   DSA_DEV uint32_t* ids() { return kid + LIST_CAP; }
 };

@@ -43,13 +43,17 @@ namespace dsa {
 constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int UNROLL = 4;      // float4 loads in flight per lane in the score pass
 constexpr int ROW_STATE = 8;   // pass-1 ticket, pass-2 ticket, digit, ready flag, low flag,
-                               // keys above the digit
+                               // keys above the digit, lists-gathered flag
 constexpr int UNROLL_STRIDED = 8;   // scalar loads in flight per lane: 4 * this
 // One workgroup reads at most a few tens of GB/s, so a row longer than this is
 // split over its P workgroups even when its block keys would fit in LDS.
 constexpr int SMALL_COLS = 16384;
 constexpr uint32_t KEPT_FLAG = 0x80000000u;
 constexpr uint64_t WAIT_LIMIT_TICKS = 200000000ull;   // 2 s of the 100 MHz clock
+// A pass-2 piece holds its -inf stores until the row's final workgroup has
+// read the row's lists (loads issued under a store stream take ~15x longer);
+// this wait orders work only, so it is short and gives up silently.
+constexpr uint64_t HOLD_LIMIT_TICKS = 2000ull;         // 20 us
 
 struct Params {
   float* logits;
@@ -770,106 +774,11 @@ DSA_DEV void long_pass1(const Params& p, int r, int b0, int b1, int npieces, con
   if (threadIdx.x == 0) {
     st_shared(&st[2], d);
     st_shared(&st[5], above);
+    st_shared(&st[6], 0u);
     st_shared(&st[0], 0u);
     vm_drain();
     st_shared(&st[3], 1u);            // the row's digit is ready
   }
-}
-
-// ---------------------------------------------------------------------------
-// Last workgroup of pass 2: exact selection among the listed blocks, masks of
-// the rejected ones, outputs, token top-k.  General form: the list is
-// gathered from the per-piece lists and the token top-k reads the kept
-// blocks' values back from the logits.
-// ---------------------------------------------------------------------------
-template <int BS>
-DSA_DEV void final_row_general(const Params& p, int r, const Row& rb, Smem& sm) {
-  float* rowp = row_ptr(p, r, rb);
-  const int nlb = rb.nlb, B = p.B;
-  const int P = piece_count(p, sm, rb, r);   // <= NT
-  const int64_t cs = p.col_stride;
-  const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
-  const uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
-  // Exclusive prefix of the per-piece list lengths; piece j's list starts at
-  // its first block (sm.hist[2 * NT + j]).
-  const uint32_t c = (int)threadIdx.x < P ? ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + threadIdx.x]) : 0u;
-  uint32_t n_list;
-  const uint32_t off = wg_excl_scan<NT>(c, sm.wv, n_list);
-  if ((int)threadIdx.x < P) {
-    sm.hist[threadIdx.x] = off;
-    sm.hist[NT + threadIdx.x] = c;
-    sm.hist[2 * NT + threadIdx.x] = (uint32_t)piece_start(p, sm, rb, r, threadIdx.x);
-  }
-  __syncthreads();
-  const bool in_lds = n_list <= (uint32_t)LIST_CAP;
-  uint32_t* lid = in_lds ? sm.ids() : p.ws_flat + (int64_t)r * p.nblocks;
-  {
-    // Gather the per-chunk lists into one ascending list; entry i belongs to
-    // the last chunk whose offset is <= i (binary search over P offsets).
-    constexpr int U = 8;
-    for (int i0 = threadIdx.x; i0 < (int)n_list; i0 += NT * U) {
-      uint32_t v[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NT;
-        v[u] = 0;
-        if (i < (int)n_list) {
-          int lo = 0, hi = P - 1;
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (sm.hist[mid] <= (uint32_t)i) lo = mid;
-            else hi = mid - 1;
-          }
-          v[u] = ld_shared(&wl[sm.hist[2 * NT + lo] + (i - (int)sm.hist[lo])]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (i0 + u * NT < (int)n_list) lid[i0 + u * NT] = v[u];
-    }
-  }
-  __syncthreads();
-  if (in_lds) {
-    constexpr int U = 8;
-    for (int i0 = threadIdx.x; i0 < (int)n_list; i0 += NT * U) {
-      uint32_t k[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NT;
-        k[u] = i < (int)n_list ? ld_shared(&wk[lid[i]]) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (i0 + u * NT < (int)n_list) sm.keys()[i0 + u * NT] = k[u];
-    }
-    __syncthreads();
-  }
-  auto getk = [&](int i) { return in_lds ? sm.keys()[i] : ld_shared(&wk[lid[i]]); };
-  int Kp = min(p.k_blocks, nlb);
-  if ((int)n_list < Kp) {
-    // Only after a call was cut short (stale workspace): keep the list.
-    if (threadIdx.x == 0) atomicOr(p.status, 4u);
-    Kp = (int)n_list;
-  }
-  uint32_t T = 0, q = 0xFFFFFFFFu;
-  if ((int)n_list > Kp) wg_radix_select<NT>((int)n_list, (uint32_t)Kp, getk, sm, T, q);
-  int32_t* bout = p.block_ids + (int64_t)r * p.k_blocks;
-  uint32_t* sel = Kp <= SEL_CAP ? sm.sel : p.ws_sel + (int64_t)r * p.k_blocks;
-  const bool write_mask = (p.flags & DSA_WRITE_MASK) != 0;
-  wg_select_compact<NT>((int)n_list, T, q, getk,
-      [&](int i, uint32_t rank, bool kept, uint64_t, int) {
-        const uint32_t b = lid[i];
-        if (kept) {
-          bout[rank] = (int32_t)b;
-          sel[rank] = b;
-        } else if (write_mask) {
-          mask_one_block(rowp, cs, B, rb.L, b);
-        }
-      }, sm);
-  for (int i = Kp + threadIdx.x; i < p.k_blocks; i += NT) bout[i] = -1;
-  __syncthreads();
-  const bool no_low = ld_shared(&p.ws_row[(int64_t)r * ROW_STATE + 4]) == 0u;
-  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, true, no_low, sm);
 }
 
 // Largest j < P with offs[j] <= i (offs nondecreasing, offs[0] = 0).
@@ -882,6 +791,123 @@ DSA_DEV int piece_of(const uint32_t* offs, int P, uint32_t i) {
   }
   return lo;
 }
+
+// ---------------------------------------------------------------------------
+// Last workgroup of pass 2: exact selection among the listed blocks, masks of
+// the rejected ones, outputs, token top-k.  General form: the list is
+// gathered from the per-piece lists and the token top-k reads the kept
+// blocks' values back from the logits.
+// ---------------------------------------------------------------------------
+template <int BS>
+DSA_DEV void final_row_general(const Params& p, int r, const Row& rb, Smem& sm) {
+  float* rowp = row_ptr(p, r, rb);
+  const bool vec = vec_ok(p, rowp);
+  const int nlb = rb.nlb, B = p.B;
+  const int P = piece_count(p, sm, rb, r);   // <= NT
+  const int64_t cs = p.col_stride;
+  const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
+  const uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
+  const uint32_t* wlk = p.ws_lkey + (int64_t)r * p.nblocks;
+  const uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
+  const int t = (int)threadIdx.x;
+  const bool jt = t < P;
+  // One round trip: the row's digit, the keys above it, the piece counts.
+  const uint32_t digit = ld_shared(&st[2]), above = ld_shared(&st[5]);
+  const uint32_t c_raw = ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + (jt ? t : 0)]);
+  const uint32_t c = jt ? c_raw : 0u;
+  // Exclusive prefix of the per-piece list lengths; piece j's list starts at
+  // its first block (sm.hist[2 * NT + j]).
+  uint32_t n_list;
+  const uint32_t off = wg_excl_scan<NT>(c, sm.wv, n_list);
+  if (jt) {
+    sm.hist[t] = off;
+    sm.hist[2 * NT + t] = (uint32_t)piece_start(p, sm, rb, r, t);
+  }
+  __syncthreads();
+  int Kp = min(p.k_blocks, nlb);
+  if ((int)n_list < Kp) {
+    // Only after a call was cut short (stale workspace): keep the list.
+    if (t == 0) atomicOr(p.status, 4u);
+    Kp = (int)n_list;
+  }
+  int32_t* bout = p.block_ids + (int64_t)r * p.k_blocks;
+  uint32_t* sel = Kp <= SEL_CAP ? sm.sel : p.ws_sel + (int64_t)r * p.k_blocks;
+  const bool write_mask = (p.flags & DSA_WRITE_MASK) != 0;
+  uint32_t T = 0, q = 0xFFFFFFFFu;
+  constexpr int U = 8;
+  if (n_list <= (uint32_t)LIST_CAP) {
+    // The list and its keys in LDS: loads issued unconditionally (clamped
+    // index), stores guarded.
+    uint32_t* lids = sm.ids();
+    uint32_t* lkeys = sm.keys();
+    for (int i0 = t; i0 < (int)n_list; i0 += NT * U) {
+      uint32_t a[U], b[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = (uint32_t)min(i0 + u * NT, (int)n_list - 1);
+        const int j = piece_of(sm.hist, P, i);
+        const uint32_t src = sm.hist[2 * NT + j] + (i - sm.hist[j]);
+        a[u] = ld_shared(&wl[src]);
+        b[u] = ld_shared(&wlk[src]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = i0 + u * NT;
+        if (i < (int)n_list) {
+          lids[i] = a[u];
+          lkeys[i] = b[u];
+        }
+      }
+    }
+    __syncthreads();
+    if (t == 0) st_shared(const_cast<uint32_t*>(&st[6]), 1u);   // lists read: -inf may go
+    auto getk = [&](int i) { return lkeys[i]; };
+    if ((int)n_list > Kp) wg_radix_select_low<NT>((int)n_list, digit, (uint32_t)Kp - above, getk, sm, T, q);
+    wg_rule_emit<NT>((int)n_list, T, q, getk, [&](int i, uint32_t rank, bool kept) {
+      const uint32_t b = lids[i];
+      if (kept) {
+        bout[rank] = (int32_t)b;
+        sel[rank] = b;
+      } else if (write_mask) {
+        mask_block_lane<BS>(rowp, cs, B, rb.L, vec, b);
+      }
+    }, sm);
+  } else {
+    // Longer lists: gathered into the workspace, keys read through it.
+    uint32_t* lid = p.ws_flat + (int64_t)r * p.nblocks;
+    for (int i0 = t; i0 < (int)n_list; i0 += NT * U) {
+      uint32_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = (uint32_t)min(i0 + u * NT, (int)n_list - 1);
+        const int j = piece_of(sm.hist, P, i);
+        v[u] = ld_shared(&wl[sm.hist[2 * NT + j] + (i - sm.hist[j])]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + u * NT < (int)n_list) st_shared(&lid[i0 + u * NT], v[u]);
+    }
+    vm_drain();
+    __syncthreads();
+    auto getk = [&](int i) { return ld_shared(&wk[ld_shared(&lid[i])]); };
+    if ((int)n_list > Kp) wg_radix_select<NT>((int)n_list, (uint32_t)Kp, getk, sm, T, q);
+    wg_select_compact<NT>((int)n_list, T, q, getk,
+        [&](int i, uint32_t rank, bool kept, uint64_t, int) {
+          const uint32_t b = ld_shared(&lid[i]);
+          if (kept) {
+            bout[rank] = (int32_t)b;
+            sel[rank] = b;
+          } else if (write_mask) {
+            mask_one_block(rowp, cs, B, rb.L, b);
+          }
+        }, sm);
+  }
+  for (int i = Kp + t; i < p.k_blocks; i += NT) bout[i] = -1;
+  __syncthreads();
+  const bool no_low = ld_shared(&st[4]) == 0u;
+  token_stage<BS>(p, r, rb, rowp, sel, Kp, T, true, no_low, sm);
+}
+
 
 // Last workgroup of pass 2, with the token candidates gathered by pass 2.
 // The listed blocks (every block whose key's top digit reaches the digit d of
@@ -901,12 +927,15 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
     const int nlb = rb.nlb, P = piece_count(p, sm, rb, r);
     const int Kp = min(p.k_blocks, nlb), Kt = min(p.k_tokens, rb.L);
     uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
-    const uint32_t digit = ld_shared(&st[2]), above = ld_shared(&st[5]);
-    const uint32_t beta = digit << 20;
     const int t = (int)threadIdx.x;
     const bool jt = t < P;
-    const uint32_t c = jt ? ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + t]) : 0u;
-    const uint32_t cc = jt ? ld_shared(&p.ws_ccnt[(int64_t)r * p.cnt_stride + t]) : 0u;
+    // One round trip: the row's digit, the keys above it, the piece counts.
+    const int tc0 = jt ? t : 0;
+    const uint32_t digit = ld_shared(&st[2]), above = ld_shared(&st[5]);
+    const uint32_t c_raw = ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + tc0]);
+    const uint32_t cc_raw = ld_shared(&p.ws_ccnt[(int64_t)r * p.cnt_stride + tc0]);
+    const uint32_t c = jt ? c_raw : 0u, cc = jt ? cc_raw : 0u;
+    const uint32_t beta = digit << 20;
     const bool ovf = __syncthreads_or(cc == 0xFFFFFFFFu) != 0;
     uint32_t n_list, n_cand;
     const uint32_t off = wg_excl_scan<NT>(c, sm.wv, n_list);
@@ -936,19 +965,18 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
     const uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
     const uint32_t* wlk = p.ws_lkey + (int64_t)r * p.nblocks;
     const int64_t creg = (int64_t)r * 2 * p.nblocks;
+    // Loads are issued unconditionally (clamped index) so that a batch is in
+    // flight together; only the stores are guarded.
     constexpr int U = 8;
     for (int i0 = t; i0 < (int)n_list; i0 += NT * U) {
       uint32_t a[U], b[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NT;
-        a[u] = b[u] = 0;
-        if (i < (int)n_list) {
-          const int j = piece_of(loffs, P, (uint32_t)i);
-          const uint32_t src = pstart[j] + ((uint32_t)i - loffs[j]);
-          a[u] = ld_shared(&wl[src]);
-          b[u] = ld_shared(&wlk[src]);
-        }
+        const uint32_t i = (uint32_t)min(i0 + u * NT, (int)n_list - 1);
+        const int j = piece_of(loffs, P, i);
+        const uint32_t src = pstart[j] + (i - loffs[j]);
+        a[u] = ld_shared(&wl[src]);
+        b[u] = ld_shared(&wlk[src]);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -959,22 +987,25 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
         }
       }
     }
-    for (int i0 = t; i0 < (int)n_cand; i0 += NT * U) {
+    // Candidate keys to LDS; their columns stay in registers until the list
+    // space is free again (n_cand <= TK_CAP = U * NT: one batch).
+    uint32_t ccol[U];
+    {
       uint32_t a[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NT;
-        a[u] = 0;
-        if (i < (int)n_cand) {
-          const int j = piece_of(coffs, P, (uint32_t)i);
-          a[u] = ld_shared(&p.ws_ckey[creg + 2 * (int64_t)pstart[j] + ((uint32_t)i - coffs[j])]);
-        }
+        const uint32_t i = (uint32_t)min(t + u * NT, max((int)n_cand - 1, 0));
+        const int j = piece_of(coffs, P, i);
+        const int64_t src = creg + 2 * (int64_t)pstart[j] + (i - coffs[j]);
+        a[u] = n_cand ? ld_shared(&p.ws_ckey[src]) : 0u;
+        ccol[u] = n_cand ? ld_shared(&p.ws_ccol[src]) : 0u;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (i0 + u * NT < (int)n_cand) tk[i0 + u * NT] = a[u];
+        if (t + u * NT < (int)n_cand) tk[t + u * NT] = a[u];
     }
     __syncthreads();
+    if (t == 0) st_shared(&st[6], 1u);   // the row's lists are read: -inf may go
 
     // Block top-k: the keys above d's bin are kept; the ties inside it are
     // resolved on the lower 20 bits.  Leaves sm.hist zero.
@@ -1003,26 +1034,14 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
     // Candidate columns; a candidate outside the kept blocks ranks nowhere.
     uint32_t* tc = sm.keys();
     uint32_t nk = 0;
-    for (int i0 = t; i0 < (int)n_cand; i0 += NT * U) {
-      uint32_t a[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NT;
-        a[u] = 0;
-        if (i < (int)n_cand) {
-          const int j = piece_of(coffs, P, (uint32_t)i);
-          a[u] = ld_shared(&p.ws_ccol[creg + 2 * (int64_t)pstart[j] + ((uint32_t)i - coffs[j])]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NT;
-        if (i < (int)n_cand) {
-          const uint32_t b = a[u] / BS;
-          tc[i] = a[u];
-          if ((sm.hist[b >> 5] >> (b & 31)) & 1u) ++nk;
-          else tk[i] = 0u;
-        }
+    for (int u = 0; u < U; ++u) {
+      const int i = t + u * NT;
+      if (i < (int)n_cand) {
+        const uint32_t b = ccol[u] / BS;
+        tc[i] = ccol[u];
+        if ((sm.hist[b >> 5] >> (b & 31)) & 1u) ++nk;
+        else tk[i] = 0u;
       }
     }
     uint32_t n_keep;
@@ -1069,6 +1088,16 @@ DSA_DEV bool wait_at_least(const Params& p, const uint32_t* word, uint32_t targe
   return sm.misc[3] != 0u;
 }
 
+// Thread 0 waits at most HOLD_LIMIT_TICKS for a flag; no error if it does not
+// come.
+DSA_DEV void hold_for(const uint32_t* flag) {
+  if (threadIdx.x == 0 && ld_shared(flag) == 0u) {
+    const uint64_t t0 = wall_clock64();
+    while (ld_shared(flag) == 0u && wall_clock64() - t0 < HOLD_LIMIT_TICKS) __builtin_amdgcn_s_sleep(1);
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Pass 2 of a long row, one piece: first the list of the piece's blocks whose
 // top digit reaches the row's digit (and their token candidates), published
@@ -1103,33 +1132,45 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
   bool cover = false;
   for (int s0 = b0; s0 < b1; s0 += CHUNK_CAP) {
     const int n = min(b1 - s0, CHUNK_CAP);
+    // Keys in registers (block s0 + threadIdx.x + u * NT), listed flags by
+    // ballot, ordered compaction from per-(batch, wave) counts.
     constexpr int U = CHUNK_CAP / NT;
+    constexpr int NW = NT / 64;
+    const int w = wave(), l = lane();
     uint32_t k[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = (int)threadIdx.x + u * NT;
-      k[u] = i < n ? ld_shared(&wk[s0 + i]) : 0u;
-    }
+    for (int u = 0; u < U; ++u) k[u] = ld_shared(&wk[s0 + min((int)threadIdx.x + u * NT, n - 1)]);
+    uint64_t m[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) keys[threadIdx.x + u * NT] = k[u];
-    __syncthreads();
-    for (int w = threadIdx.x; w < (n + 31) / 32; w += NT) {
-      uint32_t word = 0;
-      for (int j = 0; j < 32; ++j) {
-        const int i = w * 32 + j;
-        if (i < n && (keys[i] >> 20) >= digit) word |= 1u << j;
+    for (int u = 0; u < U; ++u) m[u] = ballot((int)threadIdx.x + u * NT < n && (k[u] >> 20) >= digit);
+    if (l == 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        sm.wv[u * NW + w] = popc(m[u]);
+        if (keep_bits) {
+          const int wi = ((s0 - b0) >> 5) + ((u * NT + w * 64) >> 5);
+          lbits[wi] = (uint32_t)m[u];
+          lbits[wi + 1] = (uint32_t)(m[u] >> 32);
+        }
       }
-      sm.bits[w] = word;
-      if (keep_bits) lbits[((s0 - b0) >> 5) + w] = word;
     }
+    __syncthreads();
+    const uint32_t cj = l < U * NW ? sm.wv[l] : 0u;
+    const uint32_t cinc = wave_incl_scan(cj);
+    const uint32_t nl = (uint32_t)__builtin_amdgcn_readlane((int)cinc, 63);
+    const uint32_t cx = cinc - cj;
     const uint32_t base = cnt;
-    const uint32_t nl = wg_compact<NT>(n, [&](int i) { return (keys[i] >> 20) >= digit; },
-        [&](int i, uint32_t rank) {
-          const uint32_t b = (uint32_t)(s0 + i);
-          st_shared(&wl[b0 + base + rank], b);
-          st_shared(&wlk[b0 + base + rank], keys[i]);
-          lids[rank] = b;
-        }, sm);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t pb = (uint32_t)__builtin_amdgcn_ds_bpermute((u * NW + w) << 2, (int)cx);
+      if ((m[u] >> l) & 1u) {
+        const uint32_t rank = pb + mbcnt(m[u]);
+        const uint32_t b = (uint32_t)(s0 + (int)threadIdx.x + u * NT);
+        st_shared(&wl[b0 + base + rank], b);
+        st_shared(&wlk[b0 + base + rank], k[u]);
+        lids[rank] = b;
+      }
+    }
     cnt += nl;
     __syncthreads();
     if constexpr (PG_OK) {
@@ -1189,6 +1230,9 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
   }
   (void)arrive_last(&st[1], 0u, sm);
   if (!(p.flags & DSA_WRITE_MASK)) return;
+  // (The balanced split keeps slots free for the final workgroups, which
+  // are therefore resident; in the per-row split they may not be.)
+  if (p.balanced) hold_for(&st[6]);
   if (keep_bits) {
     mask_blocks<BS>(rowp, p.col_stride, p.B, rb.L, b0, b1, vec, [&](int b) {
       const int i = b - b0;
@@ -1214,6 +1258,7 @@ DSA_DEV void final_wg(const Params& p, int r, const Row& rb, int npieces, Smem& 
   if (!wait_at_least(p, &st[1], (uint32_t)npieces, sm)) return;
   final_row<BS>(p, r, rb, sm);
   if (threadIdx.x == 0) {
+    st_shared(&st[6], 1u);
     st_shared(&st[1], 0u);
     st_shared(&st[3], 0u);
     st_shared(&st[4], 0u);
@@ -1234,13 +1279,16 @@ DSA_DEV void own_short_row(const Params& p, int r, const Row& rb, Smem& sm) {
   small_row<BS>(p, r, rb, sm);
 }
 
-// sm.pfx[0..rows]: blocks of long rows before each row (rows <= NT).
+// sm.pfx[0..rows]: blocks of long rows before each row; sm.row_s / row_L:
+// each row's start and live length (rows <= 256).
 DSA_DEV void build_plan(const Params& p, Smem& sm) {
   const int t = (int)threadIdx.x;
   uint32_t v = 0;
   if (t < p.rows) {
     const Row rb = row_bounds(p, t);
     if (rb.L > 0 && !p.one_group(rb.nlb, rb.L)) v = (uint32_t)rb.nlb;
+    sm.row_s[t] = (uint32_t)rb.s;
+    sm.row_L[t] = (uint32_t)rb.L;
   }
   uint32_t total;
   const uint32_t x = wg_excl_scan<NT>(v, sm.wv, total);
@@ -1250,6 +1298,16 @@ DSA_DEV void build_plan(const Params& p, Smem& sm) {
     sm.pfx[p.rows + 1] = ((uint64_t)total + (uint64_t)p.NQ - 1) / (uint64_t)p.NQ;
   }
   __syncthreads();
+}
+
+// Bounds of a long row from the plan (no second load of starts and ends).
+DSA_DEV Row plan_row(const Params& p, const Smem& sm, int r) {
+  Row rb;
+  rb.s = sm.row_s[r];
+  rb.L = (int32_t)sm.row_L[r];
+  rb.nlb = (int32_t)(((int64_t)rb.L + p.B - 1) / p.B);
+  rb.bad = false;
+  return rb;
 }
 
 // Start of piece k of the balanced split, k in [0, NQ + rows - 1]: the pieces
@@ -1295,7 +1353,7 @@ DSA_DEV void balanced_piece(const Params& p, int k, bool pass2, Smem& sm) {
     }
     r = a;
   }
-  const Row rb = row_bounds(p, r);
+  const Row rb = plan_row(p, sm, r);
   const uint64_t rs = sm.pfx[r], re = sm.pfx[r + 1];
   const int w0 = worker_of(sm, p.rows, rs);
   const int np = worker_of(sm, p.rows, re - 1) - w0 + 1;
@@ -1356,7 +1414,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
     const int r = g - 2 * npc;
     build_plan(p, sm);
     if (sm.pfx[r + 1] == sm.pfx[r]) return;   // not a long row
-    const Row rb = row_bounds(p, r);
+    const Row rb = plan_row(p, sm, r);
     final_wg<BS>(p, r, rb, piece_count(p, sm, rb, r), sm);
     return;
   }
@@ -1637,7 +1695,7 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     if (G > (int64_t)1 << 30) return fail(DSA_ERR_UNSUPPORTED, "too many rows");
     c->G = (int32_t)G;
     // Balanced split of long rows when one workgroup can scan every row's
-    // bounds (rows <= CUs).  A pass has at most NQ + rows - 1 non-empty pieces
+    // bounds (rows <= CUs and <= 256).  A pass has at most NQ + rows - 1 non-empty pieces
     // (one per worker plus one per row boundary inside a worker's range);
     // with the rows' owners that is one resident round at two workgroups per
     // CU when NQ = 2 * CUs - rows + 1, less a reserve of slots for the rows'
@@ -1645,7 +1703,7 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     const int64_t reserve = std::min<int64_t>(s->rows, 64);
     c->NQ = (int32_t)std::max<int64_t>(
         1, std::min<int64_t>((int64_t)c->cus * 2 - s->rows + 1 - reserve, NT));
-    c->balanced = (s->rows >= 1 && s->rows <= c->cus && s->rows <= NT) ? 1 : 0;
+    c->balanced = (s->rows >= 1 && s->rows <= c->cus && s->rows <= 256) ? 1 : 0;
     c->cnt_stride = std::max(c->P, c->NQ);
     const int64_t F = (s->k_tokens + s->block_size - 1) / s->block_size;
     // Token domain of a row: at most nlow + Kp <= 2*K_blk + F blocks (also
