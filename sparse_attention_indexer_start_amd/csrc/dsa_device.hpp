@@ -42,6 +42,13 @@ DSA_DEV uint32_t ld_shared(const uint32_t* p) {
 DSA_DEV void st_shared(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+DSA_DEV uint64_t ld_shared64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DSA_DEV void st_shared64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+DSA_DEV uint64_t pair(uint32_t lo, uint32_t hi) { return (uint64_t)lo | ((uint64_t)hi << 32); }
 DSA_DEV void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 typedef float f4v __attribute__((ext_vector_type(4)));
@@ -90,6 +97,17 @@ DSA_DEV uint32_t wave_incl_scan(uint32_t x) {
   x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true);
   x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);
   x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+
+// Inclusive running maximum over the 64 lanes (same DPP pattern as the sum).
+DSA_DEV uint32_t wave_incl_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, true));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false));
   return x;
 }
 

@@ -42,8 +42,10 @@ namespace dsa {
 
 constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int UNROLL = 4;      // float4 loads in flight per lane in the score pass
-constexpr int ROW_STATE = 8;   // pass-1 ticket, pass-2 ticket, digit, ready flag, low flag,
-                               // keys above the digit, lists-gathered flag
+// Row state words: pass-1 ticket, pass-2 ticket, digit, ready flag, low flag,
+// keys above the digit, lists-gathered flag.  Each row's state has a 128-byte
+// line of its own: workgroups poll these words.
+constexpr int ROW_STATE = 32;
 constexpr int UNROLL_STRIDED = 8;   // scalar loads in flight per lane: 4 * this
 // One workgroup reads at most a few tens of GB/s, so a row longer than this is
 // split over its P workgroups even when its block keys would fit in LDS.
@@ -78,7 +80,7 @@ struct Params {
   }
   uint32_t flags;
   uint32_t* ws_key;    // [rows][nblocks]  block keys of long rows
-  uint32_t* ws_list;   // [rows][nblocks]  listed blocks, per chunk
+  uint64_t* ws_list;   // [rows][nblocks]  listed blocks per piece: (id, key) pairs
   uint32_t* ws_flat;   // [rows][nblocks]  listed blocks, gathered (overflow)
   uint32_t* ws_hist;   // [rows][HIST_WORDS]
   uint32_t* ws_cnt;    // [rows][max(P, NQ)]  list length per piece
@@ -87,9 +89,7 @@ struct Params {
   uint32_t* ws_dblk;   // [rows][dblk_cap]   (overflow)
   uint32_t* ws_tkey;   // [rows][tkey_cap]   (overflow)
   uint32_t* ws_tcol;   // [rows][tkey_cap]   (overflow)
-  uint32_t* ws_lkey;   // [rows][nblocks]  keys of the listed blocks (beside ws_list)
-  uint32_t* ws_ccol;   // [rows][2 * nblocks]  token candidates: column (row-relative)
-  uint32_t* ws_ckey;   // [rows][2 * nblocks]  token candidates: key
+  uint64_t* ws_cand;   // [rows][2 * nblocks]  token candidates: (column, key) pairs
   uint32_t* ws_ccnt;   // [rows][max(P, NQ)]  candidates per piece (~0u: overflow)
   int64_t dblk_cap, tkey_cap;
   int32_t pregather;   // K_blk * B > K_tok and B in {4, 8, 16}
@@ -781,6 +781,56 @@ DSA_DEV void long_pass1(const Params& p, int r, int b0, int b1, int npieces, con
   }
 }
 
+// map[i] = the piece holding entry i of the pieces' concatenated lists, for
+// i < n <= 8 * NT (offs: exclusive offsets of the P <= NT pieces): each
+// non-empty piece marks its first entry, then a running maximum carries the
+// marks forward.  Three barriers.
+DSA_DEV void build_piece_map(uint32_t* map, const uint32_t* offs, int P, uint32_t n, Smem& sm) {
+  const int t = (int)threadIdx.x;
+  uint32_t* mp = map + 8 * t;
+  const bool mine = 8u * (uint32_t)t < n;
+  if (mine) {
+    *reinterpret_cast<uint4*>(mp) = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(mp + 4) = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  if (t < P) {
+    const uint32_t o = offs[t], next = t + 1 < P ? offs[t + 1] : n;
+    if (next > o) map[o] = (uint32_t)t;
+  }
+  __syncthreads();
+  uint32_t v[8];
+  uint32_t run = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = 0;
+  if (mine) {
+    const uint4 a = *reinterpret_cast<const uint4*>(mp);
+    const uint4 b = *reinterpret_cast<const uint4*>(mp + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      run = max(run, v[e]);
+      v[e] = run;
+    }
+  }
+  // The carry from earlier threads: running maximum of the thread maxima.
+  const uint32_t inc = wave_incl_max(run);
+  if (lane() == 63) sm.wv[wave()] = inc;
+  __syncthreads();
+  uint32_t carry = 0;
+  for (int x = 0; x < wave(); ++x) carry = max(carry, sm.wv[x]);
+  const uint32_t prev = (uint32_t)__shfl_up((int)inc, 1, 64);
+  if (lane() != 0) carry = max(carry, prev);
+  if (mine) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = max(v[e], carry);
+    *reinterpret_cast<uint4*>(mp) = make_uint4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<uint4*>(mp + 4) = make_uint4(v[4], v[5], v[6], v[7]);
+  }
+  __syncthreads();
+}
+
 // Largest j < P with offs[j] <= i (offs nondecreasing, offs[0] = 0).
 DSA_DEV int piece_of(const uint32_t* offs, int P, uint32_t i) {
   int lo = 0, hi = P - 1;
@@ -806,8 +856,7 @@ DSA_DEV void final_row_general(const Params& p, int r, const Row& rb, Smem& sm) 
   const int P = piece_count(p, sm, rb, r);   // <= NT
   const int64_t cs = p.col_stride;
   const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
-  const uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
-  const uint32_t* wlk = p.ws_lkey + (int64_t)r * p.nblocks;
+  const uint64_t* wl = p.ws_list + (int64_t)r * p.nblocks;
   const uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
   const int t = (int)threadIdx.x;
   const bool jt = t < P;
@@ -840,22 +889,25 @@ DSA_DEV void final_row_general(const Params& p, int r, const Row& rb, Smem& sm) 
     // index), stores guarded.
     uint32_t* lids = sm.ids();
     uint32_t* lkeys = sm.keys();
+    uint32_t* pmap = sm.tkey;
+    build_piece_map(pmap, sm.hist, P, n_list, sm);
     for (int i0 = t; i0 < (int)n_list; i0 += NT * U) {
-      uint32_t a[U], b[U];
+      uint32_t src[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = (uint32_t)min(i0 + u * NT, (int)n_list - 1);
-        const int j = piece_of(sm.hist, P, i);
-        const uint32_t src = sm.hist[2 * NT + j] + (i - sm.hist[j]);
-        a[u] = ld_shared(&wl[src]);
-        b[u] = ld_shared(&wlk[src]);
+        const uint32_t j = pmap[i];
+        src[u] = sm.hist[2 * NT + j] + (i - sm.hist[j]);
       }
+      uint64_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld_shared64(&wl[src[u]]);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u * NT;
         if (i < (int)n_list) {
-          lids[i] = a[u];
-          lkeys[i] = b[u];
+          lids[i] = (uint32_t)v[u];
+          lkeys[i] = (uint32_t)(v[u] >> 32);
         }
       }
     }
@@ -876,13 +928,15 @@ DSA_DEV void final_row_general(const Params& p, int r, const Row& rb, Smem& sm) 
     // Longer lists: gathered into the workspace, keys read through it.
     uint32_t* lid = p.ws_flat + (int64_t)r * p.nblocks;
     for (int i0 = t; i0 < (int)n_list; i0 += NT * U) {
-      uint32_t v[U];
+      uint32_t v[U], src[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = (uint32_t)min(i0 + u * NT, (int)n_list - 1);
         const int j = piece_of(sm.hist, P, i);
-        v[u] = ld_shared(&wl[sm.hist[2 * NT + j] + (i - sm.hist[j])]);
+        src[u] = sm.hist[2 * NT + j] + (i - sm.hist[j]);
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = (uint32_t)ld_shared64(&wl[src[u]]);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (i0 + u * NT < (int)n_list) st_shared(&lid[i0 + u * NT], v[u]);
@@ -962,43 +1016,56 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
     }
     __syncthreads();
     // Gather the list (ids and keys) and the candidate keys in piece order.
-    const uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
-    const uint32_t* wlk = p.ws_lkey + (int64_t)r * p.nblocks;
+    const uint64_t* wl = p.ws_list + (int64_t)r * p.nblocks;
     const int64_t creg = (int64_t)r * 2 * p.nblocks;
     // Loads are issued unconditionally (clamped index) so that a batch is in
     // flight together; only the stores are guarded.
+    // Entry -> piece maps (in sm.hist, free until the block select) instead
+    // of a search per entry: a search loop between loads would also make the
+    // compiler wait for every load issued before it.
     constexpr int U = 8;
+    uint32_t* pmap = sm.hist;
+    build_piece_map(pmap, loffs, P, n_list, sm);
     for (int i0 = t; i0 < (int)n_list; i0 += NT * U) {
-      uint32_t a[U], b[U];
+      uint32_t src[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = (uint32_t)min(i0 + u * NT, (int)n_list - 1);
-        const int j = piece_of(loffs, P, i);
-        const uint32_t src = pstart[j] + (i - loffs[j]);
-        a[u] = ld_shared(&wl[src]);
-        b[u] = ld_shared(&wlk[src]);
+        const uint32_t j = pmap[i];
+        src[u] = pstart[j] + (i - loffs[j]);
       }
+      uint64_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld_shared64(&wl[src[u]]);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = i0 + u * NT;
         if (i < (int)n_list) {
-          lids[i] = a[u];
-          lkeys[i] = b[u];
+          lids[i] = (uint32_t)v[u];
+          lkeys[i] = (uint32_t)(v[u] >> 32);
         }
       }
     }
     // Candidate keys to LDS; their columns stay in registers until the list
     // space is free again (n_cand <= TK_CAP = U * NT: one batch).
+    __syncthreads();
+    build_piece_map(pmap, coffs, P, n_cand, sm);
     uint32_t ccol[U];
     {
       uint32_t a[U];
+      int64_t src[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = (uint32_t)min(t + u * NT, max((int)n_cand - 1, 0));
-        const int j = piece_of(coffs, P, i);
-        const int64_t src = creg + 2 * (int64_t)pstart[j] + (i - coffs[j]);
-        a[u] = n_cand ? ld_shared(&p.ws_ckey[src]) : 0u;
-        ccol[u] = n_cand ? ld_shared(&p.ws_ccol[src]) : 0u;
+        const uint32_t j = n_cand ? pmap[i] : 0u;
+        src[u] = creg + 2 * (int64_t)pstart[j] + (i - coffs[j]);
+      }
+      const bool any = n_cand != 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint64_t v = any ? ld_shared64(&p.ws_cand[src[u]]) : 0u;
+        ccol[u] = (uint32_t)v;
+        a[u] = (uint32_t)(v >> 32);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -1074,7 +1141,7 @@ DSA_DEV bool wait_at_least(const Params& p, const uint32_t* word, uint32_t targe
     if (ld_shared(word) < target) {
       const uint64_t t0 = wall_clock64();
       while (ld_shared(word) < target) {
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(8);
         if (wall_clock64() - t0 > WAIT_LIMIT_TICKS) {
           atomicOr(p.status, 2u);
           ok = 0;
@@ -1093,7 +1160,7 @@ DSA_DEV bool wait_at_least(const Params& p, const uint32_t* word, uint32_t targe
 DSA_DEV void hold_for(const uint32_t* flag) {
   if (threadIdx.x == 0 && ld_shared(flag) == 0u) {
     const uint64_t t0 = wall_clock64();
-    while (ld_shared(flag) == 0u && wall_clock64() - t0 < HOLD_LIMIT_TICKS) __builtin_amdgcn_s_sleep(1);
+    while (ld_shared(flag) == 0u && wall_clock64() - t0 < HOLD_LIMIT_TICKS) __builtin_amdgcn_s_sleep(8);
   }
   __syncthreads();
 }
@@ -1113,8 +1180,7 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
   const bool vec = vec_ok(p, rowp);
   const uint32_t digit = ld_shared(&st[2]);
   const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
-  uint32_t* wl = p.ws_list + (int64_t)r * p.nblocks;
-  uint32_t* wlk = p.ws_lkey + (int64_t)r * p.nblocks;
+  uint64_t* wl = p.ws_list + (int64_t)r * p.nblocks;
   // Token candidates: every live value of a listed block whose key reaches
   // the lower edge beta of the digit's bin, in column order, into this
   // piece's region of 2 entries per block.
@@ -1166,8 +1232,7 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
       if ((m[u] >> l) & 1u) {
         const uint32_t rank = pb + mbcnt(m[u]);
         const uint32_t b = (uint32_t)(s0 + (int)threadIdx.x + u * NT);
-        st_shared(&wl[b0 + base + rank], b);
-        st_shared(&wlk[b0 + base + rank], k[u]);
+        st_shared64(&wl[b0 + base + rank], pair(b, k[u]));
         lids[rank] = b;
       }
     }
@@ -1212,8 +1277,7 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
 #pragma unroll
             for (int e = 0; e < BS; ++e) {
               if (e < nv && kk[e] >= beta) {
-                st_shared(&p.ws_ccol[creg + ccnt + o], (uint32_t)(c0 + e));
-                st_shared(&p.ws_ckey[creg + ccnt + o], kk[e]);
+                st_shared64(&p.ws_cand[creg + ccnt + o], pair((uint32_t)(c0 + e), kk[e]));
                 ++o;
               }
             }
@@ -1527,7 +1591,7 @@ struct dsa_ctx {
   void* ws;
   size_t ws_bytes;
   uint32_t *ws_key, *ws_list, *ws_flat, *ws_hist, *ws_cnt, *ws_row, *ws_sel, *ws_dblk, *ws_tkey,
-      *ws_tcol, *ws_lkey, *ws_ccol, *ws_ckey, *ws_ccnt, *status;
+      *ws_tcol, *ws_cand, *ws_ccnt, *status;
   int32_t pregather;
   uint32_t magic;
 };
@@ -1597,7 +1661,7 @@ Params base_params(const dsa_ctx* c) {
   p.cnt_stride = c->cnt_stride;
   p.small_blocks = c->small_blocks;
   p.ws_key = c->ws_key;
-  p.ws_list = c->ws_list;
+  p.ws_list = reinterpret_cast<uint64_t*>(c->ws_list);
   p.ws_flat = c->ws_flat;
   p.ws_hist = c->ws_hist;
   p.ws_cnt = c->ws_cnt;
@@ -1606,9 +1670,7 @@ Params base_params(const dsa_ctx* c) {
   p.ws_dblk = c->ws_dblk;
   p.ws_tkey = c->ws_tkey;
   p.ws_tcol = c->ws_tcol;
-  p.ws_lkey = c->ws_lkey;
-  p.ws_ccol = c->ws_ccol;
-  p.ws_ckey = c->ws_ckey;
+  p.ws_cand = reinterpret_cast<uint64_t*>(c->ws_cand);
   p.ws_ccnt = c->ws_ccnt;
   p.pregather = c->pregather;
   p.dblk_cap = c->dblk_cap;
@@ -1721,9 +1783,9 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     c->pregather = ((int64_t)s->k_blocks * s->block_size > s->k_tokens &&
                     (s->block_size == 4 || s->block_size == 8 || s->block_size == 16)) ? 1 : 0;
     const int64_t n_cand = long_rows && c->pregather ? 2 * R * nb : 0;
-    const int64_t words[] = {n_key, n_key, n_key, n_hist, n_cnt, R * ROW_STATE,
+    const int64_t words[] = {n_key, 2 * n_key, n_key, n_hist, n_cnt, R * ROW_STATE,
                              R * s->k_blocks, R * c->dblk_cap, R * c->tkey_cap,
-                             R * c->tkey_cap, n_key, n_cand, n_cand, n_cnt, 64};
+                             R * c->tkey_cap, 2 * n_cand, n_cnt, 64};
     int64_t total = 0;
     for (int64_t w : words) total += (w + 63) / 64 * 64;
     c->ws_bytes = (size_t)total * 4;
@@ -1736,7 +1798,7 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     uint32_t* base = static_cast<uint32_t*>(c->ws);
     uint32_t** slots[] = {&c->ws_key, &c->ws_list, &c->ws_flat, &c->ws_hist, &c->ws_cnt,
                           &c->ws_row, &c->ws_sel, &c->ws_dblk, &c->ws_tkey, &c->ws_tcol,
-                          &c->ws_lkey, &c->ws_ccol, &c->ws_ckey, &c->ws_ccnt, &c->status};
+                          &c->ws_cand, &c->ws_ccnt, &c->status};
     static_assert(sizeof(slots) / sizeof(slots[0]) == sizeof(words) / sizeof(words[0]), "slots");
     int64_t pos = 0;
     for (int i = 0; i < (int)(sizeof(slots) / sizeof(slots[0])); ++i) {
