@@ -77,11 +77,17 @@ typedef struct dsa_shape {
 
 typedef struct dsa_ctx dsa_ctx;
 
-/* Launch geometry chosen at init (for benchmarks and tests). */
+/*
+ * Launch geometry chosen at init (for benchmarks and tests).  Rows longer
+ * than one workgroup's share are split either per row (P workgroups each) or,
+ * when rows <= min(CUs, 256), by a balanced split in which equal ranges of the
+ * concatenated long rows go to the workgroups of each pass (then
+ * programs_per_row is 0).
+ */
 typedef struct dsa_launch_info {
-  int32_t programs_per_row;   /* P: workgroups per row for streaming passes */
+  int32_t programs_per_row;   /* P of the per-row split; 0 for the balanced split */
   int32_t threads_per_group;
-  int32_t grid_groups;        /* workgroups of one streaming launch */
+  int32_t grid_groups;        /* workgroups of the fused launch (one-launch mode) */
   int32_t small_row_blocks;   /* rows with nlb <= this run in one workgroup */
   int64_t workspace_bytes;
   int32_t fused_launches;     /* kernel launches per dsa_select_fused call */
