@@ -42,9 +42,10 @@ namespace dsa {
 
 constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int UNROLL = 4;      // float4 loads in flight per lane in the score pass
-// Row state words: pass-1 ticket, pass-2 ticket, digit, ready flag, low flag,
-// keys above the digit, lists-gathered flag.  Each row's state has a 128-byte
-// line of its own: workgroups poll these words.
+// Row state words: pass-1 ticket, pass-2 ticket, digit, ready word (digit + 1;
+// 0 until the digit is known), low flag, keys above the digit, lists-gathered
+// flag.  Each row's state has a 128-byte line of its own: workgroups poll
+// these words.
 constexpr int ROW_STATE = 32;
 constexpr int UNROLL_STRIDED = 8;   // scalar loads in flight per lane: 4 * this
 // One workgroup reads at most a few tens of GB/s, so a row longer than this is
@@ -777,7 +778,7 @@ DSA_DEV void long_pass1(const Params& p, int r, int b0, int b1, int npieces, con
     st_shared(&st[6], 0u);
     st_shared(&st[0], 0u);
     vm_drain();
-    st_shared(&st[3], 1u);            // the row's digit is ready
+    st_shared(&st[3], d + 1u);        // the row's digit is ready (and is d)
   }
 }
 
@@ -982,94 +983,164 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
     const int Kp = min(p.k_blocks, nlb), Kt = min(p.k_tokens, rb.L);
     uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
     const int t = (int)threadIdx.x;
-    const bool jt = t < P;
-    // One round trip: the row's digit, the keys above it, the piece counts.
-    const int tc0 = jt ? t : 0;
+    // The row's digit and the keys above it, loaded with the piece counts.
     const uint32_t digit = ld_shared(&st[2]), above = ld_shared(&st[5]);
-    const uint32_t c_raw = ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + tc0]);
-    const uint32_t cc_raw = ld_shared(&p.ws_ccnt[(int64_t)r * p.cnt_stride + tc0]);
-    const uint32_t c = jt ? c_raw : 0u, cc = jt ? cc_raw : 0u;
     const uint32_t beta = digit << 20;
-    const bool ovf = __syncthreads_or(cc == 0xFFFFFFFFu) != 0;
-    uint32_t n_list, n_cand;
-    const uint32_t off = wg_excl_scan<NT>(c, sm.wv, n_list);
-    const uint32_t coff = wg_excl_scan<NT>(ovf ? 0u : cc, sm.wv, n_cand);
-    const bool fast = !ovf && beta > KEY_NEG_INF && rb.L > p.k_tokens &&
-                      n_list >= (uint32_t)Kp && n_list <= (uint32_t)LIST_CAP &&
-                      n_cand <= (uint32_t)TK_CAP && nlb <= BITMAP_BITS && Kp <= SEL_CAP;
-    if (!fast) return final_row_general<BS>(p, r, rb, sm);
-
     float* rowp = row_ptr(p, r, rb);
     const bool vec = vec_ok(p, rowp);
     uint32_t* lkeys = sm.keys();
     uint32_t* lids = sm.ids();
     uint32_t* tk = sm.tkey;
-    // Piece tables (kept until the candidates are gathered; the selects
-    // below clear sm.hist): candidate offsets, first blocks, list offsets.
-    uint32_t* coffs = sm.sel;
-    uint32_t* pstart = sm.sel + NT;
-    uint32_t* loffs = sm.sel + 2 * NT;
-    if (jt) {
-      coffs[t] = coff;
-      pstart[t] = (uint32_t)piece_start(p, sm, rb, r, t);
-      loffs[t] = off;
-    }
-    __syncthreads();
-    // Gather the list (ids and keys) and the candidate keys in piece order.
     const uint64_t* wl = p.ws_list + (int64_t)r * p.nblocks;
     const int64_t creg = (int64_t)r * 2 * p.nblocks;
-    // Loads are issued unconditionally (clamped index) so that a batch is in
-    // flight together; only the stores are guarded.
-    // Entry -> piece maps (in sm.hist, free until the block select) instead
-    // of a search per entry: a search loop between loads would also make the
-    // compiler wait for every load issued before it.
     constexpr int U = 8;
-    uint32_t* pmap = sm.hist;
-    build_piece_map(pmap, loffs, P, n_list, sm);
-    for (int i0 = t; i0 < (int)n_list; i0 += NT * U) {
-      uint32_t src[U];
+    uint32_t n_list, n_cand;
+    uint32_t ccol[U];   // candidate t + u * NT: its column (its key goes to tk)
+    auto is_fast = [&](bool ovf) {
+      return !ovf && beta > KEY_NEG_INF && rb.L > p.k_tokens && n_list >= (uint32_t)Kp &&
+             n_list <= (uint32_t)LIST_CAP && n_cand <= (uint32_t)TK_CAP && nlb <= BITMAP_BITS &&
+             Kp <= SEL_CAP;
+    };
+    // Candidate slot u of this thread is candidate cbase + u * cst when
+    // u * cst < crem.
+    uint32_t cbase = (uint32_t)t, cst = (uint32_t)NT, crem = 0u;
+    bool gathered = false;
+    if (P <= 64) {
+      // Every wave holds the piece table in its lanes (lane j: piece j) and
+      // scans it itself, without a barrier.  When every piece's list and
+      // candidates fit 8 entries per thread of an equal share of the
+      // workgroup (NT / P threads per piece), each thread copies
+      // entries of its own piece only, so no search maps entries to pieces,
+      // and the lists and candidates come in one round trip.
+      const int l = lane();
+      const int jl = l < P ? l : 0;
+      const uint32_t c_raw = ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + jl]);
+      const uint32_t cc_raw = ld_shared(&p.ws_ccnt[(int64_t)r * p.cnt_stride + jl]);
+      const uint32_t ps = (uint32_t)piece_start(p, sm, rb, r, jl);
+      const bool ovf = ballot(l < P && cc_raw == 0xFFFFFFFFu) != 0;
+      const uint32_t c = l < P ? c_raw : 0u;
+      const uint32_t cc = (l < P && !ovf) ? cc_raw : 0u;
+      const uint32_t cinc = wave_incl_scan(c), ccinc = wave_incl_scan(cc);
+      n_list = (uint32_t)__builtin_amdgcn_readlane((int)cinc, 63);
+      n_cand = (uint32_t)__builtin_amdgcn_readlane((int)ccinc, 63);
+      if (!is_fast(ovf)) return final_row_general<BS>(p, r, rb, sm);
+      const uint32_t tpp = (uint32_t)(NT / P);   // threads per piece
+      const uint32_t cmax = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_max(max(c, cc)), 63);
+      if (cmax <= (uint32_t)U * tpp) {
+        const uint32_t off = cinc - c, coff = ccinc - cc;
+        const int j = (int)((uint32_t)t / tpp);
+        const uint32_t ti = (uint32_t)t - (uint32_t)j * tpp;
+        const bool live = j < P;
+        const int js = live ? j : 0;
+        const uint32_t cj = (uint32_t)__shfl((int)c, js, 64);
+        const uint32_t ccj = (uint32_t)__shfl((int)cc, js, 64);
+        const uint32_t oj = (uint32_t)__shfl((int)off, js, 64);
+        const uint32_t coj = (uint32_t)__shfl((int)coff, js, 64);
+        const uint32_t pj = (uint32_t)__shfl((int)ps, js, 64);
+        // Clamped indices: every load is issued, only the stores are guarded.
+        const uint32_t cl = cj ? cj - 1u : 0u, ccl = ccj ? ccj - 1u : 0u;
+        uint64_t vl[U], vc[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = (uint32_t)min(i0 + u * NT, (int)n_list - 1);
-        const uint32_t j = pmap[i];
-        src[u] = pstart[j] + (i - loffs[j]);
-      }
-      uint64_t v[U];
+        for (int u = 0; u < U; ++u) vl[u] = ld_shared64(&wl[pj + min(ti + u * tpp, cl)]);
+        if (n_cand != 0u) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = ld_shared64(&wl[src[u]]);
+          for (int u = 0; u < U; ++u)
+            vc[u] = ld_shared64(&p.ws_cand[creg + 2 * (int64_t)pj + min(ti + u * tpp, ccl)]);
+        } else {
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = i0 + u * NT;
-        if (i < (int)n_list) {
-          lids[i] = (uint32_t)v[u];
-          lkeys[i] = (uint32_t)(v[u] >> 32);
+          for (int u = 0; u < U; ++u) vc[u] = 0u;
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t i = ti + u * tpp;
+          if (live && i < cj) {
+            lids[oj + i] = (uint32_t)vl[u];
+            lkeys[oj + i] = (uint32_t)(vl[u] >> 32);
+          }
+          ccol[u] = (uint32_t)vc[u];
+          if (live && i < ccj) tk[coj + i] = (uint32_t)(vc[u] >> 32);
+        }
+        cbase = coj + ti;
+        cst = tpp;
+        crem = (live && ccj > ti) ? ccj - ti : 0u;
+        gathered = true;
       }
     }
-    // Candidate keys to LDS; their columns stay in registers until the list
-    // space is free again (n_cand <= TK_CAP = U * NT: one batch).
-    __syncthreads();
-    build_piece_map(pmap, coffs, P, n_cand, sm);
-    uint32_t ccol[U];
-    {
-      uint32_t a[U];
-      int64_t src[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t i = (uint32_t)min(t + u * NT, max((int)n_cand - 1, 0));
-        const uint32_t j = n_cand ? pmap[i] : 0u;
-        src[u] = creg + 2 * (int64_t)pstart[j] + (i - coffs[j]);
+    if (!gathered) {
+      const bool jt = t < P;
+      const int tc0 = jt ? t : 0;
+      const uint32_t c_raw = ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + tc0]);
+      const uint32_t cc_raw = ld_shared(&p.ws_ccnt[(int64_t)r * p.cnt_stride + tc0]);
+      const uint32_t c = jt ? c_raw : 0u, cc = jt ? cc_raw : 0u;
+      const bool ovf = __syncthreads_or(cc == 0xFFFFFFFFu) != 0;
+      const uint32_t off = wg_excl_scan<NT>(c, sm.wv, n_list);
+      const uint32_t coff = wg_excl_scan<NT>(ovf ? 0u : cc, sm.wv, n_cand);
+      if (!is_fast(ovf)) return final_row_general<BS>(p, r, rb, sm);
+
+      // Piece tables (kept until the candidates are gathered; the selects
+      // below clear sm.hist): candidate offsets, first blocks, list offsets.
+      uint32_t* coffs = sm.sel;
+      uint32_t* pstart = sm.sel + NT;
+      uint32_t* loffs = sm.sel + 2 * NT;
+      if (jt) {
+        coffs[t] = coff;
+        pstart[t] = (uint32_t)piece_start(p, sm, rb, r, t);
+        loffs[t] = off;
       }
-      const bool any = n_cand != 0;
+      __syncthreads();
+      // Gather the list (ids and keys) and the candidate keys in piece order.
+      // Loads are issued unconditionally (clamped index) so that a batch is in
+      // flight together; only the stores are guarded.
+      // Entry -> piece maps (in sm.hist, free until the block select) instead
+      // of a search per entry: a search loop between loads would also make the
+      // compiler wait for every load issued before it.
+      uint32_t* pmap = sm.hist;
+      build_piece_map(pmap, loffs, P, n_list, sm);
+      for (int i0 = t; i0 < (int)n_list; i0 += NT * U) {
+        uint32_t src[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint64_t v = any ? ld_shared64(&p.ws_cand[src[u]]) : 0u;
-        ccol[u] = (uint32_t)v;
-        a[u] = (uint32_t)(v >> 32);
+        for (int u = 0; u < U; ++u) {
+          const uint32_t i = (uint32_t)min(i0 + u * NT, (int)n_list - 1);
+          const uint32_t j = pmap[i];
+          src[u] = pstart[j] + (i - loffs[j]);
+        }
+        uint64_t v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = ld_shared64(&wl[src[u]]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int i = i0 + u * NT;
+          if (i < (int)n_list) {
+            lids[i] = (uint32_t)v[u];
+            lkeys[i] = (uint32_t)(v[u] >> 32);
+          }
+        }
       }
+      // Candidate keys to LDS; their columns stay in registers until the list
+      // space is free again (n_cand <= TK_CAP = U * NT: one batch).
+      __syncthreads();
+      build_piece_map(pmap, coffs, P, n_cand, sm);
+      {
+        uint32_t a[U];
+        int64_t src[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (t + u * NT < (int)n_cand) tk[t + u * NT] = a[u];
+        for (int u = 0; u < U; ++u) {
+          const uint32_t i = (uint32_t)min(t + u * NT, max((int)n_cand - 1, 0));
+          const uint32_t j = n_cand ? pmap[i] : 0u;
+          src[u] = creg + 2 * (int64_t)pstart[j] + (i - coffs[j]);
+        }
+        const bool any = n_cand != 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint64_t v = any ? ld_shared64(&p.ws_cand[src[u]]) : 0u;
+          ccol[u] = (uint32_t)v;
+          a[u] = (uint32_t)(v >> 32);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (t + u * NT < (int)n_cand) tk[t + u * NT] = a[u];
+      }
+      crem = n_cand > (uint32_t)t ? n_cand - (uint32_t)t : 0u;
     }
     __syncthreads();
     if (t == 0) st_shared(&st[6], 1u);   // the row's lists are read: -inf may go
@@ -1103,8 +1174,8 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
     uint32_t nk = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = t + u * NT;
-      if (i < (int)n_cand) {
+      if (u * cst < crem) {
+        const uint32_t i = cbase + u * cst;
         const uint32_t b = ccol[u] / BS;
         tc[i] = ccol[u];
         if ((sm.hist[b >> 5] >> (b & 31)) & 1u) ++nk;
@@ -1133,14 +1204,16 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
   }
 }
 
-// Thread 0 waits (time-bounded) until a row-state word reaches `target`.
-// Returns false if the wait gave up (status bit 1).
+// Thread 0 waits (time-bounded) until a row-state word reaches `target`; the
+// value it saw is left in sm.misc[4].  Returns false if the wait gave up
+// (status bit 1).
 DSA_DEV bool wait_at_least(const Params& p, const uint32_t* word, uint32_t target, Smem& sm) {
   if (threadIdx.x == 0) {
     uint32_t ok = 1;
-    if (ld_shared(word) < target) {
+    uint32_t v = ld_shared(word);
+    if (v < target) {
       const uint64_t t0 = wall_clock64();
-      while (ld_shared(word) < target) {
+      while ((v = ld_shared(word)) < target) {
         __builtin_amdgcn_s_sleep(8);
         if (wall_clock64() - t0 > WAIT_LIMIT_TICKS) {
           atomicOr(p.status, 2u);
@@ -1150,6 +1223,7 @@ DSA_DEV bool wait_at_least(const Params& p, const uint32_t* word, uint32_t targe
       }
     }
     sm.misc[3] = ok;
+    sm.misc[4] = v;
   }
   __syncthreads();
   return sm.misc[3] != 0u;
@@ -1178,7 +1252,7 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
   if (!wait_at_least(p, &st[3], 1u, sm)) return;
   float* rowp = row_ptr(p, r, rb);
   const bool vec = vec_ok(p, rowp);
-  const uint32_t digit = ld_shared(&st[2]);
+  const uint32_t digit = sm.misc[4] - 1u;   // the ready word holds digit + 1
   const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   uint64_t* wl = p.ws_list + (int64_t)r * p.nblocks;
   // Token candidates: every live value of a listed block whose key reaches
