@@ -42,11 +42,17 @@ namespace dsa {
 
 constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int UNROLL = 4;      // float4 loads in flight per lane in the score pass
-// Row state words: pass-1 ticket, pass-2 ticket, digit, ready word (digit + 1;
-// 0 until the digit is known), low flag, keys above the digit, lists-gathered
-// flag.  Each row's state has a 128-byte line of its own: workgroups poll
-// these words.
+// Row state words: [0] pass-1 ticket, [1] pass-2 ticket, [3] ready word (0 until
+// the row's digit d is known, then ready_word(d, keys above d's bin)), [4] low
+// flag, [6] lists-gathered flag.  Each row's state has a 128-byte line of its
+// own: workgroups poll these words.
 constexpr int ROW_STATE = 32;
+// The ready word: d + 1 in bits 0..12, the count of keys above d's bin from
+// bit 13 (it is below K_blk <= 2^17).  One word, so a workgroup that sees the
+// flag has both values, with no ordering between separate stores to rely on.
+DSA_DEV uint32_t ready_word(uint32_t d, uint32_t above) { return (d + 1u) | (above << 13); }
+DSA_DEV uint32_t ready_digit(uint32_t w) { return (w & 0x1FFFu) - 1u; }
+DSA_DEV uint32_t ready_above(uint32_t w) { return w >> 13; }
 constexpr int UNROLL_STRIDED = 8;   // scalar loads in flight per lane: 4 * this
 // One workgroup reads at most a few tens of GB/s, so a row longer than this is
 // split over its P workgroups even when its block keys would fit in LDS.
@@ -773,12 +779,9 @@ DSA_DEV void long_pass1(const Params& p, int r, int b0, int b1, int npieces, con
   uint32_t d, above, in_bin;
   find_bin<NT>(sm.hist, HIST_WORDS, (uint32_t)min(p.k_blocks, rb.nlb), sm, d, above, in_bin);
   if (threadIdx.x == 0) {
-    st_shared(&st[2], d);
-    st_shared(&st[5], above);
     st_shared(&st[6], 0u);
     st_shared(&st[0], 0u);
-    vm_drain();
-    st_shared(&st[3], d + 1u);        // the row's digit is ready (and is d)
+    st_shared(&st[3], ready_word(d, above));   // the row's digit is ready
   }
 }
 
@@ -862,7 +865,8 @@ DSA_DEV void final_row_general(const Params& p, int r, const Row& rb, Smem& sm) 
   const int t = (int)threadIdx.x;
   const bool jt = t < P;
   // One round trip: the row's digit, the keys above it, the piece counts.
-  const uint32_t digit = ld_shared(&st[2]), above = ld_shared(&st[5]);
+  const uint32_t rw = ld_shared(&st[3]);
+  const uint32_t digit = ready_digit(rw), above = ready_above(rw);
   const uint32_t c_raw = ld_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + (jt ? t : 0)]);
   const uint32_t c = jt ? c_raw : 0u;
   // Exclusive prefix of the per-piece list lengths; piece j's list starts at
@@ -984,7 +988,8 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
     uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
     const int t = (int)threadIdx.x;
     // The row's digit and the keys above it, loaded with the piece counts.
-    const uint32_t digit = ld_shared(&st[2]), above = ld_shared(&st[5]);
+    const uint32_t rw = ld_shared(&st[3]);
+    const uint32_t digit = ready_digit(rw), above = ready_above(rw);
     const uint32_t beta = digit << 20;
     float* rowp = row_ptr(p, r, rb);
     const bool vec = vec_ok(p, rowp);
@@ -1252,7 +1257,7 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
   if (!wait_at_least(p, &st[3], 1u, sm)) return;
   float* rowp = row_ptr(p, r, rb);
   const bool vec = vec_ok(p, rowp);
-  const uint32_t digit = sm.misc[4] - 1u;   // the ready word holds digit + 1
+  const uint32_t digit = ready_digit(sm.misc[4]);
   const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   uint64_t* wl = p.ws_list + (int64_t)r * p.nblocks;
   // Token candidates: every live value of a listed block whose key reaches
@@ -1270,19 +1275,32 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
   uint32_t* lbits = sm.hist;
   uint32_t cnt = 0, ccnt = 0;
   bool cover = false;
+  // Listing, one sub-chunk of CHUNK_CAP blocks at a time: keys in registers
+  // (block s0 + threadIdx.x + u * NT), listed flags by ballot, ordered
+  // compaction from per-(batch, wave) counts.  The next sub-chunk's keys are
+  // loaded while the current one is compacted.  Listed ids also go to LDS
+  // (all sub-chunks, in block order) for the candidate pass below.
+  constexpr int U = CHUNK_CAP / NT;
+  constexpr int NW = NT / 64;
+  const int w = wave(), l = lane();
+  uint32_t k[U];
+  {
+    const int n = min(b1 - b0, CHUNK_CAP);
+#pragma unroll
+    for (int u = 0; u < U; ++u) k[u] = ld_shared(&wk[b0 + min((int)threadIdx.x + u * NT, n - 1)]);
+  }
   for (int s0 = b0; s0 < b1; s0 += CHUNK_CAP) {
     const int n = min(b1 - s0, CHUNK_CAP);
-    // Keys in registers (block s0 + threadIdx.x + u * NT), listed flags by
-    // ballot, ordered compaction from per-(batch, wave) counts.
-    constexpr int U = CHUNK_CAP / NT;
-    constexpr int NW = NT / 64;
-    const int w = wave(), l = lane();
-    uint32_t k[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) k[u] = ld_shared(&wk[s0 + min((int)threadIdx.x + u * NT, n - 1)]);
     uint64_t m[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) m[u] = ballot((int)threadIdx.x + u * NT < n && (k[u] >> 20) >= digit);
+    uint32_t kn[U];
+    const int s1 = s0 + CHUNK_CAP;
+    if (s1 < b1) {
+      const int n1 = min(b1 - s1, CHUNK_CAP);
+#pragma unroll
+      for (int u = 0; u < U; ++u) kn[u] = ld_shared(&wk[s1 + min((int)threadIdx.x + u * NT, n1 - 1)]);
+    }
     if (l == 0) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -1304,63 +1322,68 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
     for (int u = 0; u < U; ++u) {
       const uint32_t pb = (uint32_t)__builtin_amdgcn_ds_bpermute((u * NW + w) << 2, (int)cx);
       if ((m[u] >> l) & 1u) {
-        const uint32_t rank = pb + mbcnt(m[u]);
+        const uint32_t rank = base + pb + mbcnt(m[u]);
         const uint32_t b = (uint32_t)(s0 + (int)threadIdx.x + u * NT);
-        st_shared64(&wl[b0 + base + rank], pair(b, k[u]));
-        lids[rank] = b;
+        st_shared64(&wl[b0 + rank], pair(b, k[u]));
+        if (rank < (uint32_t)LIST_CAP) lids[rank] = b;
       }
     }
     cnt += nl;
     __syncthreads();
-    if constexpr (PG_OK) {
-      if (pg) {
-        // One listed block per thread per round: its values (loads issued
-        // together), the count at or above beta, then ordered stores.
-        for (int j0 = 0; j0 < (int)nl; j0 += NT) {
-          const int j = j0 + (int)threadIdx.x;
-          uint32_t kk[BS];
-          int64_t c0 = 0;
-          int nv = 0;
-          if (j < (int)nl) {
-            c0 = (int64_t)lids[j] * BS;
-            nv = (int)min((int64_t)BS, (int64_t)rb.L - c0);
-            if (vec && nv == BS) {
-              f4v v[BS / 4];
+    if (s1 < b1) {
 #pragma unroll
-              for (int t = 0; t < BS / 4; ++t) v[t] = *reinterpret_cast<const f4v*>(rowp + c0 + 4 * t);
+      for (int u = 0; u < U; ++u) k[u] = kn[u];
+    }
+  }
+  if constexpr (PG_OK) {
+    if (pg && cnt > (uint32_t)LIST_CAP) cover = true;   // the ids did not all fit LDS
+    if (pg && !cover) {
+      // One listed block per thread per round: its values (loads issued
+      // together), the count at or above beta, then ordered stores.
+      for (int j0 = 0; j0 < (int)cnt; j0 += NT) {
+        const int j = j0 + (int)threadIdx.x;
+        uint32_t kk[BS];
+        int64_t c0 = 0;
+        int nv = 0;
+        if (j < (int)cnt) {
+          c0 = (int64_t)lids[j] * BS;
+          nv = (int)min((int64_t)BS, (int64_t)rb.L - c0);
+          if (vec && nv == BS) {
+            f4v v[BS / 4];
 #pragma unroll
-              for (int t = 0; t < BS / 4; ++t) {
-                kk[4 * t] = f2key(v[t].x);
-                kk[4 * t + 1] = f2key(v[t].y);
-                kk[4 * t + 2] = f2key(v[t].z);
-                kk[4 * t + 3] = f2key(v[t].w);
-              }
-            } else {
+            for (int t = 0; t < BS / 4; ++t) v[t] = *reinterpret_cast<const f4v*>(rowp + c0 + 4 * t);
 #pragma unroll
-              for (int e = 0; e < BS; ++e) kk[e] = e < nv ? f2key(rowp[(c0 + e) * p.col_stride]) : 0u;
+            for (int t = 0; t < BS / 4; ++t) {
+              kk[4 * t] = f2key(v[t].x);
+              kk[4 * t + 1] = f2key(v[t].y);
+              kk[4 * t + 2] = f2key(v[t].z);
+              kk[4 * t + 3] = f2key(v[t].w);
             }
-          }
-          uint32_t c = 0;
-#pragma unroll
-          for (int e = 0; e < BS; ++e) c += (e < nv && kk[e] >= beta) ? 1u : 0u;
-          uint32_t tot;
-          uint32_t o = wg_excl_scan<NT>(c, sm.wv, tot);
-          if (ccnt + tot > ccap) {
-            cover = true;
           } else {
 #pragma unroll
-            for (int e = 0; e < BS; ++e) {
-              if (e < nv && kk[e] >= beta) {
-                st_shared64(&p.ws_cand[creg + ccnt + o], pair((uint32_t)(c0 + e), kk[e]));
-                ++o;
-              }
-            }
-            ccnt += tot;
+            for (int e = 0; e < BS; ++e) kk[e] = e < nv ? f2key(rowp[(c0 + e) * p.col_stride]) : 0u;
           }
         }
+        uint32_t c = 0;
+#pragma unroll
+        for (int e = 0; e < BS; ++e) c += (e < nv && kk[e] >= beta) ? 1u : 0u;
+        uint32_t tot;
+        uint32_t o = wg_excl_scan<NT>(c, sm.wv, tot);
+        if (ccnt + tot > ccap) {
+          cover = true;
+          break;
+        }
+#pragma unroll
+        for (int e = 0; e < BS; ++e) {
+          if (e < nv && kk[e] >= beta) {
+            st_shared64(&p.ws_cand[creg + ccnt + o], pair((uint32_t)(c0 + e), kk[e]));
+            ++o;
+          }
+        }
+        ccnt += tot;
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
   if (threadIdx.x == 0) {
     st_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + part], cnt);
