@@ -120,6 +120,34 @@ def test_fused_long_rows_with_start_and_stride():
     _full_check(dc, bids, tids, scores)
 
 
+def test_fused_large_k_blocks():
+    """K_blk = 100000 of 131072 blocks: the count of keys above the digit's bin
+    needs 17 bits of the row's ready word."""
+    ends = [1048576, 900001]
+    case = wl.make_custom(len(ends), 1048576, 8, 100000, 2048, ends, seed=5, dup_frac=0.01)
+    gh.log(f"large k_blocks ends={ends}")
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused()
+    _full_check(dc, bids, tids, scores)
+
+
+def test_fused_long_rows_concentrated_lists():
+    """Sixteen long rows; in the even ones the values rise along the row, so
+    every kept block lies in the row's last pieces (more listed entries per
+    piece than the final workgroup's per-piece share: the general gather),
+    while the odd rows are random (the one-round-trip gather)."""
+    W = 262144
+    ends = [W, W - 3, 200001, W, 150000, W - 8, W, 131073] * 2
+    case = wl.make_custom(len(ends), W, 8, 2048, 2048, ends, seed=23, outlier_frac=0.01)
+    for r in range(0, len(ends), 2):
+        e = ends[r]
+        case.logits[r, :e] = np.linspace(-3.0, 3.0, e, dtype=np.float32)
+    gh.log(f"concentrated lists ends={ends}")
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused()
+    _full_check(dc, bids, tids, scores)
+
+
 @pytest.mark.parametrize("W,B,kb,kt", [(3000, 8, 40, 300), (5000, 4, 300, 2048),
                                        (70000, 8, 600, 2048), (40000, 16, 64, 4000)])
 def test_fused_special_values(W, B, kb, kt):
