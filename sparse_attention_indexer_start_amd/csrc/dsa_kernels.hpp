@@ -362,16 +362,24 @@ DSA_DEV void mask_blocks(float* rowp, int64_t cs, int B, int L, int b0, int b1, 
   const int64_t cbeg = (int64_t)b0 * B;
   const int64_t cend = min((int64_t)b1 * B, (int64_t)L);
   if constexpr (BS >= 4) {
-    for (int64_t col = cbeg + (int64_t)threadIdx.x * 4; col < cend; col += (int64_t)NT * 4) {
-      if (!masked((int)(col / BS))) continue;
-      if (vec && col + 4 <= cend) {
-        store_ninf4(rowp + col);
-      } else {
+    if (vec) {
+      for (int64_t col = cbeg + (int64_t)threadIdx.x * 4; col < cend; col += (int64_t)NT * 4) {
+        if (!masked((int)(col / BS))) continue;
+        if (col + 4 <= cend) {
+          store_ninf4(rowp + col);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (col + j < cend) store_ninf(rowp + (col + j) * cs);
+          for (int j = 0; j < 4; ++j)
+            if (col + j < cend) store_ninf(rowp + col + j);
+        }
       }
+      return;
     }
+    // Strided or unaligned: one column per lane, so each store instruction
+    // covers consecutive columns (each touched line once, not once per
+    // column of a lane's group).
+    for (int64_t col = cbeg + (int64_t)threadIdx.x; col < cend; col += NT)
+      if (masked((int)(col / BS))) store_ninf(rowp + col * cs);
   } else {
     for (int64_t col = cbeg + (int64_t)threadIdx.x; col < cend; col += NT)
       if (masked(div_b<BS>(col, B))) store_ninf(rowp + col * cs);

@@ -223,7 +223,7 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
     // with the rows' owners that is one resident round at two workgroups per
     // CU when NQ = 2 * CUs - rows + 1, less a reserve of slots for the rows'
     // final workgroups, which run while the pass-2 pieces still store -inf.
-    const int64_t reserve = std::min<int64_t>(s->rows, 64);
+    const int64_t reserve = std::min<int64_t>(s->rows, 128);
     c->NQ = (int32_t)std::max<int64_t>(
         1, std::min<int64_t>((int64_t)c->cus * 2 - s->rows + 1 - reserve, NT));
     c->balanced = (s->rows >= 1 && s->rows <= c->cus && s->rows <= 256) ? 1 : 0;
