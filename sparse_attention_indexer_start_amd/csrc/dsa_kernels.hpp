@@ -216,7 +216,38 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
     const int64_t t4 = (int64_t)threadIdx.x * 4;
     const bool leader = (threadIdx.x % G) == 0;
     if (!vec) {
-      // Strided or unaligned: scalar loads, UNROLL_STRIDED groups in flight.
+      if constexpr (BS == 16) {
+        // Strided or unaligned: one column per lane per slot, so the lanes of
+        // a load instruction read consecutive columns (each touched line is
+        // requested once, not once per column of a lane's group); a block is
+        // 16 consecutive lanes.  (For B of 4 and 8 this form makes the
+        // compiler give the kernel a scratch frame, so they keep the form
+        // below.)
+        constexpr int US = 2 * UNROLL_STRIDED;
+        const bool lead = (threadIdx.x % BS) == 0;
+        for (int64_t c0 = cbeg; c0 < cend; c0 += (int64_t)NT * US) {
+          float v[US];
+#pragma unroll
+          for (int u = 0; u < US; ++u) {
+            const int64_t col = c0 + (int64_t)u * NT + threadIdx.x;
+            v[u] = col < cend ? rowp[col * cs] : __uint_as_float(0xFFFFFFFFu);
+          }
+#pragma unroll
+          for (int u = 0; u < US; ++u) {
+            const int64_t col = c0 + (int64_t)u * NT + threadIdx.x;
+            const uint32_t kk = f2key(v[u]);
+            low |= col < cend && kk <= KEY_NEG_INF;
+            const uint32_t m = group_max<BS>(kk);
+            if (lead && col < cend) {
+              const int b = (int)(col / BS);
+              emit(b, b == nlb - 1 ? KEY_POS_INF : m);
+            }
+          }
+        }
+        return;
+      }
+      // Strided or unaligned, other B: scalar loads, UNROLL_STRIDED groups of 4
+      // in flight.
       const int64_t sstep = (int64_t)NT * 4 * UNROLL_STRIDED;
       for (int64_t c0 = cbeg; c0 < cend; c0 += sstep) {
         float v[UNROLL_STRIDED][4];
