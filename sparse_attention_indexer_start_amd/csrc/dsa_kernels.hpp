@@ -42,6 +42,10 @@ namespace dsa {
 
 constexpr int NT = 512;        // threads per workgroup (8 waves)
 constexpr int UNROLL = 4;      // float4 loads in flight per lane in the score pass
+// ... and in a long row's pass 1, which streams the whole row (measured: 8 in
+// flight there is 1 us faster on 1M-wide rows; the one-workgroup path of short
+// rows is faster with 4).
+constexpr int UNROLL_LONG = 8;
 // Row state words: [0] pass-1 ticket, [1] pass-2 ticket, [3] ready word (0 until
 // the row's digit d is known, then ready_word(d, keys above d's bin)), [4] low
 // flag, [6] lists-gathered flag.  Each row's state has a 128-byte line of its
@@ -206,7 +210,7 @@ DSA_DEV uint32_t block_max_key(const float* rowp, int64_t cs, bool vec, int64_t 
 // Block scores of blocks [b0, b1): emit(b, key) once per block.
 // ---------------------------------------------------------------------------
 // `low` is set when some live value of the range ranks at or below -inf.
-template <int BS, class Emit>
+template <int BS, int UNR = UNROLL, class Emit>
 DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, int b1,
                           int nlb, bool vec, Emit emit, bool& low) {
   if constexpr (BS >= 4) {
@@ -277,16 +281,16 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
       }
       return;
     }
-    const int64_t step = (int64_t)NT * 4 * UNROLL;
+    const int64_t step = (int64_t)NT * 4 * UNR;
     for (int64_t c0 = cbeg; c0 < cend; c0 += step) {
-      uint32_t k[UNROLL];
+      uint32_t k[UNR];
       if (vec) {
-        // Whole vectors first, so that all UNROLL loads are in flight together;
+        // Whole vectors first, so that all UNR loads are in flight together;
         // the one partial vector at the end of the range is filled afterwards.
         const float z = __uint_as_float(0xFFFFFFFFu);    // key 0: below every float
-        f4v v[UNROLL];
+        f4v v[UNR];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
+        for (int u = 0; u < UNR; ++u) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
           v[u] = col + 4 <= cend ? *reinterpret_cast<const f4v*>(rowp + col) : f4v{z, z, z, z};
         }
@@ -294,7 +298,7 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
         // their loads are in flight together with the vector loads.
         int tu = -1;
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
+        for (int u = 0; u < UNR; ++u) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
           if (col < cend && col + 4 > cend) tu = u;
         }
@@ -306,10 +310,10 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
           if (col + 2 < cend) t2 = rowp[col + 2];
         }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
+        for (int u = 0; u < UNR; ++u)
           if (u == tu) v[u] = f4v{t0, t1, t2, z};
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
+        for (int u = 0; u < UNR; ++u) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
           k[u] = max(max(f2key(v[u].x), f2key(v[u].y)), max(f2key(v[u].z), f2key(v[u].w)));
 #pragma unroll
@@ -317,16 +321,16 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
             low |= (col + j < cend) && f2key(v[u][j]) <= KEY_NEG_INF;
         }
       } else {
-        float v[UNROLL][4];
+        float v[UNR][4];
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
+        for (int u = 0; u < UNR; ++u) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             v[u][j] = (col + j < cend) ? rowp[(col + j) * cs] : __uint_as_float(0xFFFFFFFFu);
         }
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
+        for (int u = 0; u < UNR; ++u) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
           k[u] = max(max(f2key(v[u][0]), f2key(v[u][1])), max(f2key(v[u][2]), f2key(v[u][3])));
 #pragma unroll
@@ -335,7 +339,7 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
         }
       }
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
+      for (int u = 0; u < UNR; ++u) {
         const uint32_t m = group_max<G>(k[u]);
         const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
         if (leader && col < cend) {
@@ -347,10 +351,10 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
   } else if constexpr (BS == 1 || BS == 2) {
     const int64_t cbeg = (int64_t)b0 * BS;
     const int64_t cend = min((int64_t)b1 * BS, (int64_t)L);
-    for (int64_t c0 = cbeg + (int64_t)threadIdx.x * 4; c0 < cend; c0 += (int64_t)NT * 4 * UNROLL) {
-      uint32_t k[UNROLL][4];
+    for (int64_t c0 = cbeg + (int64_t)threadIdx.x * 4; c0 < cend; c0 += (int64_t)NT * 4 * UNR) {
+      uint32_t k[UNR][4];
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
+      for (int u = 0; u < UNR; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + j;
@@ -358,7 +362,7 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
           low |= col < cend && k[u][j] <= KEY_NEG_INF;
         }
 #pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
+      for (int u = 0; u < UNR; ++u)
 #pragma unroll
         for (int j = 0; j < 4; j += BS) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + j;
@@ -792,7 +796,8 @@ DSA_DEV void long_pass1(const Params& p, int r, int b0, int b1, int npieces, con
   uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   float* sc = p.scores ? p.scores + (int64_t)r * p.nblocks : nullptr;
   bool low = false;
-  score_blocks<BS>(rowp, p.col_stride, p.B, rb.L, b0, b1, rb.nlb, vec, [&](int b, uint32_t k) {
+  constexpr int UNR = BS >= 4 ? UNROLL_LONG : UNROLL;   // (B of 1, 2: registers)
+  score_blocks<BS, UNR>(rowp, p.col_stride, p.B, rb.L, b0, b1, rb.nlb, vec, [&](int b, uint32_t k) {
     st_shared(&wk[b], k);
     if (sc) sc[b] = key2f(k);
     atomicAdd(&sm.hist[k >> 20], 1u);
