@@ -17,14 +17,15 @@
 //
 // A row with at most LIST_CAP live blocks is handled end to end by its first
 // workgroup from LDS.  A longer row is split over its P workgroups in two
-// passes of one launch: pass 1 scores a chunk of blocks into the workspace and
-// adds a 12-bit key-digit histogram; the last pass-1 workgroup of the row finds
-// the digit that holds the K_blk-th score and raises the row's ready flag.
-// Pass-2 workgroups (grid indices above every pass-1 workgroup) wait for that
-// flag, mask each block below the digit and list the others; the last of them
-// settles the exact selection among the listed blocks, masks the rejected ones
-// and runs the token top-k.  A pass-2 workgroup waits only for workgroups with
-// lower grid indices, which never wait, and its wait is time-bounded.
+// passes of one launch: pass 1 scores a chunk of blocks into the workspace,
+// adds a 12-bit key-digit histogram and takes the row's pass-1 ticket.
+// Pass-2 workgroups (grid indices above every pass-1 workgroup) wait until
+// every ticket is in, find the digit that holds the K_blk-th score from the
+// histogram, mask each block below the digit and list the others; the row's
+// final workgroup settles the exact selection among the listed blocks, masks
+// the rejected ones and runs the token top-k.  A pass-2 or final workgroup
+// waits only for workgroups with lower grid indices, which never wait on
+// higher ones, and its wait is time-bounded.
 //
 // This header holds the kernel templates; each block-size specialisation is
 // compiled in a translation unit of its own (dsa_bs_unit.hip) and reached
@@ -46,9 +47,9 @@ constexpr int UNROLL = 4;      // float4 loads in flight per lane in the score p
 // flight there is 1 us faster on 1M-wide rows; the one-workgroup path of short
 // rows is faster with 4).
 constexpr int UNROLL_LONG = 8;
-// Row state words: [0] pass-1 ticket, [1] pass-2 ticket, [3] ready word (0 until
-// the row's digit d is known, then ready_word(d, keys above d's bin)), [4] low
-// flag, [6] lists-gathered flag.  Each row's state has a 128-byte line of its
+// Row state words: [0] pass-1 ticket, [1] pass-2 ticket, [3] ready word (written
+// by the pass-2 pieces for the final step: ready_word(d, keys above d's bin)),
+// [4] low flag, [6] lists-gathered flag.  Each row's state has a 128-byte line of its
 // own: workgroups poll these words.
 constexpr int ROW_STATE = 32;
 // The ready word: d + 1 in bits 0..12, the count of keys above d's bin from
@@ -809,24 +810,12 @@ DSA_DEV void long_pass1(const Params& p, int r, int b0, int b1, int npieces, con
     const uint32_t c = sm.hist[j];
     if (c) atomicAdd(&gh[j], c);
   }
-  if (!arrive_last(&st[0], (uint32_t)npieces, sm)) return;
-  constexpr int PER = HIST_WORDS / NT;
-  uint32_t h[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) h[u] = ld_shared(&gh[threadIdx.x + u * NT]);
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    sm.hist[threadIdx.x + u * NT] = h[u];
-    if (h[u]) st_shared(&gh[threadIdx.x + u * NT], 0u);   // clean for the next call
-  }
-  __syncthreads();
-  uint32_t d, above, in_bin;
-  find_bin<NT>(sm.hist, HIST_WORDS, (uint32_t)min(p.k_blocks, rb.nlb), sm, d, above, in_bin);
-  if (threadIdx.x == 0) {
-    st_shared(&st[6], 0u);
-    st_shared(&st[0], 0u);
-    st_shared(&st[3], ready_word(d, above));   // the row's digit is ready
-  }
+  // The row's lists-read flag is cleared before the ticket (pass 2 holds its
+  // -inf stores until the final workgroup sets it); once all npieces tickets
+  // are in, the pass-2 pieces find the digit from the histogram themselves.
+  if (threadIdx.x == 0) st_shared(&st[6], 0u);
+  (void)arrive_last(&st[0], 0u, sm);
+  (void)npieces;
 }
 
 // map[i] = the piece holding entry i of the pieces' concatenated lists, for
@@ -1295,13 +1284,28 @@ DSA_DEV void hold_for(const uint32_t* flag) {
 // the piece.  The row's final workgroup starts as soon as all lists are in.
 // ---------------------------------------------------------------------------
 template <int BS>
-DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const Row& rb,
-                        Smem& sm) {
+DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, int npieces,
+                        const Row& rb, Smem& sm) {
   uint32_t* st = p.ws_row + (int64_t)r * ROW_STATE;
-  if (!wait_at_least(p, &st[3], 1u, sm)) return;
+  if (!wait_at_least(p, &st[0], (uint32_t)npieces, sm)) return;
+  // Every pass-1 ticket is in, so the row's histogram is complete: find the
+  // digit d of the K_blk-th block key (every piece does, with the same
+  // result) and publish it with the count above d's bin for the final step.
+  uint32_t* gh = p.ws_hist + (int64_t)r * HIST_WORDS;
+  {
+    constexpr int PER = HIST_WORDS / NT;
+    uint32_t h[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) h[u] = ld_shared(&gh[threadIdx.x + u * NT]);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) sm.hist[threadIdx.x + u * NT] = h[u];
+    __syncthreads();
+  }
+  uint32_t digit, above, in_bin;
+  find_bin<NT>(sm.hist, HIST_WORDS, (uint32_t)min(p.k_blocks, rb.nlb), sm, digit, above, in_bin);
+  if (threadIdx.x == 0) st_shared(&st[3], ready_word(digit, above));
   float* rowp = row_ptr(p, r, rb);
   const bool vec = vec_ok(p, rowp);
-  const uint32_t digit = ready_digit(sm.misc[4]);
   const uint32_t* wk = p.ws_key + (int64_t)r * p.nblocks;
   uint64_t* wl = p.ws_list + (int64_t)r * p.nblocks;
   // Token candidates: every live value of a listed block whose key reaches
@@ -1433,7 +1437,18 @@ DSA_DEV void long_pass2(const Params& p, int r, int b0, int b1, int part, const 
     st_shared(&p.ws_cnt[(int64_t)r * p.cnt_stride + part], cnt);
     st_shared(&p.ws_ccnt[(int64_t)r * p.cnt_stride + part], (pg && !cover) ? ccnt : 0xFFFFFFFFu);
   }
-  (void)arrive_last(&st[1], 0u, sm);
+  if (arrive_last(&st[1], (uint32_t)npieces, sm)) {
+    // The last piece of the row: every piece has read the histogram, so its
+    // non-zero bins and the pass-1 ticket are cleared for the next call.
+    constexpr int PER = HIST_WORDS / NT;
+    uint32_t h[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) h[u] = ld_shared(&gh[threadIdx.x + u * NT]);
+#pragma unroll
+    for (int u = 0; u < PER; ++u)
+      if (h[u]) st_shared(&gh[threadIdx.x + u * NT], 0u);
+    if (threadIdx.x == 0) st_shared(&st[0], 0u);
+  }
   if (!(p.flags & DSA_WRITE_MASK)) return;
   // (The balanced split keeps slots free for the final workgroups, which
   // are therefore resident; in the per-row split they may not be.)
@@ -1570,7 +1585,7 @@ DSA_DEV void balanced_piece(const Params& p, int k, bool pass2, Smem& sm) {
   const int part = worker_of(sm, p.rows, s0) - w0;
   const int b0 = (int)(s0 - rs), b1 = (int)(s1 - rs);
   if (!pass2) long_pass1<BS>(p, r, b0, b1, np, rb, sm);
-  else long_pass2<BS>(p, r, b0, b1, part, rb, sm);
+  else long_pass2<BS>(p, r, b0, b1, part, np, rb, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1606,7 +1621,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   int b0, b1;
   chunk_of(rb, p.P, part, b0, b1);
   if (!pass2) long_pass1<BS>(p, r, b0, b1, p.P, rb, sm);
-  else long_pass2<BS>(p, r, b0, b1, part, rb, sm);
+  else long_pass2<BS>(p, r, b0, b1, part, p.P, rb, sm);
 }
 
 template <int BS>
