@@ -316,11 +316,16 @@ DSA_DEV void radix_low_passes(ForKeys for_keys, uint32_t prefix, uint32_t krem, 
 // Radix passes of the top-K rule below over keys visited by
 // for_keys(f) (f(key) once per element).  Digits of 12, 12 and 8 bits over
 // the 4096-word histogram, which must be zero on entry and is zero on return.
+// top_counted: the caller has already counted every key's top digit into the
+// histogram (and passed a barrier since).
 template <int NT, class ForKeys>
-DSA_DEV void radix_passes(ForKeys for_keys, uint32_t K, Smem& sm, uint32_t& T, uint32_t& q) {
+DSA_DEV void radix_passes(ForKeys for_keys, uint32_t K, Smem& sm, uint32_t& T, uint32_t& q,
+                          bool top_counted = false) {
   uint32_t d, above, in_bin;
-  for_keys([&](uint32_t k) { atomicAdd(&sm.hist[k >> 20], 1u); });
-  __syncthreads();
+  if (!top_counted) {
+    for_keys([&](uint32_t k) { atomicAdd(&sm.hist[k >> 20], 1u); });
+    __syncthreads();
+  }
   find_bin_zero<NT, 4096>(sm.hist, K, sm, d, above, in_bin);
   const uint32_t krem = K - above;
   if (in_bin == krem) return keep_from(d << 20, T, q);
@@ -329,7 +334,7 @@ DSA_DEV void radix_passes(ForKeys for_keys, uint32_t K, Smem& sm, uint32_t& T, u
 
 template <int NT, int U, class GetKey>
 DSA_DEV void radix_select_regs(int n, uint32_t K, GetKey getk, Smem& sm, uint32_t& T,
-                               uint32_t& q) {
+                               uint32_t& q, bool top_counted = false) {
   uint32_t k[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -340,7 +345,7 @@ DSA_DEV void radix_select_regs(int n, uint32_t K, GetKey getk, Smem& sm, uint32_
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if ((int)threadIdx.x + u * NT < n) f(k[u]);
-  }, K, sm, T, q);
+  }, K, sm, T, q, top_counted);
 }
 
 // The (T, q) rule for the top K of getk(0..n), n <= 8 * NT, when the top
@@ -378,17 +383,19 @@ DSA_DEV void wg_radix_select_low(int n, uint32_t d20, uint32_t krem, GetKey getk
 // whole.  Up to 8 * NT keys are held in registers across the passes; longer
 // inputs are re-read each pass, U loads at a time per thread.
 // hist_zero: the caller guarantees sm.hist[0..4096) is zero.  On return it is.
+// top_counted: instead, the caller has counted every key's top 12-bit digit
+// into sm.hist (and passed a barrier since).
 template <int NT, int U = 8, class GetKey>
 DSA_DEV void wg_radix_select(int n, uint32_t K, GetKey getk, Smem& sm, uint32_t& T,
-                             uint32_t& q, bool hist_zero = false) {
-  if (!hist_zero) {
+                             uint32_t& q, bool hist_zero = false, bool top_counted = false) {
+  if (!hist_zero && !top_counted) {
     for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
     __syncthreads();
   }
-  if (n <= NT) return radix_select_regs<NT, 1>(n, K, getk, sm, T, q);
-  if (n <= 2 * NT) return radix_select_regs<NT, 2>(n, K, getk, sm, T, q);
-  if (n <= 4 * NT) return radix_select_regs<NT, 4>(n, K, getk, sm, T, q);
-  if (n <= 8 * NT) return radix_select_regs<NT, 8>(n, K, getk, sm, T, q);
+  if (n <= NT) return radix_select_regs<NT, 1>(n, K, getk, sm, T, q, top_counted);
+  if (n <= 2 * NT) return radix_select_regs<NT, 2>(n, K, getk, sm, T, q, top_counted);
+  if (n <= 4 * NT) return radix_select_regs<NT, 4>(n, K, getk, sm, T, q, top_counted);
+  if (n <= 8 * NT) return radix_select_regs<NT, 8>(n, K, getk, sm, T, q, top_counted);
   radix_passes<NT>([&](auto f) {
     for (int i0 = threadIdx.x; i0 < n; i0 += NT * U) {
       uint32_t k[U];
@@ -401,7 +408,7 @@ DSA_DEV void wg_radix_select(int n, uint32_t K, GetKey getk, Smem& sm, uint32_t&
       for (int u = 0; u < U; ++u)
         if (i0 + u * NT < n) f(k[u]);
     }
-  }, K, sm, T, q);
+  }, K, sm, T, q, top_counted);
 }
 
 // Ordered application of the (T, q) rule to [0, n), n <= 8 * NT, keys held in

@@ -745,13 +745,17 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
     // The select's histogram starts from zero; cleared while the loads fly.
     for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
     bool low = false;
+    // When a select follows, each key's top digit is counted as it is scored
+    // (the select's first histogram), and the barrier below completes it.
+    const bool do_select = nlb > Kp;
     score_blocks<BS>(rowp, p.col_stride, B, L, 0, nlb, nlb, vec, [&](int b, uint32_t k) {
       keys[b] = k;
       if (sc) sc[b] = key2f(k);
+      if (do_select) atomicAdd(&sm.hist[k >> 20], 1u);
     }, low);
     no_low = __syncthreads_or(low) == 0;
     auto getk = [&](int i) { return keys[i]; };
-    if (nlb > Kp) wg_radix_select<NT>(nlb, (uint32_t)Kp, getk, sm, T, q, true);
+    if (do_select) wg_radix_select<NT>(nlb, (uint32_t)Kp, getk, sm, T, q, true, true);
     // One ordered pass: kept ids out, the lowest non-kept ids listed (for the
     // token fill), and each non-kept block masked by the lane that owns it.
     const bool do_mask = (p.flags & DSA_WRITE_MASK) && nlb > Kp;
