@@ -221,6 +221,91 @@ def pin_buffer_bounds_worked(o):
     assert mk[1].tolist() == [5.0] * 12
 
 
+_REPEAT_ROW = [5, 1, 4, 9, 2, 6, 3, 8]     # every row's values in the repeat pins
+
+
+def pin_starts_repeat_worked(o):
+    """Per-request starts read at row // starts_repeat, per-row ends.
+
+    The report on PR #56628 (key source) loads a row's start and end at
+    row // ROW_REPEAT.  Two requests of four rows each: starts [1, 4] (the
+    array carries six more entries that the rule never reads), ends per row
+    [3, 4, 5, 9, 5, 6, 8, 20], width 8, B=2, K_blk=2, K_tok=3, every row
+    holding [5, 1, 4, 9, 2, 6, 3, 8].  Worked by hand:
+
+    row 0  s=1 [1,3)   one block            blocks [0]    tokens 1 2
+    row 1  s=1 [1,4)   {1,2} {3}            blocks [0 1]  tokens 1 2 3
+    row 2  s=1 [1,5)   {1,2} {3,4}          blocks [0 1]  tokens 2 3 4 (9, 4, 2)
+    row 3  s=1 [1,8)   maxima 4 9 6 | pin   blocks [1 3]  cols 1 2 5 6 -> -inf,
+                                                          tokens 3 4 7 (9, 8, 2)
+    row 4  s=4 [4,5)                        blocks [0]    tokens 4
+    row 5  s=4 [4,6)   {4,5}                blocks [0]    tokens 4 5
+    row 6  s=4 [4,8)   {4,5} {6,7}          blocks [0 1]  tokens 5 6 7 (8, 6, 3)
+    row 7  s=4 end 20 clamps to 8: as row 6
+    """
+    lg = np.tile(np.array(_REPEAT_ROW, dtype=np.float32), (8, 1))
+    starts = np.array([1, 4, 0, 2, 3, 0, 6, 5], dtype=np.int32)
+    ends = np.array([3, 4, 5, 9, 5, 6, 8, 20], dtype=np.int32)
+    bl, tk, sc, mk = o.select_fused(lg, starts, ends, 2, 2, 3, starts_repeat=4, ends_repeat=1)
+    assert bl.tolist() == [[0, -1], [0, 1], [0, 1], [1, 3], [0, -1], [0, -1], [0, 1], [0, 1]], bl
+    assert tk.tolist() == [[1, 2, -1], [1, 2, 3], [2, 3, 4], [3, 4, 7], [4, -1, -1],
+                           [4, 5, -1], [5, 6, 7], [5, 6, 7]], tk
+    want = lg.copy()
+    want[3, [1, 2, 5, 6]] = NEG_INF
+    assert np.array_equal(mk.view(np.uint32), want.view(np.uint32))
+    for r in range(8):
+        assert o.row_bounds(r, starts, ends, 8, 4, 1)[:2] == (
+            [1, 4][r // 4], min(int(ends[r]), 8)), r
+
+
+def pin_ends_repeat_worked(o):
+    """Ends read at row // ends_repeat (starts absent: every row starts at 0).
+
+    ends_repeat=2 over ends [5, 9, 3, 8] (the array carries four more entries
+    that the rule never reads); width 8, B=2, K_blk=2, K_tok=3, every row
+    holding [5, 1, 4, 9, 2, 6, 3, 8].  Worked by hand:
+
+    end 5        maxima 5 9 | pin        blocks [1 2]  cols 0 1 -> -inf,
+                                                       tokens 2 3 4 (9, 4, 2)
+    end 9 -> 8   maxima 5 9 6 | pin      blocks [1 3]  cols 0 1 4 5 -> -inf,
+                                                       tokens 2 3 7 (9, 8, 4)
+    end 3        {0,1} {2}               blocks [0 1]  tokens 0 1 2
+    end 8        as end 9
+    """
+    lg = np.tile(np.array(_REPEAT_ROW, dtype=np.float32), (8, 1))
+    ends = np.array([5, 9, 3, 8, 1, 2, 7, 6], dtype=np.int32)
+    bl, tk, sc, mk = o.select_fused(lg, None, ends, 2, 2, 3, starts_repeat=1, ends_repeat=2)
+    per_end = {5: ([1, 2], [2, 3, 4], [0, 1]), 9: ([1, 3], [2, 3, 7], [0, 1, 4, 5]),
+               3: ([0, 1], [0, 1, 2], []), 8: ([1, 3], [2, 3, 7], [0, 1, 4, 5])}
+    want = lg.copy()
+    for r in range(8):
+        b, t, cols = per_end[[5, 9, 3, 8][r // 2]]
+        assert bl[r].tolist() == b and tk[r].tolist() == t, (r, bl[r], tk[r])
+        want[r, cols] = NEG_INF
+    assert np.array_equal(mk.view(np.uint32), want.view(np.uint32))
+
+
+def pin_mask_ignores_invalid_ids(o):
+    """Block ids of -1, negative, nlb or beyond select nothing.
+
+    The page's mask flags a block only for candidate ids inside the row's
+    blocks (report on PR #56628, key source: candidate_blocks feed the flags).
+    Row [0, 7) at B=2 has blocks {0,1} {2,3} {4,5} {6}; the ids list block 1
+    once among -1, -7, 4 (= nlb) and 10**6.  Columns 0 1 4 5 6 become -inf,
+    columns 2 3 keep their values, column 7 (past end) is untouched; the
+    newest block is not listed, so it is masked too.
+    """
+    vals = np.array([5, 1, 4, 9, 2, 6, 3, 8], dtype=np.float32)
+    ids = [-1, 1, -7, 4, 10**6]
+    got = o.mask_live(vals[:7], 2, np.array(ids, dtype=np.int64))
+    want = [NEG_INF, NEG_INF, 4.0, 9.0, NEG_INF, NEG_INF, NEG_INF]
+    assert got.tolist() == want, got
+    lg = vals[None, :].copy()
+    out = o.candidate_mask(lg, None, np.array([7], np.int32), 2,
+                           np.array([ids], dtype=np.int32))
+    assert out[0].tolist() == want + [8.0], out
+
+
 # ---------------------------------------------------------------------------
 # Special cases that reduce to a plain routine
 # ---------------------------------------------------------------------------

@@ -156,7 +156,34 @@ def _m_descending_output(o):
     o.top_k_indices = top_k_indices
 
 
+def _m_repeat_ignored(o):
+    def row_bounds(row, starts, ends, width, starts_repeat=1, ends_repeat=1):
+        s = 0 if starts is None else int(starts[row])         # indexes by row, not row // repeat
+        e = int(ends[row])
+        e_c = min(e, width)
+        if s < 0:
+            return s, e_c, 0
+        return s, e_c, max(0, e_c - s)
+    o.row_bounds = row_bounds
+
+
+def _m_negative_id_wraps(o):
+    def mask_live(vals, B, kept_blocks):
+        out = np.array(vals, dtype=np.float32, copy=True)
+        L = out.size
+        nlb = o.num_live_blocks(L, B)
+        keep = np.zeros(nlb, dtype=bool)
+        kb = np.asarray(kept_blocks, dtype=np.int64)
+        kb = kb[(kb >= -nlb) & (kb < nlb)]                    # a -1 wraps to the newest block
+        keep[kb] = True
+        out.view(np.uint32)[~np.repeat(keep, B)[:L]] = o.NEG_INF_BITS
+        return out
+    o.mask_live = mask_live
+
+
 MUTANTS = {
+    "repeat_ignored": _m_repeat_ignored,
+    "negative_id_wraps": _m_negative_id_wraps,
     "tie_to_higher_index": _m_tie_high,
     "selects_smallest": _m_smallest,
     "key_forgets_negatives": _m_key_sign,
