@@ -9,9 +9,13 @@ sigma 0.8) clipped to [1, 8192].
 
 The timed region is a HIP-graph replay of K steps, each on its own copy of
 the input (so every step sees unmasked logits and no step hits another's
-cache lines), bracketed by device synchronisation.  Per-call kernel time is
-then measured with HIP events around each call on the launch stream, and the
-CPU oracle is timed on a bounded sample of the same workload.
+cache lines), bracketed by device synchronisation and by HIP events on the
+launch stream; ms_per_step is the events' time over K.  The roofline
+fraction divides the algorithmic bytes of one call (4*L read per row, the
+-inf stores, the index stores and 8 bytes of bounds per row) by ms_per_step.
+The same run also times the long-decode workload (32 rows x 1M width, the
+bandwidth-bound case) under the key "long_decode", and the C oracle is timed
+on all host threads over whole passes of the default workload.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one GPU.
 """
@@ -48,85 +52,53 @@ def measured_traffic(workload: str, sha: str):
 
 
 def cpu_baseline(case, seconds: float):
-    """The oracle as it stands, on a bounded sample of the same rows."""
-    import numpy as np
-    import oracle
+    """The C oracle as it stands, on all host threads, over whole passes of the
+    same workload rows (about ``seconds`` of work)."""
+    from oracle import c_oracle
     sh = case.shape
-    rows = list(range(sh.rows))
-    lens = [oracle.row_bounds(r, case.starts, case.ends, sh.width, sh.starts_repeat,
-                              sh.ends_repeat)[2] for r in rows]
-    # Longest rows first would bias the sample; walk rows in order.
-    done = 0
-    t0 = time.perf_counter()
-    passes = 0
+    threads = c_oracle.default_threads()
+    c_oracle.load()
+    # Calibrate: double the pass count until a call takes a tenth of the budget.
+    reps = 1
     while True:
-        for r in rows:
-            s, e, L = oracle.row_bounds(r, case.starts, case.ends, sh.width,
-                                        sh.starts_repeat, sh.ends_repeat)
-            if L:
-                live = np.array(case.logits[r, s:e], dtype=np.float32)
-                oracle.select_row(live, sh.block_size, sh.k_blocks, sh.k_tokens)
-            done += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        else:
-            passes += 1
-            continue
-        break
+        t0 = time.perf_counter()
+        c_oracle.select_case(case, with_scores=False, threads=threads, repeat=reps)
+        dt = time.perf_counter() - t0
+        if dt >= 0.1 * seconds or reps >= 1 << 20:
+            break
+        reps *= 2
+    reps = int(max(1, min(1 << 24, reps * seconds / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    c_oracle.select_case(case, with_scores=False, threads=threads, repeat=reps)
     dt = time.perf_counter() - t0
-    return dict(value=done / dt, unit="rows/s", cores=1, kind="oracle",
-                sample=f"{done} rows of the workload in order ({passes} full passes), "
-                       f"{dt:.1f} s on 1 host thread (numpy)",
-                live_columns_per_row_mean=float(np.mean(lens)))
+    return dict(value=sh.rows * reps / dt, unit="rows/s", cores=threads, kind="oracle",
+                sample=f"{reps} full passes over the {sh.rows} rows of the workload "
+                       f"({sh.rows * reps} rows), {dt:.1f} s on {threads} host threads "
+                       f"(C oracle: threshold selection; mask written to a copy)")
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="short_decode",
-                    choices=["tiny", "short_decode", "mtp_ragged", "long_decode", "prefill_chunk"])
-    ap.add_argument("--no-graph", action="store_true", help="time eager calls instead")
-    ap.add_argument("--no-mask", action="store_true", help="do not write the mask")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--buffer-budget-gb", type=float, default=48.0)
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); the selection has no multi-GPU path here.",
-              file=sys.stderr)
-        return 2
-
+def run_workload(name: str, steps: int, warmup: int, write_mask: bool, use_graph: bool,
+                 budget_gb: float, width=None) -> dict:
+    """Graph replay of `steps` fused calls, each on its own copy of the input."""
     import numpy as np
     import torch
     from sparse_attention_indexer_start_amd import binding, metrics
     from sparse_attention_indexer_start_amd import workloads as wl
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
-    binding.load()
     dev = torch.device("cuda", 0)
-
-    log(f"generating {args.workload}")
-    case = wl.make_config(args.workload)
+    log(f"{name}: generating" + (f" at width {width}" if width else ""))
+    case = wl.make_config(name, width=width)
     sh = case.shape
-    write_mask = not args.no_mask
     nbytes = case.buf.nbytes
-    need = args.steps + args.warmup
-    nbuf = int(max(1, min(need, (args.buffer_budget_gb * 2**30) // nbytes)))
-    log(f"{nbuf} device copies of {nbytes / 2**20:.1f} MiB ({nbytes} bytes each)")
+    need = steps + warmup
+    nbuf = int(max(1, min(need, (budget_gb * 2**30) // nbytes)))
+    log(f"{name}: {nbuf} device copies of {nbytes / 2**20:.1f} MiB")
     base = torch.from_numpy(case.buf).to(dev)
     ring = [base.clone() for _ in range(nbuf)]
     starts = None if case.starts is None else torch.from_numpy(case.starts).to(dev)
     ends = torch.from_numpy(case.ends).to(dev)
     cs = sh.col_stride
     views = [b[:, ::cs] for b in ring]
-
     ctx = binding.Context(sh.rows, sh.width, sh.block_size, sh.k_blocks, sh.k_tokens,
                           row_stride=sh.row_stride, col_stride=cs,
                           starts_repeat=sh.starts_repeat, ends_repeat=sh.ends_repeat)
@@ -142,16 +114,13 @@ def main() -> int:
         for i in idx:
             ring[i % nbuf].copy_(base)
 
-    log("warmup")
-    for i in range(args.warmup):
+    for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-    restore(range(args.warmup))
+    restore(range(warmup))
     torch.cuda.synchronize()
 
-    steps = args.steps
-    first = args.warmup
-    use_graph = not args.no_graph
+    first = warmup
     graph = None
     if use_graph:
         try:
@@ -167,7 +136,8 @@ def main() -> int:
             restore(range(first, first + steps))
             torch.cuda.synchronize()
 
-    log(f"timed region: {steps} steps ({'graph replay' if use_graph else 'eager'})")
+    log(f"{name}: timed region, {steps} steps ({'graph replay' if use_graph else 'eager'})")
+    # HIP events on the launch stream bracket the timed region.
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -182,9 +152,12 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     region_ms = ev0.elapsed_time(ev1)
-    log(f"timed region {region_ms:.3f} ms (wall {wall * 1e3:.3f} ms)")
+    status = ctx.read_status()
+    if status != 0:
+        raise RuntimeError(f"{name}: context status {status:#x} after the timed region")
+    log(f"{name}: timed region {region_ms:.3f} ms (wall {wall * 1e3:.3f} ms)")
 
-    # Per-call kernel time: HIP events around each call on the launch stream.
+    # Eager calls with events around each (context only: includes launch gaps).
     restore(range(first, first + steps))
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -195,60 +168,125 @@ def main() -> int:
         evs[i][1].record(stream)
     torch.cuda.synchronize()
     durs = np.array([a.elapsed_time(b) for a, b in evs])   # ms
-    call_ms = float(np.mean(durs))
 
-    alg = metrics.fused_bytes(case.starts, case.ends, sh.rows, sh.width, sh.block_size,
-                              sh.k_blocks, sh.k_tokens, sh.starts_repeat, sh.ends_repeat,
-                              write_mask=write_mask)
-    per_call = alg["total_bytes"]
+    args_b = (case.starts, case.ends, sh.rows, sh.width, sh.block_size, sh.k_blocks,
+              sh.k_tokens, sh.starts_repeat, sh.ends_repeat)
+    plain = metrics.plain_bytes(*args_b, write_mask=write_mask)
+    needed = metrics.fused_bytes(*args_b, write_mask=write_mask)
     ms_per_step = region_ms / steps
-    value = sh.rows * steps / (region_ms * 1e-3)
-    live_gbps = per_call / (ms_per_step * 1e-3) / 1e9
-    achieved = per_call / (call_ms * 1e-3) / 1e9
+    per_call = plain["total_bytes"]
+    achieved = per_call / (ms_per_step * 1e-3) / 1e9
     sha = metrics.source_sha()
-    traffic = measured_traffic(args.workload, sha)
+    out = dict(
+        workload=name, ms_per_step=ms_per_step, rows_per_s=sh.rows * steps / (region_ms * 1e-3),
+        config={
+            "workload": name, "rows": sh.rows, "width": sh.width,
+            "block_size": sh.block_size, "k_blocks": sh.k_blocks, "k_tokens": sh.k_tokens,
+            "col_stride": cs, "starts_repeat": sh.starts_repeat, "ends_repeat": sh.ends_repeat,
+            "write_mask": write_mask, "graph": use_graph, "distinct_buffers": nbuf,
+            "grid_groups": info.grid_groups, "threads_per_group": info.threads_per_group,
+            "launches_per_call": info.fused_launches,
+        },
+        alg_bytes_per_call=per_call, alg_bytes_breakdown=plain,
+        needed_bytes_per_call=needed["total_bytes"],
+        eager_call_ms_mean=float(np.mean(durs)),
+        eager_call_ms_p10_p90=[float(np.percentile(durs, 10)), float(np.percentile(durs, 90))],
+        roofline={
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": measured_traffic(name, sha) if width is None else None,
+            "basis": "4*L read + -inf stores + index stores + 8 B bounds per row, per call, "
+                     "over the graph replay's time per call (HIP events on the launch stream)",
+        },
+        source_sha=sha, buffer_bytes=nbytes, case=case,
+    )
+    ctx.close()
+    del ring, views, base
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="short_decode",
+                    choices=["tiny", "short_decode", "mtp_ragged", "long_decode", "prefill_chunk"])
+    ap.add_argument("--width", type=int, default=None,
+                    help="override the buffer width (same bounds and live values)")
+    ap.add_argument("--no-graph", action="store_true", help="time eager calls instead")
+    ap.add_argument("--no-mask", action="store_true", help="do not write the mask")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="do not also time the long-decode workload")
+    ap.add_argument("--buffer-budget-gb", type=float, default=48.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the selection has no multi-GPU path here.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from sparse_attention_indexer_start_amd import binding
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    binding.load()
+    write_mask = not args.no_mask
+    use_graph = not args.no_graph
+
+    main_run = run_workload(args.workload, args.steps, args.warmup, write_mask, use_graph,
+                            args.buffer_budget_gb, args.width)
+    second = None
+    if not args.no_secondary and args.workload != "long_decode" and args.width is None:
+        second = run_workload("long_decode", args.steps, args.warmup, write_mask, use_graph,
+                              args.buffer_budget_gb)
+        second.pop("case")
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"cpu baseline (oracle, ~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(case, args.cpu_seconds)
+        log(f"cpu baseline (C oracle, ~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(main_run["case"], args.cpu_seconds)
+    main_run.pop("case")
 
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": main_run["rows_per_s"],
         "unit": "rows/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": main_run["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {
-            "workload": args.workload, "rows": sh.rows, "width": sh.width,
-            "block_size": sh.block_size, "k_blocks": sh.k_blocks, "k_tokens": sh.k_tokens,
-            "col_stride": cs, "write_mask": write_mask, "graph": use_graph,
-            "distinct_buffers": nbuf, "programs_per_row": info.programs_per_row,
-            "threads_per_group": info.threads_per_group,
-            "launches_per_call": info.fused_launches,
-        },
-        "live_bytes_per_step": per_call,
-        "live_GBps": live_gbps,
-        "pct_of_hbm_peak": 100.0 * live_gbps / HBM_PEAK_GBPS,
-        "kernel_ms_per_call": call_ms,
-        "kernel_ms_p10_p90": [float(np.percentile(durs, 10)), float(np.percentile(durs, 90))],
-        "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-        },
+        "config": main_run["config"],
+        "live_bytes_per_step": main_run["alg_bytes_per_call"],
+        "live_GBps": main_run["roofline"]["achieved"],
+        "pct_of_hbm_peak": 100.0 * main_run["roofline"]["frac"],
+        "alg_bytes_breakdown": main_run["alg_bytes_breakdown"],
+        "needed_bytes_per_call": main_run["needed_bytes_per_call"],
+        "eager_call_ms_mean": main_run["eager_call_ms_mean"],
+        "eager_call_ms_p10_p90": main_run["eager_call_ms_p10_p90"],
+        "roofline": main_run["roofline"],
         "cpu_baseline": cpu,
-        "source_sha": sha,
-        "buffer_bytes": nbytes,
+        "source_sha": main_run["source_sha"],
+        "buffer_bytes": main_run["buffer_bytes"],
     }
+    if second is not None:
+        out["long_decode"] = {k: second[k] for k in (
+            "ms_per_step", "rows_per_s", "alg_bytes_per_call", "needed_bytes_per_call",
+            "eager_call_ms_mean", "roofline", "config")}
     print(json.dumps(out), flush=True)
-    ctx.close()
     return 0
 
 

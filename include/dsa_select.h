@@ -94,10 +94,16 @@ typedef struct dsa_launch_info {
 } dsa_launch_info;
 
 /*
- * dsa_select_init -- validate the shape, choose the launch geometry from the
- * shape and the device's CU count only, allocate and zero the workspace on
- * `device` (so call it outside stream capture).  On success *out owns the
- * workspace until dsa_select_destroy.
+ * dsa_select_init -- [P1] Summary (the launch shape is derived from the
+ * tensor shapes alone and stays fixed for graph replay while the work follows
+ * each row's [start, end)); [P4] implementation (a fixed grid keeps graph
+ * capture valid).  Validates the shape, chooses the launch geometry from the
+ * shape and the device's CU count only, and allocates and zeroes the
+ * workspace on `device` (so call it outside stream capture).  On success *out
+ * owns the workspace until dsa_select_destroy.  Errors: DSA_ERR_INVALID_ARG
+ * for a null pointer or a bad size, stride or repeat; DSA_ERR_UNSUPPORTED
+ * for width >= 2^31 or k_blocks + k_tokens > 131072; DSA_ERR_HIP when the
+ * allocation fails (nothing is then left allocated and *out is NULL).
  */
 int dsa_select_init(const dsa_shape* shape, int device, dsa_ctx** out);
 
@@ -148,7 +154,11 @@ int dsa_candidate_mask(dsa_ctx* ctx, float* logits, const int32_t* starts,
                        hipStream_t stream);
 
 /*
- * dsa_select_fused -- the whole chain in one pass over the live logits:
+ * dsa_select_fused -- [P1] Summary (select_candidate_blocks scores the blocks
+ * of the row's range with the newest-block pin and feeds apply_candidate_mask;
+ * the row top-k bounds its scan by the same ends); [P4] implementation and
+ * key source (the mask strided over [start, end), flags from the candidate
+ * blocks).  The whole chain in one pass over the live logits:
  * block scores (with the pin) -> top-k_blocks blocks -> mask -> top-k_tokens
  * tokens of the masked row.  Outputs equal those of dsa_block_scores,
  * dsa_topk(BLOCKS), dsa_candidate_mask, dsa_topk(TOKENS) run in that order:
@@ -168,9 +178,13 @@ int dsa_select_fused(dsa_ctx* ctx, float* logits, const int32_t* starts,
  * dsa_read_status -- copy the context's device status word to *out after
  * synchronizing the context's device.  Bit 0: a row had start < 0 (treated as
  * empty).  Bit 1: a second-pass wait gave up after its time limit (the row's
- * outputs are then incomplete).  Bit 2: a fused call found its workspace inconsistent, which only a
- * call cut short can leave behind (dsa_reset_workspace clears it).  0 means no
- * contract violation since init or the last reset.
+ * outputs are then incomplete).  Bit 2: a fused call found its workspace
+ * inconsistent, which only a call cut short can leave behind.  0 means no
+ * contract violation since init or the last reset.  The calls return before
+ * the device runs, so this word is how a fused call reports a given-up wait:
+ * after bit 1 or bit 2 the workspace may hold a partial row state, and the
+ * caller must call dsa_reset_workspace before the next call on the context
+ * (bit 0 alone needs no reset).
  */
 int dsa_read_status(dsa_ctx* ctx, uint32_t* out);
 

@@ -742,12 +742,16 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
   } else {
     float* sc = p.scores ? p.scores + (int64_t)r * p.nblocks : nullptr;
     uint32_t* keys = sm.keys();
-    // The select's histogram starts from zero; cleared while the loads fly.
-    for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
     bool low = false;
     // When a select follows, each key's top digit is counted as it is scored
-    // (the select's first histogram), and the barrier below completes it.
+    // (the select's first histogram), and the barrier after the scores
+    // completes it.  The histogram is cleared first, behind a barrier of its
+    // own: a lane's count may land before another wave's clear otherwise.
     const bool do_select = nlb > Kp;
+    if (do_select) {
+      for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
+      __syncthreads();
+    }
     score_blocks<BS>(rowp, p.col_stride, B, L, 0, nlb, nlb, vec, [&](int b, uint32_t k) {
       keys[b] = k;
       if (sc) sc[b] = key2f(k);
@@ -762,8 +766,10 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
     uint32_t* nonkept = sm.tkey;
     wg_rule_emit<NT>(nlb, T, q, getk, [&](int i, uint32_t rank, bool kept) {
       if (kept) {
-        bout[rank] = i;
-        sel[rank] = (uint32_t)i;
+        if (rank < (uint32_t)Kp) {   // (always, for an exact histogram)
+          bout[rank] = i;
+          sel[rank] = (uint32_t)i;
+        }
       } else {
         const uint32_t nk = (uint32_t)i - rank;
         if (nk < (uint32_t)TK_CAP) nonkept[nk] = (uint32_t)i;
@@ -960,8 +966,10 @@ DSA_DEV void final_row_general(const Params& p, int r, const Row& rb, Smem& sm) 
     wg_rule_emit<NT>((int)n_list, T, q, getk, [&](int i, uint32_t rank, bool kept) {
       const uint32_t b = lids[i];
       if (kept) {
-        bout[rank] = (int32_t)b;
-        sel[rank] = b;
+        if (rank < (uint32_t)Kp) {
+          bout[rank] = (int32_t)b;
+          sel[rank] = b;
+        }
       } else if (write_mask) {
         mask_block_lane<BS>(rowp, cs, B, rb.L, vec, b);
       }
@@ -991,8 +999,10 @@ DSA_DEV void final_row_general(const Params& p, int r, const Row& rb, Smem& sm) 
         [&](int i, uint32_t rank, bool kept, uint64_t, int) {
           const uint32_t b = ld_shared(&lid[i]);
           if (kept) {
-            bout[rank] = (int32_t)b;
-            sel[rank] = b;
+            if (rank < (uint32_t)Kp) {
+              bout[rank] = (int32_t)b;
+              sel[rank] = b;
+            }
           } else if (write_mask) {
             mask_one_block(rowp, cs, B, rb.L, b);
           }
@@ -1202,7 +1212,7 @@ DSA_DEV void final_row(const Params& p, int r, const Row& rb, Smem& sm) {
     wg_rule_emit<NT>((int)n_list, T, q, getk, [&](int i, uint32_t rank, bool kept) {
       const uint32_t b = lids[i];
       if (kept) {
-        bout[rank] = (int32_t)b;
+        if (rank < (uint32_t)Kp) bout[rank] = (int32_t)b;
         atomicOr(&sm.hist[b >> 5], 1u << (b & 31));    // kept-block bitmap
       } else if (wm) {
         mask_block_lane<BS>(rowp, p.col_stride, BS, rb.L, vec, b);

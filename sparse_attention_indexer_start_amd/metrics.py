@@ -14,6 +14,10 @@ Per row with live length L, nlb = ceil(L / B) live blocks:
 
 Workspace traffic (block keys, histograms, lists) is an intermediate and is not
 counted.
+
+``plain_bytes`` is the simpler count that charges the ``4 * L`` read on every
+non-empty row and 8 bytes of bounds per row, whether or not the values can
+change the result.  It is the figure the roofline fraction is quoted on.
 """
 from __future__ import annotations
 
@@ -61,3 +65,18 @@ def fused_bytes(starts, ends, rows: int, width: int, block_size: int, k_blocks: 
     total = reads + mask + idx + sc + bounds
     return dict(read_bytes=reads + bounds, mask_bytes=mask, index_bytes=idx,
                 score_bytes=sc, total_bytes=total, live_columns=int(L.sum()))
+
+
+def plain_bytes(starts, ends, rows: int, width: int, block_size: int, k_blocks: int,
+                k_tokens: int, starts_repeat: int = 1, ends_repeat: int = 1,
+                write_mask: bool = True) -> dict:
+    """Per call: 4*L read on every row, 4*B*max(nlb - K_blk, 0) of -inf,
+    4*(K_blk + K_tok) of indices with pads, and 8 bytes of bounds per row."""
+    L = row_lengths(starts, ends, rows, width, starts_repeat, ends_repeat)
+    nlb = -(-L // block_size)
+    reads = int((4 * L).sum())
+    mask = int((4 * block_size * np.maximum(nlb - k_blocks, 0)).sum()) if write_mask else 0
+    idx = rows * 4 * (k_blocks + k_tokens)
+    bounds = rows * 8
+    return dict(read_bytes=reads, mask_bytes=mask, index_bytes=idx, bounds_bytes=bounds,
+                total_bytes=reads + mask + idx + bounds, live_columns=int(L.sum()))

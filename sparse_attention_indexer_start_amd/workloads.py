@@ -251,8 +251,14 @@ def config_bounds(name: str, seed_offset: int = 0):
     raise KeyError(name)
 
 
-def make_config(name: str, seed_offset: int = 0, rows_to_fill=None) -> Case:
+def make_config(name: str, seed_offset: int = 0, rows_to_fill=None,
+                width: Optional[int] = None) -> Case:
+    """A named workload; ``width`` overrides the buffer width and keeps the
+    bounds and live values (each row's values depend only on the seed, the
+    row and its live range)."""
     sh, starts, ends, seed = config_bounds(name, seed_offset)
+    if width is not None:
+        sh = dataclasses.replace(sh, width=int(width))
     return build_case(name, sh, starts, ends, seed, cfg=CONFIG_IDS[name],
                       rows_to_fill=rows_to_fill, **CONFIG_EXTRAS[name])
 

@@ -3,10 +3,12 @@ library through its binding, and compare with the oracle row by row."""
 from __future__ import annotations
 
 import sys
+import time
 
 import numpy as np
 
 import oracle
+from oracle import c_oracle
 from sparse_attention_indexer_start_amd import binding
 from sparse_attention_indexer_start_amd import workloads as wl
 
@@ -62,9 +64,16 @@ class DevCase:
                          scores if with_scores else None, write_mask,
                          two_launches=two_launches)
         torch.cuda.synchronize()
+        assert_status_clean(ctx)
         if own:
             ctx.close()
-        return bids, tids, scores
+        return bids, tids, (scores if with_scores else None)
+
+
+def assert_status_clean(ctx):
+    """No contract violation, no given-up wait and no stale workspace so far."""
+    st = ctx.read_status()
+    assert st == 0, f"context status word {st:#x} after a fused call"
 
 
 def oracle_row(case: wl.Case, r: int):
@@ -114,6 +123,46 @@ def check_rows_against_oracle(dc: DevCase, rows, bids, tids, scores, masked=True
         got_row = row_bits(dc.buf[r])
         diff = np.nonzero(got_row != want_row.view(np.uint32))[0]
         assert diff.size == 0, f"row {r} buffer differs at underlying columns {diff[:8]}"
+
+
+def row_live_lengths(case: wl.Case):
+    sh = case.shape
+    out = np.zeros((sh.rows, 3), np.int64)
+    for r in range(sh.rows):
+        out[r] = oracle.row_bounds(r, case.starts, case.ends, sh.width, sh.starts_repeat,
+                                   sh.ends_repeat)
+    return out
+
+
+def check_all_rows_c(dc: DevCase, bids, tids, scores=None, write_mask=True):
+    """Every row against the C oracle, bit for bit: block ids, token ids,
+    scores (when given; and nothing written past nlb) and the whole underlying
+    buffer (live span, head, tail, interleaved elements)."""
+    case, sh = dc.case, dc.sh
+    t0 = time.perf_counter()
+    wb, wt, ws, wm = c_oracle.select_case(case, write_mask=write_mask,
+                                          with_scores=scores is not None)
+    log(f"  C oracle over {sh.rows} rows: {time.perf_counter() - t0:.2f} s "
+        f"({c_oracle.default_threads()} threads)")
+    gb = bids.cpu().numpy()
+    gt = tids.cpu().numpy()
+    bad = np.nonzero((gb != wb).any(1))[0]
+    assert bad.size == 0, f"block ids differ on {bad.size} rows, first {bad[:8]}"
+    bad = np.nonzero((gt != wt).any(1))[0]
+    assert bad.size == 0, f"token ids differ on {bad.size} rows, first {bad[:8]}"
+    if scores is not None:
+        lens = row_live_lengths(case)[:, 2]
+        nlb = -(-lens // sh.block_size)
+        written = np.arange(sh.nblocks)[None, :] < nlb[:, None]
+        want = np.where(written, ws.view(np.uint32), np.uint32(SCORE_FILL_BITS))
+        got = scores.cpu().numpy().view(np.uint32)
+        bad = np.nonzero((got != want).any(1))[0]
+        assert bad.size == 0, f"scores differ on {bad.size} rows, first {bad[:8]}"
+    got_buf = dc.buf.cpu().numpy().view(np.uint32)
+    want_buf = (wm if write_mask else case.buf).view(np.uint32)
+    bad = np.nonzero((got_buf != want_buf).any(1))[0]
+    assert bad.size == 0, f"buffer differs on {bad.size} rows, first {bad[:8]}"
+    log(f"  all {sh.rows} rows bit-exact against the C oracle")
 
 
 def check_whole_buffer(dc: DevCase, write_mask=True, chunk_rows=256):

@@ -2,9 +2,11 @@
 
 Every comparison is bit-exact: indices, scores and the masked buffer
 (including the tail past end, the head before start and the interleaved
-elements of a strided view).  Small cases are compared row by row in full;
-the full-size workloads are compared on sampled rows with the oracle and on
-every row through properties checked on the device.
+elements of a strided view).  Every row of every case, the full-size
+workloads included, is compared with the C oracle (threshold selection, all
+host cores); small cases and sampled rows of the full-size workloads are
+also compared with the numpy oracle (full sort), and every fused call must
+leave the context's status word at zero.
 """
 import numpy as np
 import pytest
@@ -29,6 +31,7 @@ def _device():
 
 def _full_check(dc, bids, tids, scores, write_mask=True):
     gh.check_rows_against_oracle(dc, range(dc.sh.rows), bids, tids, scores, masked=write_mask)
+    gh.check_all_rows_c(dc, bids, tids, scores, write_mask)
     gh.check_whole_buffer(dc, write_mask)
     gh.check_invariants_all_rows(dc, bids, tids)
 
@@ -192,6 +195,82 @@ def test_fused_repeatable():
     ctx.close()
 
 
+@pytest.mark.parametrize("name", ["long_rows", "short_rows"])
+def test_graph_replays_bit_identical(name):
+    """One captured fused call replayed 100 times, the buffer restored by
+    eager copies between replays: every replay equals the first, which equals
+    the C oracle, and the status word stays zero."""
+    import torch
+    if name == "long_rows":
+        case = wl.make_custom(4, 300000, 8, 2048, 2048, [300000, 299999, 150001, 65537],
+                              seed=17, dup_frac=0.02, outlier_frac=0.01)
+    else:
+        case = wl.make_custom(6, 20000, 8, 256, 2048, [20000, 8192, 4000, 2049, 300, 1],
+                              seed=18, dup_frac=0.02)
+    dc = gh.DevCase(case)
+    ctx = dc.context()
+    bids, tids, scores = dc.outputs()
+    ctx.select_fused(dc.logits, dc.starts, dc.ends, bids, tids, scores, True)
+    torch.cuda.synchronize()
+    dc.restore()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ctx.select_fused(dc.logits, dc.starts, dc.ends, bids, tids, scores, True)
+    torch.cuda.synchronize()
+    ref = None
+    for i in range(100):
+        dc.restore()
+        bids.fill_(-7)
+        tids.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (bids.cpu().numpy(), tids.cpu().numpy(), scores.cpu().numpy().view(np.uint32),
+               dc.buf.cpu().numpy().view(np.uint32))
+        if ref is None:
+            ref = got
+            gh.check_all_rows_c(dc, bids, tids, scores)
+        else:
+            for a, b in zip(ref, got):
+                assert np.array_equal(a, b), f"replay {i} differs from the first"
+    gh.assert_status_clean(ctx)
+    ctx.close()
+
+
+def test_width_independence_short_decode():
+    """The short-decode rows at widths 8192 and 1,048,576: same outputs (and
+    both equal the C oracle); the kernel time is logged for both."""
+    import torch
+    outs = {}
+    for W in (8192, 1048576):
+        case = wl.make_config("short_decode", width=W)
+        dc = gh.DevCase(case)
+        ctx = dc.context()
+        bids, tids, _ = dc.run_fused(ctx, with_scores=False)
+        gh.check_all_rows_c(dc, bids, tids, None)
+        outs[W] = (bids.cpu().numpy(), tids.cpu().numpy(),
+                   dc.buf[:, :8192].cpu().numpy().view(np.uint32))
+        # time 20 calls on restored copies (HIP events on the launch stream)
+        copies = [dc.pristine.clone() for _ in range(20)]
+        stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for c in copies:
+            ctx.select_fused(c, dc.starts, dc.ends, bids, tids, None, True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        gh.assert_status_clean(ctx)
+        gh.log(f"width {W}: {e0.elapsed_time(e1) / 20 * 1e3:.2f} us per eager call, "
+               f"grid {ctx.info().grid_groups} workgroups")
+        ctx.close()
+        del copies, dc
+    a, b = outs[8192], outs[1048576]
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
 # ---------------------------------------------------------------------------
 # The four steps one by one
 # ---------------------------------------------------------------------------
@@ -325,6 +404,7 @@ def test_graph_replay_tracks_changing_ends():
             dcv.case, dcv.sh, dcv.buf, dcv.pristine = case, case.shape, dc.buf, dc.pristine
             dcv.starts, dcv.ends = None, dc.ends
             _full_check(dcv, bids, tids, scores)
+            gh.assert_status_clean(ctx)
     ctx.close()
 
 
@@ -394,23 +474,29 @@ def _sample_rows(case, n_random=6, seed=0):
     ("short_decode", False), ("mtp_ragged", False), ("mtp_ragged", True),
     ("long_decode", False), ("long_decode", True), ("prefill_chunk", False)])
 def test_full_size_workload(name, two):
+    """Every row of the workload, as the bench runs it (no scores) and with
+    scores, against the C oracle; sampled rows against the numpy oracle."""
     gh.log(f"workload {name}: generating")
     case = wl.make_config(name)
     dc = gh.DevCase(case)
-    gh.log(f"workload {name}: running (two_launches={two})")
-    bids, tids, scores = dc.run_fused(two_launches=two)
-    gh.log(f"workload {name}: whole-buffer checks")
+    gh.log(f"workload {name}: running (two_launches={two}, no scores)")
+    bids, tids, _ = dc.run_fused(two_launches=two, with_scores=False)
+    gh.check_all_rows_c(dc, bids, tids, None)
     gh.check_whole_buffer(dc)
-    gh.check_invariants_all_rows(dc, bids, tids)
     rows = _sample_rows(case, n_random=8 if name != "long_decode" else 4)
     if name == "mtp_ragged":
         rows = sorted(set(rows) | set(range(16)))   # the edge requests 1023/1024/1025/width
-    gh.log(f"workload {name}: oracle rows {rows}")
-    gh.check_rows_against_oracle(dc, rows, bids, tids, scores)
+    gh.log(f"workload {name}: numpy oracle rows {rows}")
+    gh.check_rows_against_oracle(dc, rows, bids, tids, None)
+    dc.restore()
+    gh.log(f"workload {name}: running with scores")
+    bids, tids, scores = dc.run_fused(two_launches=two, with_scores=True)
+    gh.check_all_rows_c(dc, bids, tids, scores)
 
 
 def test_prefill_graph_replay_new_ends():
-    """Prefill-chunk shape: capture once, replay with the +100/+200 end sets."""
+    """Prefill-chunk shape: capture once, replay with the +100/+200 end sets;
+    every row of every replay against the C oracle."""
     import torch
     base = wl.make_config("prefill_chunk")
     dc = gh.DevCase(base)
@@ -432,8 +518,9 @@ def test_prefill_graph_replay_new_ends():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
+        gh.assert_status_clean(ctx)
         dc.case = case
+        gh.check_all_rows_c(dc, bids, tids, scores)
         gh.check_whole_buffer(dc)
-        gh.check_invariants_all_rows(dc, bids, tids)
         gh.check_rows_against_oracle(dc, _sample_rows(case, 6, seed=off), bids, tids, scores)
     ctx.close()
