@@ -175,6 +175,28 @@ int dsa_select_fused(dsa_ctx* ctx, float* logits, const int32_t* starts,
                      float* scores, uint32_t flags, hipStream_t stream);
 
 /*
+ * dsa_select_fused_noalloc -- for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): dsa_select_fused for `shape` on `device` without a context.
+ * Same arguments, outputs and flags as dsa_select_fused; the workspace is a
+ * library-owned array of 256 MiB per device (held from the first call on that
+ * device until the process ends), and the call allocates nothing.  A shape
+ * whose workspace would exceed 256 MiB is rejected with DSA_ERR_UNSUPPORTED
+ * before anything is launched (dsa_select_query on a context of the shape
+ * reports its workspace_bytes).  Each call first clears, on `stream`, the
+ * workspace words that must start at zero, then launches the fused kernel.
+ * status: nullable device pointer to one uint32 that the caller zeroes; the
+ * kernels OR into it the bits described under dsa_read_status (NULL: not
+ * reported).  Every call on one device shares that device's array: calls
+ * that overlap in time on one device (on different streams, or from several
+ * threads) race and give undefined results; order them on one stream.
+ */
+int dsa_select_fused_noalloc(const dsa_shape* shape, int device, float* logits,
+                             const int32_t* starts, const int32_t* ends,
+                             int32_t* block_ids, int32_t* token_ids, float* scores,
+                             uint32_t flags, uint32_t* status, hipStream_t stream);
+
+/*
  * dsa_read_status -- copy the context's device status word to *out after
  * synchronizing the context's device.  Bit 0: a row had start < 0 (treated as
  * empty).  Bit 1: a second-pass wait gave up after its time limit (the row's

@@ -29,7 +29,7 @@ STATUS_NAMES = {
 EXPORTED = (
     "dsa_select_init", "dsa_select_destroy", "dsa_select_query", "dsa_block_scores",
     "dsa_topk", "dsa_candidate_mask", "dsa_select_fused", "dsa_read_status",
-    "dsa_reset_workspace", "dsa_last_error",
+    "dsa_reset_workspace", "dsa_last_error", "dsa_select_fused_noalloc",
 )
 
 
@@ -86,6 +86,8 @@ def load() -> ctypes.CDLL:
         lib.dsa_select_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, u32, vp]
         lib.dsa_read_status.argtypes = [vp, ctypes.POINTER(u32)]
         lib.dsa_reset_workspace.argtypes = [vp, vp]
+        lib.dsa_select_fused_noalloc.argtypes = [ctypes.POINTER(Shape), i32, vp, vp, vp, vp,
+                                                 vp, vp, u32, vp, vp]
         lib.dsa_last_error.restype = ctypes.c_char_p
         for name in EXPORTED:
             if name != "dsa_last_error":
@@ -268,3 +270,40 @@ def select(logits, starts, ends, block_size: int, k_blocks: int, k_tokens: int,
     torch.cuda.current_stream(logits.device).synchronize()
     ctx.close()
     return (bids, tids, sc) if return_scores else (bids, tids)
+
+
+def select_fused_noalloc(logits, starts, ends, block_ids, token_ids, block_size: int,
+                         k_blocks: int, k_tokens: int, scores=None, write_mask: bool = True,
+                         starts_repeat: int = 1, ends_repeat: int = 1, status=None,
+                         two_launches: bool = False, stream=None) -> None:
+    """The allocation-free fused call (no context): the library's per-device
+    scratch array is its workspace.  ``status`` is an optional int32 device
+    tensor of one element, zeroed by the caller, into which status bits are
+    ORed."""
+    import torch
+    rows, width = logits.shape
+    if logits.dtype != torch.float32 or not logits.is_cuda:
+        raise ValueError("logits must be a float32 device tensor")
+    for t, name, shp in ((block_ids, "block_ids", (rows, k_blocks)),
+                         (token_ids, "token_ids", (rows, k_tokens))):
+        if t.dtype != torch.int32 or not t.is_contiguous() or tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be contiguous int32 {shp}")
+    for t, name in ((starts, "starts"), (ends, "ends"), (status, "status")):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    nblocks = -(-width // block_size) if width else 0
+    if scores is not None and (scores.dtype != torch.float32 or not scores.is_contiguous()
+                               or tuple(scores.shape) != (rows, nblocks)):
+        raise ValueError("scores must be contiguous float32 [rows, nblocks]")
+    col_stride = logits.stride(1) if width > 1 else 1
+    row_stride = logits.stride(0) if rows > 1 else max(1, width * col_stride)
+    shape = Shape(rows, block_size, k_blocks, k_tokens, width, row_stride, col_stride,
+                  starts_repeat, ends_repeat)
+    dev = logits.device.index or 0
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    flags = (DSA_WRITE_MASK if write_mask else 0) | (DSA_TWO_LAUNCHES if two_launches else 0)
+    _check(load().dsa_select_fused_noalloc(ctypes.byref(shape), dev, _ptr(logits), _ptr(starts),
+                                           _ptr(ends), _ptr(block_ids), _ptr(token_ids),
+                                           _ptr(scores), flags, _ptr(status),
+                                           ctypes.c_void_p(stream.cuda_stream)))

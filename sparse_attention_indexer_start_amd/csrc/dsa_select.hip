@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <type_traits>
@@ -34,7 +35,21 @@ __global__ __launch_bounds__(NT) void k_topk_blocks(Params p) {
   for (int i = Kp + threadIdx.x; i < p.k_blocks; i += NT) out[i] = -1;
 }
 
+// Zeroes n32 words at p (vector stores; n32 a multiple of 4, p 16-byte aligned).
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* p, int64_t n32) {
+  uint4* q = reinterpret_cast<uint4*>(p);
+  const int64_t n4 = n32 / 4;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256)
+    q[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 }  // namespace dsa
+
+// Workspace of dsa_select_fused_noalloc: one copy per device, held until the
+// process ends.  In host code this name is only a handle; its device address
+// comes from hipGetSymbolAddress, once per device.
+static constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)256 << 20;
+static __device__ __align__(256) uint32_t scratch[NOALLOC_SCRATCH_BYTES / 4];
 
 // ===========================================================================
 // Host side: the C ABI.
@@ -60,6 +75,16 @@ namespace {
 
 constexpr uint32_t CTX_MAGIC = 0x44534131u;
 thread_local std::string g_err;
+
+// Per-device state of the allocation-free entry point.
+constexpr int NOALLOC_MAX_DEVICES = 64;
+struct NoallocDevice {
+  bool ready;
+  int cus;
+  uint32_t* ptr;   // this device's copy of `scratch`
+};
+NoallocDevice g_noalloc[NOALLOC_MAX_DEVICES];
+std::mutex g_noalloc_mutex;
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -168,15 +193,7 @@ int launch_check(const char* what) {
   return DSA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* dsa_last_error(void) { return g_err.c_str(); }
-
-int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
-  if (out == nullptr) return fail(DSA_ERR_INVALID_ARG, "out is null");
-  *out = nullptr;
+int validate_shape(const dsa_shape* s, int device) {
   if (s == nullptr) return fail(DSA_ERR_INVALID_ARG, "shape is null");
   if (s->rows < 0 || s->width < 0) return fail(DSA_ERR_INVALID_ARG, "rows and width must be >= 0");
   if (s->width >= (int64_t)1 << 31) return fail(DSA_ERR_UNSUPPORTED, "width must be < 2^31");
@@ -190,82 +207,168 @@ int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
   if ((int64_t)s->k_blocks + s->k_tokens > BITMAP_BITS)
     return fail(DSA_ERR_UNSUPPORTED, "k_blocks + k_tokens must be <= %d", BITMAP_BITS);
   if (device < 0) return fail(DSA_ERR_INVALID_ARG, "device must be >= 0");
+  return DSA_OK;
+}
 
-  dsa_ctx* c = new (std::nothrow) dsa_ctx;
-  if (!c) return fail(DSA_ERR_HIP, "host allocation failed");
+// Workspace slots, in layout order.  The first three are the words that must
+// be zero when a call starts (the status word, the row states and the digit
+// histograms); the others are written before they are read.
+enum Slot { S_STATUS, S_ROW, S_HIST, S_KEY, S_LIST, S_FLAT, S_CNT, S_SEL, S_DBLK, S_TKEY,
+            S_TCOL, S_CAND, S_CCNT, N_SLOTS };
+constexpr int N_ZERO_SLOTS = 3;
+
+int64_t slot_words(int64_t w) { return (w + 63) / 64 * 64; }
+
+// Launch geometry and workspace sizes of a shape on a device with `cus` CUs
+// (no device call); words[i] = the size of slot i in 32-bit words.
+int plan_ctx(const dsa_shape* s, int device, int cus, dsa_ctx* c, int64_t* words) {
   std::memset(c, 0, sizeof(*c));
   c->sh = *s;
   c->device = device;
   c->magic = CTX_MAGIC;
+  c->cus = cus;
   const int64_t nb = s->width > 0 ? (s->width + s->block_size - 1) / s->block_size : 0;
   c->nblocks = (int32_t)nb;
   c->small_blocks = LIST_CAP;
+  // Workgroups per row: about two per CU in all (one resident round at two
+  // workgroups per CU), no more than one per 256 blocks of the buffer, and
+  // at most NT.
+  const int64_t target = (int64_t)cus * 2;
+  int64_t P = s->rows > 0 ? (target + s->rows - 1) / s->rows : 1;
+  const int64_t pmax = std::max<int64_t>(1, (nb + 255) / 256);
+  P = std::max<int64_t>(1, std::min<int64_t>({P, pmax, (int64_t)NT}));
+  c->P = (int32_t)P;
+  const int64_t G = P * s->rows;
+  if (G > (int64_t)1 << 30) return fail(DSA_ERR_UNSUPPORTED, "too many rows");
+  c->G = (int32_t)G;
+  // Balanced split of long rows when one workgroup can scan every row's
+  // bounds (rows <= CUs and <= 256).  A pass has at most NQ + rows - 1 non-empty pieces
+  // (one per worker plus one per row boundary inside a worker's range);
+  // with the rows' owners that is one resident round at two workgroups per
+  // CU when NQ = 2 * CUs - rows + 1, less a reserve of slots for the rows'
+  // final workgroups, which run while the pass-2 pieces still store -inf.
+  const int64_t reserve = std::min<int64_t>(s->rows, 128);
+  c->NQ = (int32_t)std::max<int64_t>(
+      1, std::min<int64_t>((int64_t)cus * 2 - s->rows + 1 - reserve, NT));
+  c->balanced = (s->rows >= 1 && s->rows <= cus && s->rows <= 256) ? 1 : 0;
+  c->cnt_stride = std::max(c->P, c->NQ);
+  const int64_t F = (s->k_tokens + s->block_size - 1) / s->block_size;
+  // Token domain of a row: at most nlow + Kp <= 2*K_blk + F blocks (also
+  // with repeated ids given to the standalone token top-k).
+  c->dblk_cap = 2 * (int64_t)s->k_blocks + F + 1;
+  c->tkey_cap = c->dblk_cap * s->block_size;
+  for (int i = 0; i < N_SLOTS; ++i) words[i] = 0;
+  if (empty_shape(c)) return DSA_OK;
+  const bool long_rows = may_split(c);
+  const int64_t R = s->rows;
+  const int64_t n_key = long_rows ? R * nb : 0;
+  const int64_t n_cnt = long_rows ? R * c->cnt_stride : 0;
+  // Token candidates are gathered in pass 2 when the kept blocks hold more
+  // columns than the token top-k keeps (otherwise the closed form applies).
+  c->pregather = ((int64_t)s->k_blocks * s->block_size > s->k_tokens &&
+                  (s->block_size == 4 || s->block_size == 8 || s->block_size == 16)) ? 1 : 0;
+  const int64_t n_cand = long_rows && c->pregather ? 2 * R * nb : 0;
+  words[S_STATUS] = 64;
+  words[S_ROW] = R * ROW_STATE;
+  words[S_HIST] = long_rows ? R * HIST_WORDS : 0;
+  words[S_KEY] = n_key;
+  words[S_LIST] = 2 * n_key;
+  words[S_FLAT] = n_key;
+  words[S_CNT] = n_cnt;
+  words[S_SEL] = R * s->k_blocks;
+  words[S_DBLK] = R * c->dblk_cap;
+  words[S_TKEY] = R * c->tkey_cap;
+  words[S_TCOL] = R * c->tkey_cap;
+  words[S_CAND] = 2 * n_cand;
+  words[S_CCNT] = n_cnt;
+  int64_t total = 0;
+  for (int i = 0; i < N_SLOTS; ++i) total += slot_words(words[i]);
+  c->ws_bytes = (size_t)total * 4;
+  return DSA_OK;
+}
 
-  int rc = on_device(device, [&]() -> int {
-    hipDeviceProp_t prop;
-    hipError_t e = hipGetDeviceProperties(&prop, device);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
-    c->cus = prop.multiProcessorCount;
-    // Workgroups per row: about two per CU in all (one resident round at two
-    // workgroups per CU), no more than one per 256 blocks of the buffer, and
-    // at most NT.
-    const int64_t target = (int64_t)c->cus * 2;
-    int64_t P = s->rows > 0 ? (target + s->rows - 1) / s->rows : 1;
-    const int64_t pmax = std::max<int64_t>(1, (nb + 255) / 256);
-    P = std::max<int64_t>(1, std::min<int64_t>({P, pmax, (int64_t)NT}));
-    c->P = (int32_t)P;
-    const int64_t G = P * s->rows;
-    if (G > (int64_t)1 << 30) return fail(DSA_ERR_UNSUPPORTED, "too many rows");
-    c->G = (int32_t)G;
-    // Balanced split of long rows when one workgroup can scan every row's
-    // bounds (rows <= CUs and <= 256).  A pass has at most NQ + rows - 1 non-empty pieces
-    // (one per worker plus one per row boundary inside a worker's range);
-    // with the rows' owners that is one resident round at two workgroups per
-    // CU when NQ = 2 * CUs - rows + 1, less a reserve of slots for the rows'
-    // final workgroups, which run while the pass-2 pieces still store -inf.
-    const int64_t reserve = std::min<int64_t>(s->rows, 128);
-    c->NQ = (int32_t)std::max<int64_t>(
-        1, std::min<int64_t>((int64_t)c->cus * 2 - s->rows + 1 - reserve, NT));
-    c->balanced = (s->rows >= 1 && s->rows <= c->cus && s->rows <= 256) ? 1 : 0;
-    c->cnt_stride = std::max(c->P, c->NQ);
-    const int64_t F = (s->k_tokens + s->block_size - 1) / s->block_size;
-    // Token domain of a row: at most nlow + Kp <= 2*K_blk + F blocks (also
-    // with repeated ids given to the standalone token top-k).
-    c->dblk_cap = 2 * (int64_t)s->k_blocks + F + 1;
-    c->tkey_cap = c->dblk_cap * s->block_size;
-    if (empty_shape(c)) return DSA_OK;
-    const bool long_rows = may_split(c);
-    const int64_t R = s->rows;
-    const int64_t n_key = long_rows ? R * nb : 0;
-    const int64_t n_hist = long_rows ? R * HIST_WORDS : 0;
-    const int64_t n_cnt = long_rows ? R * c->cnt_stride : 0;
-    // Token candidates are gathered in pass 2 when the kept blocks hold more
-    // columns than the token top-k keeps (otherwise the closed form applies).
-    c->pregather = ((int64_t)s->k_blocks * s->block_size > s->k_tokens &&
-                    (s->block_size == 4 || s->block_size == 8 || s->block_size == 16)) ? 1 : 0;
-    const int64_t n_cand = long_rows && c->pregather ? 2 * R * nb : 0;
-    const int64_t words[] = {n_key, 2 * n_key, n_key, n_hist, n_cnt, R * ROW_STATE,
-                             R * s->k_blocks, R * c->dblk_cap, R * c->tkey_cap,
-                             R * c->tkey_cap, 2 * n_cand, n_cnt, 64};
-    int64_t total = 0;
-    for (int64_t w : words) total += (w + 63) / 64 * 64;
-    c->ws_bytes = (size_t)total * 4;
+// Points the context's slots into the workspace at `base` (256-byte aligned).
+void assign_slots(dsa_ctx* c, uint32_t* base, const int64_t* words) {
+  uint32_t** slots[N_SLOTS] = {&c->status, &c->ws_row, &c->ws_hist, &c->ws_key, &c->ws_list,
+                               &c->ws_flat, &c->ws_cnt, &c->ws_sel, &c->ws_dblk, &c->ws_tkey,
+                               &c->ws_tcol, &c->ws_cand, &c->ws_ccnt};
+  int64_t pos = 0;
+  for (int i = 0; i < N_SLOTS; ++i) {
+    *slots[i] = words[i] ? base + pos : nullptr;
+    pos += slot_words(words[i]);
+  }
+}
+
+// Words at the start of the workspace that must be zero when a call starts.
+int64_t zero_words(const int64_t* words) {
+  int64_t n = 0;
+  for (int i = 0; i < N_ZERO_SLOTS; ++i) n += slot_words(words[i]);
+  return n;
+}
+
+// The fused launch(es) of one call on a planned context.
+int launch_fused(const dsa_ctx* c, float* logits, const int32_t* starts, const int32_t* ends,
+                 int32_t* block_ids, int32_t* token_ids, float* scores, uint32_t flags,
+                 hipStream_t stream) {
+  Params p = base_params(c);
+  p.logits = logits;
+  p.starts = starts;
+  p.ends = ends;
+  p.block_ids = block_ids;
+  p.token_ids = token_ids;
+  p.scores = scores;
+  p.flags = flags & DSA_WRITE_MASK;
+  // Long rows need the second pass: in the same launch (its workgroups wait
+  // for their row's first pass) or, on request, in a second launch.
+  const bool long_rows = may_split(c);
+  const bool two = long_rows && (flags & DSA_TWO_LAUNCHES);
+  p.balanced = long_rows && c->balanced;
+  // First launch: short rows and pass 1; pass 2 in the same launch or a
+  // second one.
+  const int npc = c->NQ + c->sh.rows - 1;
+  const int first = p.balanced ? c->sh.rows + npc : c->G;
+  const int second = p.balanced ? npc + c->sh.rows : c->G + c->sh.rows;
+  const int grid = fused_grid(c);
+  int r2 = DSA_OK;
+  const Kernel kern = p.balanced ? Kernel::FusedBalanced : Kernel::Fused;
+  p.phase_base = 0;
+  launch_bs(p.B, kern, (unsigned)(two ? first : grid), p, stream);
+  if ((r2 = launch_check("k_fused launch")) != DSA_OK) return r2;
+  if (two) {
+    p.phase_base = first;
+    launch_bs(p.B, kern, (unsigned)second, p, stream);
+    r2 = launch_check("k_fused (second pass) launch");
+  }
+  return r2;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_err.c_str(); }
+
+int dsa_select_init(const dsa_shape* s, int device, dsa_ctx** out) {
+  if (out == nullptr) return fail(DSA_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  int rc = validate_shape(s, device);
+  if (rc != DSA_OK) return rc;
+  dsa_ctx* c = new (std::nothrow) dsa_ctx;
+  if (!c) return fail(DSA_ERR_HIP, "host allocation failed");
+  rc = on_device(device, [&]() -> int {
+    int cus = 0;
+    hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+    int64_t words[N_SLOTS];
+    const int r = plan_ctx(s, device, cus, c, words);
+    if (r != DSA_OK || empty_shape(c)) return r;
     e = hipMalloc(&c->ws, c->ws_bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
     e = hipMemset(c->ws, 0, c->ws_bytes);
     if (e != hipSuccess) return hip_fail(e, "hipMemset(workspace)");
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-    uint32_t* base = static_cast<uint32_t*>(c->ws);
-    uint32_t** slots[] = {&c->ws_key, &c->ws_list, &c->ws_flat, &c->ws_hist, &c->ws_cnt,
-                          &c->ws_row, &c->ws_sel, &c->ws_dblk, &c->ws_tkey, &c->ws_tcol,
-                          &c->ws_cand, &c->ws_ccnt, &c->status};
-    static_assert(sizeof(slots) / sizeof(slots[0]) == sizeof(words) / sizeof(words[0]), "slots");
-    int64_t pos = 0;
-    for (int i = 0; i < (int)(sizeof(slots) / sizeof(slots[0])); ++i) {
-      *slots[i] = words[i] ? base + pos : nullptr;
-      pos += (words[i] + 63) / 64 * 64;
-    }
+    assign_slots(c, static_cast<uint32_t*>(c->ws), words);
     return DSA_OK;
   });
   if (rc != DSA_OK) {
@@ -376,36 +479,59 @@ int dsa_select_fused(dsa_ctx* c, float* logits, const int32_t* starts, const int
   if (!logits || !ends || !block_ids || !token_ids)
     return fail(DSA_ERR_INVALID_ARG, "logits, ends, block_ids and token_ids must be non-null");
   return on_device(c->device, [&]() -> int {
-    Params p = base_params(c);
-    p.logits = logits;
-    p.starts = starts;
-    p.ends = ends;
-    p.block_ids = block_ids;
-    p.token_ids = token_ids;
-    p.scores = scores;
-    p.flags = flags & DSA_WRITE_MASK;
-    // Long rows need the second pass: in the same launch (its workgroups wait
-    // for their row's first pass) or, on request, in a second launch.
-    const bool long_rows = may_split(c);
-    const bool two = long_rows && (flags & DSA_TWO_LAUNCHES);
-    p.balanced = long_rows && c->balanced;
-    // First launch: short rows and pass 1; pass 2 in the same launch or a
-    // second one.
-    const int npc = c->NQ + c->sh.rows - 1;
-    const int first = p.balanced ? c->sh.rows + npc : c->G;
-    const int second = p.balanced ? npc + c->sh.rows : c->G + c->sh.rows;
-    const int grid = fused_grid(c);
-    int r2 = DSA_OK;
-    const Kernel kern = p.balanced ? Kernel::FusedBalanced : Kernel::Fused;
-    p.phase_base = 0;
-    launch_bs(p.B, kern, (unsigned)(two ? first : grid), p, stream);
-    if ((r2 = launch_check("k_fused launch")) != DSA_OK) return r2;
-    if (two) {
-      p.phase_base = first;
-      launch_bs(p.B, kern, (unsigned)second, p, stream);
-      r2 = launch_check("k_fused (second pass) launch");
+    return launch_fused(c, logits, starts, ends, block_ids, token_ids, scores, flags, stream);
+  });
+}
+
+int dsa_select_fused_noalloc(const dsa_shape* s, int device, float* logits,
+                             const int32_t* starts, const int32_t* ends, int32_t* block_ids,
+                             int32_t* token_ids, float* scores, uint32_t flags,
+                             uint32_t* status, hipStream_t stream) {
+  int rc = validate_shape(s, device);
+  if (rc != DSA_OK) return rc;
+  if (flags & ~(uint32_t)(DSA_WRITE_MASK | DSA_TWO_LAUNCHES))
+    return fail(DSA_ERR_INVALID_ARG, "unknown flags %#x", flags);
+  if (s->rows == 0 || s->width == 0) return DSA_OK;
+  if (!logits || !ends || !block_ids || !token_ids)
+    return fail(DSA_ERR_INVALID_ARG, "logits, ends, block_ids and token_ids must be non-null");
+  if (device >= NOALLOC_MAX_DEVICES)
+    return fail(DSA_ERR_UNSUPPORTED, "device %d: at most %d devices", device, NOALLOC_MAX_DEVICES);
+  return on_device(device, [&]() -> int {
+    NoallocDevice& nd = g_noalloc[device];
+    {
+      std::lock_guard<std::mutex> lock(g_noalloc_mutex);
+      if (!nd.ready) {
+        // Once per device, with the device current: the device address of
+        // this device's copy of the scratch array, and the CU count.
+        void* ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(CU count)");
+        nd.ptr = static_cast<uint32_t*>(ptr);
+        nd.cus = cus;
+        nd.ready = true;
+      }
     }
-    return r2;
+    dsa_ctx c;
+    int64_t words[N_SLOTS];
+    int r = plan_ctx(s, device, nd.cus, &c, words);
+    if (r != DSA_OK) return r;
+    if (c.ws_bytes > NOALLOC_SCRATCH_BYTES)
+      return fail(DSA_ERR_UNSUPPORTED,
+                  "this shape needs %lld bytes of workspace; the allocation-free entry point "
+                  "holds %lld (use dsa_select_init and dsa_select_fused)",
+                  (long long)c.ws_bytes, (long long)NOALLOC_SCRATCH_BYTES);
+    assign_slots(&c, nd.ptr, words);
+    if (status) c.status = status;
+    // The scratch keeps the previous call's contents (of any shape): the words
+    // that must start at zero are cleared by a kernel on the call's stream.
+    const int64_t nz = zero_words(words);
+    const unsigned zb = (unsigned)std::min<int64_t>((nz / 4 + 255) / 256, 1024);
+    hipLaunchKernelGGL(k_zero_words, dim3(zb), dim3(256), 0, stream, nd.ptr, nz);
+    if ((r = launch_check("k_zero_words launch")) != DSA_OK) return r;
+    return launch_fused(&c, logits, starts, ends, block_ids, token_ids, scores, flags, stream);
   });
 }
 
