@@ -116,8 +116,14 @@ struct Row {
 
 DSA_DEV Row row_bounds(const Params& p, int r) {
   Row rb;
-  const int64_t s = p.starts ? (int64_t)p.starts[r / p.starts_repeat] : 0;
-  const int64_t e = (int64_t)p.ends[r / p.ends_repeat];
+  // Both loads are issued before either value is used (without starts the
+  // first one re-reads the end and is discarded), so one round trip serves.
+  const int32_t* ep = p.ends + r / p.ends_repeat;
+  const int32_t* sp = p.starts ? p.starts + r / p.starts_repeat : ep;
+  const int32_t sv = *sp;
+  const int32_t ev = *ep;
+  const int64_t s = p.starts ? (int64_t)sv : 0;
+  const int64_t e = (int64_t)ev;
   const int64_t ec = e < p.width ? e : p.width;
   rb.bad = s < 0;
   const int64_t L = (s < 0 || ec <= s) ? 0 : ec - s;
@@ -760,24 +766,59 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
     no_low = __syncthreads_or(low) == 0;
     auto getk = [&](int i) { return keys[i]; };
     if (do_select) wg_radix_select<NT>(nlb, (uint32_t)Kp, getk, sm, T, q, true, true);
+    // The token top-k in closed form, written by this same pass, when every
+    // kept column ranks above -inf (no live value at or below -inf), the
+    // newest block is kept (its +inf key is above T) and the kept columns
+    // C = (Kp - 1) * B + (the newest block's columns) are at most Kt: the
+    // tokens are then the C kept columns plus the first Kt - C columns of the
+    // dropped blocks in column order.  In ascending order, kept block i with
+    // kept-rank j (all earlier kept blocks whole) starts at position
+    // j * B + min(Kt - C, (i - j) * B), and a dropped column c taken by the
+    // fill sits at position c - s (every block before it is taken whole).
+    const int Kt = min(p.k_tokens, L);
+    const int64_t C = (int64_t)(Kp - 1) * B + (L - (int64_t)(nlb - 1) * B);
+    const bool fuse_tok = no_low && T < KEY_POS_INF && L > p.k_tokens && C <= Kt;
+    const int64_t qt = (int64_t)Kt - C;
+    int32_t* tout = p.token_ids + (int64_t)r * p.k_tokens;
+    const int32_t s32 = (int32_t)rb.s;
     // One ordered pass: kept ids out, the lowest non-kept ids listed (for the
     // token fill), and each non-kept block masked by the lane that owns it.
     const bool do_mask = (p.flags & DSA_WRITE_MASK) && nlb > Kp;
     uint32_t* nonkept = sm.tkey;
     wg_rule_emit<NT>(nlb, T, q, getk, [&](int i, uint32_t rank, bool kept) {
+      const int n = (int)min((int64_t)B, (int64_t)L - (int64_t)i * B);
       if (kept) {
         if (rank < (uint32_t)Kp) {   // (always, for an exact histogram)
           bout[rank] = i;
-          sel[rank] = (uint32_t)i;
+          if (!fuse_tok) sel[rank] = (uint32_t)i;
+          else {
+            const int64_t pos = (int64_t)rank * B + min(qt, ((int64_t)i - rank) * B);
+            if constexpr (BS > 0) {
+#pragma unroll
+              for (int e = 0; e < BS; ++e)
+                if (e < n) tout[pos + e] = s32 + i * BS + e;
+            } else {
+              for (int e = 0; e < n; ++e) tout[pos + e] = s32 + i * B + e;
+            }
+          }
         }
       } else {
         const uint32_t nk = (uint32_t)i - rank;
-        if (nk < (uint32_t)TK_CAP) nonkept[nk] = (uint32_t)i;
+        if (!fuse_tok) {
+          if (nk < (uint32_t)TK_CAP) nonkept[nk] = (uint32_t)i;
+        } else if ((int64_t)nk * B < qt) {
+          const int m = (int)min((int64_t)n, qt - (int64_t)nk * B);
+          for (int e = 0; e < m; ++e) tout[(int64_t)i * B + e] = s32 + i * B + e;
+        }
         if (do_mask) mask_block_lane<BS>(rowp, p.col_stride, B, L, vec, i);
       }
     }, sm);
     n_nonkept = min(nlb - Kp, TK_CAP);
     for (int i = Kp + threadIdx.x; i < p.k_blocks; i += NT) bout[i] = -1;
+    if (fuse_tok) {
+      for (int i = Kt + threadIdx.x; i < p.k_tokens; i += NT) tout[i] = -1;
+      return;
+    }
   }
   __syncthreads();
   token_stage<BS>(p, r, rb, rowp, sel, Kp, T, true, no_low, sm, sm.tkey, n_nonkept);
