@@ -272,3 +272,95 @@ def make_custom(rows: int, width: int, block_size: int, k_blocks: int,
     st = None if starts is None else np.asarray(starts, dtype=np.int32)
     return build_case("custom", sh, st, np.asarray(ends, dtype=np.int32), seed,
                       cfg=0, dup_frac=dup_frac, outlier_frac=outlier_frac)
+
+
+# --------------------------------------------------------------------------
+# Inputs of the fused indexer-logits producer (FP8 query/key codes).
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class IndexerCase:
+    """q8 uint8 [Q, H, D] and k8 uint8 [S, D] hold OCP E4M3 codes; w float32
+    [Q, H]; kscale float32 [S] or None; row t reads starts[t // starts_repeat]
+    (None: 0) and ends[t // ends_repeat]."""
+    name: str
+    q8: np.ndarray
+    k8: np.ndarray
+    w: np.ndarray
+    kscale: Optional[np.ndarray]
+    starts: Optional[np.ndarray]
+    ends: np.ndarray
+    block_size: int
+    k_blocks: int
+    k_tokens: int
+    starts_repeat: int = 1
+    ends_repeat: int = 1
+
+    @property
+    def queries(self) -> int:
+        return self.q8.shape[0]
+
+    @property
+    def heads(self) -> int:
+        return self.q8.shape[1]
+
+    @property
+    def head_dim(self) -> int:
+        return self.q8.shape[2]
+
+    @property
+    def keys(self) -> int:
+        return self.k8.shape[0]
+
+
+def e4m3_codes(rng: np.random.Generator, shape, exp_lo: int = 5, exp_hi: int = 7) -> np.ndarray:
+    """Random E4M3 bytes: random sign, exponent field in [exp_lo, exp_hi],
+    random 3-bit mantissa (bit fields only; no value arithmetic)."""
+    sign = rng.integers(0, 2, size=shape, dtype=np.uint8) << 7
+    expo = rng.integers(exp_lo, exp_hi + 1, size=shape, dtype=np.uint8) << 3
+    mant = rng.integers(0, 8, size=shape, dtype=np.uint8)
+    return (sign | expo | mant).astype(np.uint8)
+
+
+def make_indexer_custom(queries: int, keys: int, heads: int, head_dim: int, block_size: int,
+                        k_blocks: int, k_tokens: int, ends, starts=None, seed: int = 1,
+                        with_kscale: bool = True, starts_repeat: int = 1,
+                        ends_repeat: int = 1, name: str = "indexer_custom") -> IndexerCase:
+    """Seeded synthetic indexer inputs.  Query and key codes have exponent
+    fields 5..7 (magnitudes 0.25..1.875), head weights are +-n/16 with n in
+    1..16, and key scales are 1, 1/2 or 1/4."""
+    rng = np.random.default_rng([seed, 48726])
+    q8 = e4m3_codes(rng, (queries, heads, head_dim))
+    k8 = e4m3_codes(rng, (keys, head_dim))
+    n = rng.integers(1, 17, size=(queries, heads)).astype(np.float32)
+    sgn = np.where(rng.integers(0, 2, size=(queries, heads)) == 1, 1.0, -1.0).astype(np.float32)
+    w = (sgn * n / np.float32(16.0)).astype(np.float32)
+    kscale = None
+    if with_kscale:
+        kscale = np.ldexp(np.ones(keys, np.float32),
+                          -rng.integers(0, 3, size=keys)).astype(np.float32)
+    st = None if starts is None else np.asarray(starts, dtype=np.int32)
+    return IndexerCase(name, q8, k8, w, kscale, st, np.asarray(ends, dtype=np.int32),
+                       block_size, k_blocks, k_tokens, starts_repeat, ends_repeat)
+
+
+INDEXER_CONFIGS = {
+    # a prefill chunk of 8192 queries at the end of a 262,144-token context,
+    # 64 indexer heads of dimension 128, top-256 blocks of 8 then top-2048 tokens
+    "indexer_prefill": dict(queries=8192, keys=262144, heads=64, head_dim=128,
+                            block_size=8, k_blocks=256, k_tokens=2048),
+    # the same per-row work on a chunk of 256 queries (parity-sized)
+    "indexer_small": dict(queries=256, keys=65536, heads=64, head_dim=128,
+                          block_size=8, k_blocks=256, k_tokens=2048),
+}
+
+
+def make_indexer_config(name: str, seed_offset: int = 0) -> IndexerCase:
+    """Causal bounds: query t of a chunk of Q at the end of S keys sees keys
+    [0, S - Q + t + 1)."""
+    c = INDEXER_CONFIGS[name]
+    Q, S = c["queries"], c["keys"]
+    ends = (S - Q + np.arange(Q) + 1).astype(np.int32)
+    return make_indexer_custom(Q, S, c["heads"], c["head_dim"], c["block_size"],
+                               c["k_blocks"], c["k_tokens"], ends,
+                               seed=BASE_SEED + 100 + seed_offset, name=name)
