@@ -71,8 +71,11 @@ def indexer_logits_row(q8_row, k8_cols, w_row, kscale_cols=None) -> np.ndarray:
     q8_row: uint8 [H, D]; k8_cols: uint8 [n, D]; w_row: float32 [H];
     kscale_cols: float32 [n] or None (all ones).
     """
-    q = e4m3_decode(q8_row)                       # [H, D]
-    k = e4m3_decode(k8_cols)                      # [n, D]
+    return _logits_decoded(e4m3_decode(q8_row), e4m3_decode(k8_cols), w_row, kscale_cols)
+
+
+def _logits_decoded(q, k, w_row, kscale_cols):
+    """The formula on decoded values: q float64 [H, D], k float64 [n, D]."""
     d = k @ q.T                                   # [n, H]: q[t, h] . k[c]
     w = np.asarray(w_row, dtype=np.float64)
     s = np.maximum(d, 0.0) @ w                    # [n]: sum_h w[h] * max(0, d)
@@ -119,12 +122,13 @@ def indexer_select(q8, k8, w, kscale, starts, ends, B: int, k_blocks: int, k_tok
     block_ids = np.full((Q, k_blocks), -1, dtype=np.int32)
     token_ids = np.full((Q, k_tokens), -1, dtype=np.int32)
     logits = {}
+    kd = e4m3_decode(k8)                          # every key decoded once
     for t in (range(Q) if rows is None else rows):
         s, e, L = dsa_oracle.row_bounds(t, starts, ends, S, starts_repeat, ends_repeat)
         if L == 0:
             continue
         ks = None if kscale is None else kscale[s:e]
-        lg = indexer_logits_row(q8[t], k8[s:e], w[t], ks)
+        lg = _logits_decoded(e4m3_decode(q8[t]), kd[s:e], w[t], ks)
         _, bl, _, tk = dsa_oracle.select_row(lg, B, k_blocks, k_tokens)
         block_ids[t, : bl.size] = bl
         token_ids[t, : tk.size] = tk + s

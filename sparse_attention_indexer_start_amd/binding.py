@@ -30,6 +30,7 @@ EXPORTED = (
     "dsa_select_init", "dsa_select_destroy", "dsa_select_query", "dsa_block_scores",
     "dsa_topk", "dsa_candidate_mask", "dsa_select_fused", "dsa_read_status",
     "dsa_reset_workspace", "dsa_last_error", "dsa_select_fused_noalloc",
+    "dsa_indexer_select", "dsa_indexer_last_error",
 )
 
 
@@ -54,6 +55,16 @@ class LaunchInfo(ctypes.Structure):
         ("programs_per_row", ctypes.c_int32), ("threads_per_group", ctypes.c_int32),
         ("grid_groups", ctypes.c_int32), ("small_row_blocks", ctypes.c_int32),
         ("workspace_bytes", ctypes.c_int64), ("fused_launches", ctypes.c_int32),
+    ]
+
+
+class IndexerShape(ctypes.Structure):
+    _fields_ = [
+        ("queries", ctypes.c_int32), ("heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("k_blocks", ctypes.c_int32), ("k_tokens", ctypes.c_int32),
+        ("keys", ctypes.c_int64), ("starts_repeat", ctypes.c_int32),
+        ("ends_repeat", ctypes.c_int32),
     ]
 
 
@@ -88,9 +99,12 @@ def load() -> ctypes.CDLL:
         lib.dsa_reset_workspace.argtypes = [vp, vp]
         lib.dsa_select_fused_noalloc.argtypes = [ctypes.POINTER(Shape), i32, vp, vp, vp, vp,
                                                  vp, vp, u32, vp, vp]
+        lib.dsa_indexer_select.argtypes = [ctypes.POINTER(IndexerShape), i32, vp, vp, vp, vp,
+                                           vp, vp, vp, vp, vp, vp]
+        lib.dsa_indexer_last_error.restype = ctypes.c_char_p
         lib.dsa_last_error.restype = ctypes.c_char_p
         for name in EXPORTED:
-            if name != "dsa_last_error":
+            if name not in ("dsa_last_error", "dsa_indexer_last_error"):
                 getattr(lib, name).restype = i32
         _lib = lib
         return lib
@@ -307,3 +321,53 @@ def select_fused_noalloc(logits, starts, ends, block_ids, token_ids, block_size:
                                            _ptr(ends), _ptr(block_ids), _ptr(token_ids),
                                            _ptr(scores), flags, _ptr(status),
                                            ctypes.c_void_p(stream.cuda_stream)))
+
+
+def indexer_select(q8, k8, w, kscale, starts, ends, block_size: int, k_blocks: int,
+                   k_tokens: int, starts_repeat: int = 1, ends_repeat: int = 1,
+                   block_ids=None, token_ids=None, logits_out=None, stream=None):
+    """The fused FP8 indexer logits plus selection (include/dsa_indexer.h).
+
+    q8 uint8 [Q, H, D] and k8 uint8 [S, D] device tensors of E4M3 codes, w
+    float32 [Q, H], kscale float32 [S] or None, starts/ends int32.  Returns
+    (block_ids [Q, k_blocks], token_ids [Q, k_tokens]), allocated with torch
+    when not given.  ``logits_out`` (float32 [Q, S]) receives the live logits.
+    """
+    import torch
+    Q, H, D = q8.shape
+    S = k8.shape[0]
+    dev = q8.device
+    for t, name, dt in ((q8, "q8", torch.uint8), (k8, "k8", torch.uint8),
+                        (w, "w", torch.float32), (kscale, "kscale", torch.float32),
+                        (starts, "starts", torch.int32), (ends, "ends", torch.int32),
+                        (logits_out, "logits_out", torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dt} device tensor")
+    if k8.dim() != 2 or k8.shape[1] != D or tuple(w.shape) != (Q, H):
+        raise ValueError("k8 must be [S, D] and w [Q, H]")
+    if kscale is not None and tuple(kscale.shape) != (S,):
+        raise ValueError("kscale must be [S]")
+    if ends is None or ends.numel() < -(-Q // ends_repeat):
+        raise ValueError(f"ends needs {-(-Q // ends_repeat)} entries")
+    if starts is not None and starts.numel() < -(-Q // starts_repeat):
+        raise ValueError(f"starts needs {-(-Q // starts_repeat)} entries")
+    if logits_out is not None and tuple(logits_out.shape) != (Q, S):
+        raise ValueError("logits_out must be [Q, S]")
+    if block_ids is None:
+        block_ids = torch.empty((Q, k_blocks), dtype=torch.int32, device=dev)
+    if token_ids is None:
+        token_ids = torch.empty((Q, k_tokens), dtype=torch.int32, device=dev)
+    for t, name, shp in ((block_ids, "block_ids", (Q, k_blocks)),
+                         (token_ids, "token_ids", (Q, k_tokens))):
+        if t.dtype != torch.int32 or not t.is_contiguous() or tuple(t.shape) != shp:
+            raise ValueError(f"{name} must be contiguous int32 {shp}")
+    shape = IndexerShape(Q, H, D, block_size, k_blocks, k_tokens, S, starts_repeat, ends_repeat)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    rc = load().dsa_indexer_select(ctypes.byref(shape), dev.index or 0, _ptr(q8), _ptr(k8),
+                                   _ptr(w), _ptr(kscale), _ptr(starts), _ptr(ends),
+                                   _ptr(block_ids), _ptr(token_ids), _ptr(logits_out),
+                                   ctypes.c_void_p(stream.cuda_stream))
+    if rc != 0:
+        raise DsaError(rc, load().dsa_indexer_last_error().decode(errors="replace"))
+    return block_ids, token_ids

@@ -1,6 +1,7 @@
 """The C ABI on the host: the library loads, exports every declared symbol, and
 rejects bad arguments with a status and a message (no GPU needed)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -9,7 +10,7 @@ import pytest
 from sparse_attention_indexer_start_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dsa_select.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 @pytest.fixture(scope="module")
@@ -21,9 +22,11 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
