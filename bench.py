@@ -207,6 +207,67 @@ def run_workload(name: str, steps: int, warmup: int, write_mask: bool, use_graph
     return out
 
 
+FP8_PEAK_TFLOPS = 5000.0   # MI355X dense FP8 matrix peak
+
+
+def run_indexer(name: str, steps: int, warmup: int) -> dict:
+    """Graph replay of `steps` fused FP8 indexer calls (logits never stored)."""
+    import numpy as np
+    import torch
+    from sparse_attention_indexer_start_amd import binding
+    from sparse_attention_indexer_start_amd import workloads as wl
+
+    log(f"{name}: generating")
+    case = wl.make_indexer_config(name)
+    dev = torch.device("cuda", 0)
+    d = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q8, k8, w, ks, st, en = d(case.q8), d(case.k8), d(case.w), d(case.kscale), \
+        d(case.starts), d(case.ends)
+    bids = torch.empty((case.queries, case.k_blocks), dtype=torch.int32, device=dev)
+    tids = torch.empty((case.queries, case.k_tokens), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        binding.indexer_select(q8, k8, w, ks, st, en, case.block_size, case.k_blocks,
+                               case.k_tokens, case.starts_repeat, case.ends_repeat,
+                               block_ids=bids, token_ids=tids)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            call()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    lens = np.minimum(case.ends.astype(np.int64), case.keys)
+    live = int(lens.sum())
+    # the block pass: 2*H*D flops per (query, live key); kept-column recompute
+    # only when K_blk * B > K_tok (not in this configuration)
+    flops = 2.0 * case.heads * case.head_dim * live
+    achieved = flops / (ms * 1e-3) / 1e12
+    return dict(
+        ms_per_step=ms, queries_per_s=case.queries / (ms * 1e-3),
+        config={"workload": name, "queries": case.queries, "keys": case.keys,
+                "heads": case.heads, "head_dim": case.head_dim,
+                "block_size": case.block_size, "k_blocks": case.k_blocks,
+                "k_tokens": case.k_tokens, "dtype": "fp8 e4m3 in, fp32 accumulate",
+                "graph": True},
+        flops_per_call=flops, live_keys_per_call=live,
+        roofline={"bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS,
+                  "unit": "TFLOP/s", "frac": achieved / FP8_PEAK_TFLOPS, "traffic": None,
+                  "basis": "2*heads*head_dim flops per (query, live key) over the graph "
+                           "replay's time per call"},
+    )
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +284,10 @@ def main() -> int:
     ap.add_argument("--no-secondary", action="store_true",
                     help="do not also time the long-decode workload")
     ap.add_argument("--buffer-budget-gb", type=float, default=48.0)
+    ap.add_argument("--no-indexer", action="store_true",
+                    help="do not also time the fused FP8 indexer (prefill chunk)")
+    ap.add_argument("--indexer-only", action="store_true",
+                    help="time only the fused FP8 indexer")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -242,6 +307,10 @@ def main() -> int:
     write_mask = not args.no_mask
     use_graph = not args.no_graph
 
+    if args.indexer_only:
+        ix = run_indexer("indexer_prefill", min(args.steps, 10), min(args.warmup, 2))
+        print(json.dumps({"indexer_prefill": ix}), flush=True)
+        return 0
     main_run = run_workload(args.workload, args.steps, args.warmup, write_mask, use_graph,
                             args.buffer_budget_gb, args.width)
     second = None
@@ -249,6 +318,10 @@ def main() -> int:
         second = run_workload("long_decode", args.steps, args.warmup, write_mask, use_graph,
                               args.buffer_budget_gb)
         second.pop("case")
+
+    indexer = None
+    if not args.no_indexer and args.width is None:
+        indexer = run_indexer("indexer_prefill", min(args.steps, 10), min(args.warmup, 2))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -286,6 +359,8 @@ def main() -> int:
         out["long_decode"] = {k: second[k] for k in (
             "ms_per_step", "rows_per_s", "alg_bytes_per_call", "needed_bytes_per_call",
             "eager_call_ms_mean", "roofline", "config")}
+    if indexer is not None:
+        out["indexer_prefill"] = indexer
     print(json.dumps(out), flush=True)
     return 0
 

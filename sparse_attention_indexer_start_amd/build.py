@@ -57,7 +57,8 @@ def units(extra=()) -> list:
     out = [(os.path.join(BUILD_DIR, "dsa_select.o"),
             [*_common(), *extra, "-c", HOST_SOURCE]),
            (os.path.join(BUILD_DIR, "dsa_indexer.o"),
-            [*_common(), *extra, "-c", INDEXER_SOURCE])]
+            # matrix-core results straight into VGPRs (no accumulator copies)
+            [*_common(), *extra, "-mllvm", "-amdgpu-mfma-vgpr-form", "-c", INDEXER_SOURCE])]
     for bs in BLOCK_SIZES:
         out.append((os.path.join(BUILD_DIR, f"dsa_bs{bs}.o"),
                     [*_common(), *extra, f"-DDSA_BS={bs}", "-c", BS_SOURCE]))

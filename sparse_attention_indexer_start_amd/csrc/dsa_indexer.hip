@@ -53,6 +53,7 @@ constexpr int WAVES = 4;            // query rows per workgroup
 constexpr int CAP = 1024;           // candidate entries per wave
 constexpr int KMAX = CAP / 2;       // largest K the streaming select keeps
 constexpr int D = 128;              // head dimension (bytes per FP8 key)
+constexpr int STAGE = 128;          // keys staged in LDS per step (shared mode)
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -175,7 +176,7 @@ DSA_DEV void wave_offer(WaveLds& s, int& n, uint32_t& thr, int K, bool valid, ui
                         uint32_t id) {
   uint64_t m = ballot(valid && key > thr);
   if (m == 0) return;
-  if (n + (int)popc(m) > CAP) {
+  if (n + (int)popc(m) > CAP) {          // (at most 32 offers at a time)
     thr = wave_keep_top(s, n, K);
     n = K;
     m = ballot(valid && key > thr);
@@ -199,6 +200,16 @@ DSA_DEV v8i load_key_slice(const uint8_t* k, int64_t col) {
   return r;
 }
 
+// x summed over the four lanes l % 16 + 16 j (every lane gets the sum):
+// v_permlane32_swap exchanges the two 32-lane halves of a register and
+// v_permlane16_swap the two 16-lane rows of each half, without LDS.
+DSA_DEV float sum_over_lane_groups(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(h[0]) + __uint_as_float(h[1]);   // x(l) + x(l ^ 32)
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);            // y(l) + y(l ^ 16)
+}
+
 // Logit of key `col` (the same value in the four lanes l % 16 == col slot).
 template <int HG>
 DSA_DEV float logit_of(const v8i (&qa)[HG], const float (&wr)[HG][4], v8i kb) {
@@ -209,83 +220,239 @@ DSA_DEV float logit_of(const v8i (&qa)[HG], const float (&wr)[HG][4], v8i kb) {
     // E8M0 scales of 127 (2^0): the plain FP8 product.
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[g], kb, acc, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part += wr[g][i] * fmaxf(acc[i], 0.f);
+    for (int i = 0; i < 4; ++i)   // ReLU as one signed-integer max of the bits
+      part += wr[g][i] * __int_as_float(max(__float_as_int(acc[i]), 0));
   }
-  part += __shfl_xor(part, 16, 64);
-  part += __shfl_xor(part, 32, 64);
-  return part;
+  return sum_over_lane_groups(part);
+}
+
+// 2 * HG matrix-core instructions for a pair of 16-key halves: acc[h][g]
+// = heads 16g.. of this lane's slot times half h's keys.
+template <int HG>
+DSA_DEV void mfma_pair(const v8i (&qa)[HG], v8i ka, v8i kb, v4f (&acc)[2][HG]) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    acc[0][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[g], ka, z, 0, 0, 0, 127, 0, 127);
+    acc[1][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[g], kb, z, 0, 0, 0, 127, 0, 127);
+  }
+}
+
+// The head sums of a pair: lanes 0-15 get the first half's key l % 16,
+// lanes 16-31 the second half's (lanes 32-63 the same again).
+template <int HG>
+DSA_DEV float epilogue_pair(const float (&wr)[HG][4], const v4f (&acc)[2][HG]) {
+  float pa = 0.f, pb = 0.f;
+#pragma unroll
+  for (int g = 0; g < HG; ++g)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {   // ReLU as one signed-integer max of the bits
+      pa += wr[g][i] * __int_as_float(max(__float_as_int(acc[0][g][i]), 0));
+      pb += wr[g][i] * __int_as_float(max(__float_as_int(acc[1][g][i]), 0));
+    }
+  pa = sum_over_lane_groups(pa);
+  pb = sum_over_lane_groups(pb);
+  return (lane() & 16) ? pb : pa;
+}
+
+// The B operand of half h (keys 16h..16h+15 of a staged 32-key tile) for
+// this lane: key 16h + l % 16, bytes [32 * (l / 16), +32).  Tile rows are
+// 128 bytes; their 16-byte chunks are stored XOR-swizzled by the row's low
+// three bits, so the 16 rows read by one instruction spread over the banks.
+DSA_DEV v8i lds_key_slice(const uint8_t* tile, int h) {
+  const int r = 16 * h + (lane() & 15);
+  const int j0 = 2 * (lane() >> 4);
+  const int4 x = *reinterpret_cast<const int4*>(tile + r * D + 16 * (j0 ^ (r & 7)));
+  const int4 y = *reinterpret_cast<const int4*>(tile + r * D + 16 * ((j0 + 1) ^ (r & 7)));
+  v8i v;
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  return v;
 }
 
 template <int HG, int BS>
 __global__ __launch_bounds__(64 * WAVES) void k_indexer_select(Args a) {
   __shared__ WaveLds lds[WAVES];
+  __shared__ __align__(16) uint8_t ktile[2][STAGE * D];   // staged keys, double buffered
+  __shared__ int64_t row_s[WAVES], row_e[WAVES];
   const int w = wave(), l = lane();
   WaveLds& s = lds[w];
   const int t = (int)blockIdx.x * WAVES + w;
-  if (t >= a.Q) return;
-  // Row bounds (both loads issued before either is used).
-  const int32_t* ep = a.ends + t / a.ends_repeat;
-  const int32_t* sp = a.starts ? a.starts + t / a.starts_repeat : ep;
-  const int32_t sv = *sp, ev = *ep;
-  const int64_t s0 = a.starts ? (int64_t)sv : 0;
-  const int64_t e0 = (int64_t)ev < a.S ? (int64_t)ev : a.S;
+  // Row bounds (both loads issued before either is used); rows past the
+  // last query are empty.
+  int64_t s0 = 0, e0 = 0;
+  if (t < a.Q) {
+    const int32_t* ep = a.ends + t / a.ends_repeat;
+    const int32_t* sp = a.starts ? a.starts + t / a.starts_repeat : ep;
+    const int32_t sv = *sp, ev = *ep;
+    s0 = a.starts ? (int64_t)sv : 0;
+    e0 = (int64_t)ev < a.S ? (int64_t)ev : a.S;
+  }
   const int64_t L64 = (s0 < 0 || e0 <= s0) ? 0 : e0 - s0;
   const int L = (int)L64;
-  int32_t* bout = a.block_ids + (int64_t)t * a.k_blocks;
-  int32_t* tout = a.token_ids + (int64_t)t * a.k_tokens;
-  if (L == 0) {
-    for (int i = l; i < a.k_blocks; i += 64) bout[i] = -1;
-    for (int i = l; i < a.k_tokens; i += 64) tout[i] = -1;
-    return;
+  if (l == 0) {
+    row_s[w] = L ? s0 : -1;
+    row_e[w] = L ? e0 : -1;
   }
+  __syncthreads();
+  // The workgroup stages each key tile once for all its rows when every
+  // non-empty row starts at the same offset modulo 16 (then every row's
+  // blocks line up with the 16-key halves of the tiles).
+  int64_t base = -1, top = -1;
+  int live_rows = 0;
+  for (int x = 0; x < WAVES; ++x) {
+    if (row_s[x] < 0) continue;
+    ++live_rows;
+    base = base < 0 ? row_s[x] : min(base, row_s[x]);
+    top = max(top, row_e[x]);
+  }
+  bool shared_mode = live_rows >= 2;
+  for (int x = 0; x < WAVES; ++x)
+    if (row_s[x] >= 0 && ((row_s[x] - base) & 15) != 0) shared_mode = false;
   const int64_t s_ = s0;
   const int nlb = (L + BS - 1) / BS;
   const int Kb = min(a.k_blocks, nlb);
   // This lane's query slices (A operands) and head weights.
   v8i qa[HG];
   float wr[HG][4];
-  const uint8_t* qrow = a.q + (int64_t)t * a.H * D;
+  if (L > 0) {
+    const uint8_t* qrow = a.q + (int64_t)t * a.H * D;
 #pragma unroll
-  for (int g = 0; g < HG; ++g) {
-    const int4* p = reinterpret_cast<const int4*>(qrow + (16 * g + (l & 15)) * D + (l >> 4) * 32);
-    const int4 x = p[0], y = p[1];
-    qa[g][0] = x.x; qa[g][1] = x.y; qa[g][2] = x.z; qa[g][3] = x.w;
-    qa[g][4] = y.x; qa[g][5] = y.y; qa[g][6] = y.z; qa[g][7] = y.w;
+    for (int g = 0; g < HG; ++g) {
+      const int4* p = reinterpret_cast<const int4*>(qrow + (16 * g + (l & 15)) * D + (l >> 4) * 32);
+      const int4 x = p[0], y = p[1];
+      qa[g][0] = x.x; qa[g][1] = x.y; qa[g][2] = x.z; qa[g][3] = x.w;
+      qa[g][4] = y.x; qa[g][5] = y.y; qa[g][6] = y.z; qa[g][7] = y.w;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wr[g][i] = a.w[(int64_t)t * a.H + 16 * g + 4 * (l >> 4) + i];
+      for (int i = 0; i < 4; ++i) wr[g][i] = a.w[(int64_t)t * a.H + 16 * g + 4 * (l >> 4) + i];
+    }
   }
   const uint8_t* krow = a.k + s_ * D;
-  const float* ksr = a.kscale ? a.kscale + s_ : nullptr;
-  float* lout = a.logits_out ? a.logits_out + (int64_t)t * a.S + s_ : nullptr;
+  float* lout = (a.logits_out && L > 0) ? a.logits_out + (int64_t)t * a.S + s_ : nullptr;
   const int c16 = l & 15;
+  const int lo32 = l & 31;
 
   // ---- block pass: logits tile by tile, block maxima, streaming top-K_blk ----
+  // Two 16-key halves per step.  After the head sums every lane group holds
+  // its key's logit, so lanes 0-15 take the first half's and lanes 16-31 the
+  // second's: one block maximum and one offer serve 32 keys.
   int n = 0;
   uint32_t thr = 0u;
-  v8i kb = load_key_slice(krow, min(c16, L - 1));
-  float ks = ksr ? ksr[min(c16, L - 1)] : 1.f;
-  for (int c0 = 0; c0 < L; c0 += 16) {
-    const int cn = c0 + 16;
-    // next tile's keys are in flight while this one is computed
-    v8i kb_next = kb;
-    float ks_next = ks;
-    if (cn < L) {
-      kb_next = load_key_slice(krow, min(cn + c16, L - 1));
-      if (ksr) ks_next = ksr[min(cn + c16, L - 1)];
-    }
-    const int col = c0 + c16;
-    const bool valid = col < L;
-    const float lg = logit_of<HG>(qa, wr, kb) * ks;
-    if (lout && valid && l < 16) lout[col] = lg;
+  // One step's 32 logits (lanes 0-31, key k0 + lane, row-relative column
+  // col) go to the block maxima and the candidate buffer.
+  // ks: the key scale of this lane's key (1 without scales).
+  auto consume = [&](float lg, int col, float ks) {
+    const bool valid = l < 32 && col >= 0 && col < L;
+    lg *= ks;
+    if (lout && valid) lout[col] = lg;
     uint32_t key = valid ? f2key(lg) : 0u;
     key = group_max<BS>(key);
-    const int b = col / BS;
-    const bool head = l < 16 && (c16 % BS) == 0 && valid;
+    const int b = col >= 0 ? col / BS : -1;
+    const bool head = valid && (col % BS) == 0;
     if (b == nlb - 1) key = KEY_POS_INF;
     wave_offer(s, n, thr, Kb, head, key, (uint32_t)b);
-    kb = kb_next;
-    ks = ks_next;
+  };
+  if (shared_mode) {
+    // Each thread stages 4 of the 1024 16-byte chunks of a 128-key step;
+    // the next step's chunks are loaded into registers while this step's
+    // 8 halves are computed from LDS.
+    const int tid = (int)threadIdx.x;
+    constexpr int PER_T = STAGE * D / 16 / (64 * WAVES);
+    // chunk u of this thread: key row (tid >> 3) + 32 u, chunk tid & 7
+    const int tr = tid >> 3, tj = tid & 7;
+    const int soff0 = tr * D + 16 * (tj ^ (tr & 7));     // (row + 32 u) & 7 == row & 7
+    int4 nxt0, nxt1, nxt2, nxt3;
+    static_assert(PER_T == 4, "four staged chunks per thread");
+#define DSA_IDX_FETCH(k0)                                                                   \
+    do {                                                                                    \
+      const uint8_t* src_ = a.k + 16 * tj;                                                  \
+      nxt0 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr, top - 1) * D);            \
+      nxt1 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr + 32, top - 1) * D);       \
+      nxt2 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr + 64, top - 1) * D);       \
+      nxt3 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr + 96, top - 1) * D);       \
+    } while (0)
+#define DSA_IDX_STAGE(buf)                                                                  \
+    do {                                                                                    \
+      *reinterpret_cast<int4*>((buf) + soff0) = nxt0;                                       \
+      *reinterpret_cast<int4*>((buf) + soff0 + 32 * D) = nxt1;                              \
+      *reinterpret_cast<int4*>((buf) + soff0 + 64 * D) = nxt2;                              \
+      *reinterpret_cast<int4*>((buf) + soff0 + 96 * D) = nxt3;                              \
+    } while (0)
+    // key scales of this lane's keys in a step (k0 + 32 m + l % 32), one
+    // step ahead like the keys
+    float ksc[STAGE / 32], ksn[STAGE / 32];
+#pragma unroll
+    for (int m = 0; m < STAGE / 32; ++m) {
+      ksc[m] = a.kscale ? a.kscale[min(base + 32 * m + lo32, top - 1)] : 1.f;
+      ksn[m] = 1.f;
+    }
+    DSA_IDX_FETCH(base);
+    DSA_IDX_STAGE(ktile[0]);
+    __syncthreads();
+    int cur = 0;
+    for (int64_t k0 = base; k0 < top; k0 += STAGE) {
+      const bool more = k0 + STAGE < top;
+      if (more) {
+        DSA_IDX_FETCH(k0 + STAGE);
+        if (a.kscale) {
+#pragma unroll
+          for (int m = 0; m < STAGE / 32; ++m)
+            ksn[m] = a.kscale[min(k0 + STAGE + 32 * m + lo32, top - 1)];
+        }
+      }
+      if (L > 0 && k0 + STAGE > s_ && k0 < e0) {
+        const uint8_t* tile = ktile[cur];
+        // Software pipeline over the step's pairs: the next pair's matrix
+        // instructions are issued between the current pair's epilogue
+        // instructions, so the matrix core and the vector ALU overlap within
+        // the wave.
+        v4f acc[2][2][HG];
+        mfma_pair<HG>(qa, lds_key_slice(tile, 0), lds_key_slice(tile, 1), acc[0]);
+#pragma unroll
+        for (int m = 0; m < STAGE / 32; ++m) {
+          if (m + 1 < STAGE / 32)
+            mfma_pair<HG>(qa, lds_key_slice(tile, 2 * m + 2), lds_key_slice(tile, 2 * m + 3),
+                          acc[(m + 1) & 1]);
+          const float lg = epilogue_pair<HG>(wr, acc[m & 1]);
+          if (m + 1 < STAGE / 32) {
+#pragma unroll
+            for (int x = 0; x < 2 * HG; ++x) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one matrix instruction
+              __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then four vector ALU
+            }
+          }
+          consume(lg, (int)(k0 + 32 * m - s_) + lo32, ksc[m]);
+        }
+      }
+      if (more) DSA_IDX_STAGE(ktile[cur ^ 1]);
+#pragma unroll
+      for (int m = 0; m < STAGE / 32; ++m) ksc[m] = ksn[m];
+      __syncthreads();
+      cur ^= 1;
+    }
+#undef DSA_IDX_FETCH
+#undef DSA_IDX_STAGE
+  } else if (L > 0) {
+    // Each wave streams its own keys; a step's loads are issued one half ahead.
+    v8i kx = load_key_slice(krow, min(c16, L - 1));
+    for (int c0 = 0; c0 < L; c0 += 32) {
+      const v8i ky = load_key_slice(krow, min(c0 + 16 + c16, L - 1));
+      const float lga = logit_of<HG>(qa, wr, kx);
+      if (c0 + 32 < L) kx = load_key_slice(krow, min(c0 + 32 + c16, L - 1));
+      const float lgb = logit_of<HG>(qa, wr, ky);
+      const int col = c0 + lo32;
+      consume((l & 16) ? lgb : lga, col, a.kscale ? a.kscale[s_ + min(col, L - 1)] : 1.f);
+    }
   }
+  int32_t* bout = a.block_ids + (int64_t)t * a.k_blocks;
+  int32_t* tout = a.token_ids + (int64_t)t * a.k_tokens;
+  if (t >= a.Q) return;
+  if (L == 0) {
+    for (int i = l; i < a.k_blocks; i += 64) bout[i] = -1;
+    for (int i = l; i < a.k_tokens; i += 64) tout[i] = -1;
+    return;
+  }
+  const float* ksr = a.kscale ? a.kscale + s_ : nullptr;
   wave_lds_sync();
   (void)wave_keep_top(s, n, Kb);
   n = min(n, Kb);
