@@ -29,10 +29,14 @@ import numpy as np
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
+# The sources of the decode-path kernels the counter profiles are taken on.
+DECODE_SOURCES = ("dsa_bs_unit.hip", "dsa_device.hpp", "dsa_kernels.hpp", "dsa_select.hip")
+
+
 def source_sha() -> str:
-    """Short hash of the kernel sources (ties a counter profile to the code)."""
+    """Short hash of the decode-path kernel sources (ties a counter profile to the code)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in DECODE_SOURCES:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
