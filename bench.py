@@ -268,6 +268,49 @@ def run_indexer(name: str, steps: int, warmup: int) -> dict:
     )
 
 
+def run_row_topk(rows: int, width: int, k: int, steps: int, warmup: int) -> dict:
+    """Graph replay of `steps` cooperative row top-k calls over seeded rows."""
+    import numpy as np
+    import torch
+    from sparse_attention_indexer_start_amd import binding, metrics
+    from sparse_attention_indexer_start_amd import workloads as wl
+
+    log(f"row top-k {rows} x {width}, k={k}: generating")
+    case = wl.make_custom(rows, width, 8, 1, 1, [width] * rows, seed=20261217, dup_frac=0.01)
+    dev = torch.device("cuda", 0)
+    buf = torch.from_numpy(case.buf).to(dev)
+    ends = torch.from_numpy(case.ends).to(dev)
+    op = binding.RowTopk(rows, width, k)
+    out = torch.empty((rows, k), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        op(buf, None, ends, out)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            op(buf, None, ends, out)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    alg = rows * (4 * width + 4 * k + 8)
+    achieved = alg / (ms * 1e-3) / 1e9
+    pieces = op.pieces()
+    op.close()
+    return dict(ms_per_step=ms, rows=rows, width=width, k=k, pieces_per_row=pieces,
+                alg_bytes_per_call=alg,
+                roofline={"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                          "basis": "4*L read + 4*k index stores + 8 B bounds per row over the "
+                                   "graph replay's time per call (the row is read up to five "
+                                   "times: three digit passes, count, emit)"})
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -288,6 +331,10 @@ def main() -> int:
                     help="do not also time the fused FP8 indexer (prefill chunk)")
     ap.add_argument("--indexer-only", action="store_true",
                     help="time only the fused FP8 indexer")
+    ap.add_argument("--no-row-topk", action="store_true",
+                    help="do not also time the cooperative row top-k (16M-column rows)")
+    ap.add_argument("--row-topk-only", action="store_true",
+                    help="time only the cooperative row top-k")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -307,6 +354,11 @@ def main() -> int:
     write_mask = not args.no_mask
     use_graph = not args.no_graph
 
+    if args.row_topk_only:
+        rt = [run_row_topk(1, 16 * 2**20, kk, min(args.steps, 20), min(args.warmup, 2))
+              for kk in (2048, 2**20)]
+        print(json.dumps({"row_topk": rt}), flush=True)
+        return 0
     if args.indexer_only:
         ix = run_indexer("indexer_prefill", min(args.steps, 10), min(args.warmup, 2))
         print(json.dumps({"indexer_prefill": ix}), flush=True)
@@ -322,6 +374,11 @@ def main() -> int:
     indexer = None
     if not args.no_indexer and args.width is None:
         indexer = run_indexer("indexer_prefill", min(args.steps, 10), min(args.warmup, 2))
+
+    row_topk = None
+    if not args.no_row_topk and args.width is None:
+        row_topk = [run_row_topk(1, 16 * 2**20, kk, min(args.steps, 20), min(args.warmup, 2))
+                    for kk in (2048, 2**20)]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -361,6 +418,8 @@ def main() -> int:
             "eager_call_ms_mean", "roofline", "config")}
     if indexer is not None:
         out["indexer_prefill"] = indexer
+    if row_topk is not None:
+        out["row_topk"] = row_topk
     print(json.dumps(out), flush=True)
     return 0
 

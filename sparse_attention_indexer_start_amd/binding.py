@@ -31,6 +31,8 @@ EXPORTED = (
     "dsa_topk", "dsa_candidate_mask", "dsa_select_fused", "dsa_read_status",
     "dsa_reset_workspace", "dsa_last_error", "dsa_select_fused_noalloc",
     "dsa_indexer_select", "dsa_indexer_last_error",
+    "dsa_row_topk_init", "dsa_row_topk_destroy", "dsa_row_topk_pieces", "dsa_row_topk",
+    "dsa_row_topk_last_error",
 )
 
 
@@ -68,6 +70,14 @@ class IndexerShape(ctypes.Structure):
     ]
 
 
+class TopkShape(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("k", ctypes.c_int32), ("width", ctypes.c_int64),
+        ("row_stride", ctypes.c_int64), ("col_stride", ctypes.c_int64),
+        ("starts_repeat", ctypes.c_int32), ("ends_repeat", ctypes.c_int32),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -102,9 +112,14 @@ def load() -> ctypes.CDLL:
         lib.dsa_indexer_select.argtypes = [ctypes.POINTER(IndexerShape), i32, vp, vp, vp, vp,
                                            vp, vp, vp, vp, vp, vp]
         lib.dsa_indexer_last_error.restype = ctypes.c_char_p
+        lib.dsa_row_topk_init.argtypes = [ctypes.POINTER(TopkShape), i32, ctypes.POINTER(vp)]
+        lib.dsa_row_topk_destroy.argtypes = [vp]
+        lib.dsa_row_topk_pieces.argtypes = [vp]
+        lib.dsa_row_topk.argtypes = [vp, vp, vp, vp, vp, vp]
+        lib.dsa_row_topk_last_error.restype = ctypes.c_char_p
         lib.dsa_last_error.restype = ctypes.c_char_p
         for name in EXPORTED:
-            if name not in ("dsa_last_error", "dsa_indexer_last_error"):
+            if not name.endswith("last_error"):
                 getattr(lib, name).restype = i32
         _lib = lib
         return lib
@@ -371,3 +386,70 @@ def indexer_select(q8, k8, w, kscale, starts, ends, block_size: int, k_blocks: i
     if rc != 0:
         raise DsaError(rc, load().dsa_indexer_last_error().decode(errors="replace"))
     return block_ids, token_ids
+
+
+class RowTopk:
+    """Cooperative per-row top-k for very long rows (include/dsa_row_topk.h)."""
+
+    def __init__(self, rows: int, width: int, k: int, row_stride: Optional[int] = None,
+                 col_stride: int = 1, starts_repeat: int = 1, ends_repeat: int = 1,
+                 device: int = 0):
+        lib = load()
+        self.shape = TopkShape(rows, k, width,
+                               max(1, width * col_stride) if row_stride is None else row_stride,
+                               col_stride, starts_repeat, ends_repeat)
+        self.device = device
+        h = ctypes.c_void_p()
+        self._check(lib.dsa_row_topk_init(ctypes.byref(self.shape), device, ctypes.byref(h)))
+        self._h = h
+
+    @staticmethod
+    def _check(rc: int) -> None:
+        if rc != 0:
+            raise DsaError(rc, load().dsa_row_topk_last_error().decode(errors="replace"))
+
+    def pieces(self) -> int:
+        n = load().dsa_row_topk_pieces(self._h)
+        if n < 0:
+            self._check(n)
+        return n
+
+    def __call__(self, logits, starts, ends, out=None, stream=None):
+        import torch
+        sh = self.shape
+        if logits.dtype != torch.float32 or not logits.is_cuda:
+            raise ValueError("logits must be a float32 device tensor")
+        if tuple(logits.shape) != (sh.rows, sh.width):
+            raise ValueError(f"logits shape {tuple(logits.shape)} != {(sh.rows, sh.width)}")
+        if sh.rows > 1 and sh.width > 0 and logits.stride(0) != sh.row_stride:
+            raise ValueError("logits row stride differs from the context's")
+        if sh.width > 1 and logits.stride(1) != sh.col_stride:
+            raise ValueError("logits column stride differs from the context's")
+        for t, name, n in ((starts, "starts", -(-sh.rows // sh.starts_repeat)),
+                           (ends, "ends", -(-sh.rows // sh.ends_repeat))):
+            if t is None:
+                if name == "ends":
+                    raise ValueError("ends is required")
+                continue
+            if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < n:
+                raise ValueError(f"{name} must be a contiguous int32 tensor of >= {n} entries")
+        if out is None:
+            out = torch.empty((sh.rows, sh.k), dtype=torch.int32, device=logits.device)
+        if out.dtype != torch.int32 or not out.is_contiguous() or tuple(out.shape) != (sh.rows, sh.k):
+            raise ValueError(f"out must be contiguous int32 {(sh.rows, sh.k)}")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        self._check(load().dsa_row_topk(self._h, _ptr(logits), _ptr(starts), _ptr(ends),
+                                        _ptr(out), ctypes.c_void_p(stream.cuda_stream)))
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._check(load().dsa_row_topk_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
