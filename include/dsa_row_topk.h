@@ -17,8 +17,9 @@
  *
  * Layout: logits fp32 device view [rows, width], element (r, c) at
  * logits[r * row_stride + c * col_stride]; starts/ends int32 device arrays;
- * out int32 device [rows, k], contiguous, fully written.  Values in [s, e')
- * are expected to be finite.
+ * out int32 device [rows, k], contiguous, fully written.  Every fp32 value is
+ * ranked by the order-preserving key (u >= 2^31 ? ~u : u | 2^31 on its bits):
+ * infinities rank as values, a NaN ranks by its bit pattern.
  *
  * The context owns a workspace of (4096 + 8 + 4 P) words per row, P pieces
  * per row fixed at init from the shape and the device's CU count (it does not
