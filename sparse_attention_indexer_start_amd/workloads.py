@@ -364,3 +364,146 @@ def make_indexer_config(name: str, seed_offset: int = 0) -> IndexerCase:
     return make_indexer_custom(Q, S, c["heads"], c["head_dim"], c["block_size"],
                                c["k_blocks"], c["k_tokens"], ends,
                                seed=BASE_SEED + 100 + seed_offset, name=name)
+
+
+# --------------------------------------------------------------------------
+# Inputs of the sparse attention over each row's selected tokens.
+# --------------------------------------------------------------------------
+
+def bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bf16 codes (round to nearest even on the bit
+    pattern; the inputs here are finite)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@dataclasses.dataclass
+class AttnCase:
+    """q uint16 bf16 [R, Hkv * G, D]; k_cache / v_cache uint16 bf16
+    [num_slots, Hkv, D] (None when the caches are generated on the device
+    from ``cache_seed``); token_ids int32 [R, K] ascending with -1 pads;
+    page_table int32 [num_seqs, pages_per_seq] (-1: unmapped) or None; row r
+    belongs to sequence r // rows_per_seq; gate uint16 bf16 like q, or None."""
+    name: str
+    q: np.ndarray
+    k_cache: Optional[np.ndarray]
+    v_cache: Optional[np.ndarray]
+    token_ids: np.ndarray
+    page_table: Optional[np.ndarray]
+    page_size: int
+    rows_per_seq: int
+    gate: Optional[np.ndarray]
+    kv_heads: int
+    group: int
+    head_dim: int
+    sm_scale: float
+    num_slots: int
+    seq_lens: np.ndarray
+    cache_seed: int = 0
+
+    @property
+    def rows(self) -> int:
+        return self.q.shape[0]
+
+    @property
+    def k_tokens(self) -> int:
+        return self.token_ids.shape[1]
+
+
+def _sorted_sample(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
+    """k distinct integers of [0, n), ascending."""
+    if k >= n:
+        return np.arange(n, dtype=np.int64)
+    if n <= 4 * k:
+        return np.sort(rng.permutation(n)[:k])
+    picked = np.unique(rng.integers(0, n, size=k + k // 4 + 16))
+    while picked.size < k:
+        picked = np.unique(np.concatenate([picked, rng.integers(0, n, size=k)]))
+    return np.sort(rng.permutation(picked)[:k])
+
+
+def make_attn_custom(seq_lens, rows_per_seq: int, kv_heads: int, group: int, head_dim: int,
+                     k_tokens: int, page_size: int = 16, paged: bool = True,
+                     with_gate: bool = True, seed: int = 1, q_scale: float = 1.0,
+                     host_caches: bool = True, spare_pages: int = 3,
+                     name: str = "attn_custom") -> AttnCase:
+    """Seeded synthetic attention inputs.
+
+    Sequence n has seq_lens[n] cached positions; its rows_per_seq rows are
+    consecutive query tokens (multi-token prediction), row j seeing the first
+    seq_lens[n] - (rows_per_seq - 1 - j) positions.  Each row selects
+    min(k_tokens, visible) distinct positions uniformly, ascending, padded
+    with -1.  Pages are scattered: a random permutation of the physical pages
+    (plus ``spare_pages`` never mapped) backs the sequences, and table
+    entries past a sequence's length are -1.  q, K, V and the gate are
+    N(0, 1) rounded to bf16 (q times ``q_scale``); the softmax scale is
+    1 / sqrt(head_dim).
+    """
+    rng = np.random.default_rng([seed, 57273])
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    nseq = seq_lens.size
+    R = nseq * rows_per_seq
+    hq = kv_heads * group
+    pages = [int(-(-int(L) // page_size)) for L in seq_lens]
+    if paged:
+        total = sum(pages) + spare_pages
+        perm = rng.permutation(total).astype(np.int32)
+        pps = max(1, max(pages) if pages else 1)
+        table = np.full((nseq, pps), -1, dtype=np.int32)
+        at = 0
+        for n, p in enumerate(pages):
+            table[n, :p] = perm[at:at + p]
+            at += p
+        num_slots = total * page_size
+    else:
+        table = None
+        num_slots = int(seq_lens.max()) if nseq else 0
+    ids = np.full((R, k_tokens), -1, dtype=np.int32)
+    for n in range(nseq):
+        for j in range(rows_per_seq):
+            vis = max(0, int(seq_lens[n]) - (rows_per_seq - 1 - j))
+            pick = _sorted_sample(rng, vis, min(k_tokens, vis))
+            ids[n * rows_per_seq + j, :pick.size] = pick
+    q = bf16_bits(rng.standard_normal((R, hq, head_dim), dtype=np.float32) * np.float32(q_scale))
+    gate = bf16_bits(rng.standard_normal((R, hq, head_dim), dtype=np.float32)) if with_gate else None
+    kc = vc = None
+    if host_caches:
+        kc = bf16_bits(rng.standard_normal((num_slots, kv_heads, head_dim), dtype=np.float32))
+        vc = bf16_bits(rng.standard_normal((num_slots, kv_heads, head_dim), dtype=np.float32))
+    return AttnCase(name, q, kc, vc, ids, table, page_size, rows_per_seq, gate, kv_heads, group,
+                    head_dim, 1.0 / math.sqrt(head_dim), num_slots, seq_lens,
+                    cache_seed=seed)
+
+
+ATTN_CONFIGS = {
+    # decode at 128 concurrent requests with 3 draft tokens (4 query rows per
+    # request), 2 kv heads of 256 dimensions with 12 query heads each, the
+    # 2048 selected tokens of each row out of contexts of 32K-128K tokens
+    # (5% of requests shorter than 2048), a 64-token paged cache and an
+    # output gate; the K/V caches (about 21 GB) are generated on the device
+    "attn_decode": dict(num_seqs=128, rows_per_seq=4, kv_heads=2, group=12, head_dim=256,
+                        k_tokens=2048, page_size=64, ctx=(32768, 131072), short_frac=0.05,
+                        host_caches=False),
+    # one request (4 rows), 1 kv head with 3 query heads: the latency case
+    "attn_c1": dict(num_seqs=1, rows_per_seq=4, kv_heads=1, group=3, head_dim=256,
+                    k_tokens=2048, page_size=64, ctx=(65536, 65536), short_frac=0.0,
+                    host_caches=False),
+    # parity-sized: 8 requests x 4 rows, host caches, queries scaled by 3 so
+    # that each softmax concentrates on a few tokens
+    "attn_small": dict(num_seqs=8, rows_per_seq=4, kv_heads=2, group=12, head_dim=256,
+                       k_tokens=2048, page_size=64, ctx=(1, 12000), short_frac=0.25,
+                       host_caches=True, q_scale=3.0),
+}
+
+
+def make_attn_config(name: str, seed_offset: int = 0) -> AttnCase:
+    c = ATTN_CONFIGS[name]
+    rng = np.random.default_rng([BASE_SEED + 200 + seed_offset, len(name)])
+    lo, hi = c["ctx"]
+    lens = rng.integers(lo, hi + 1, size=c["num_seqs"])
+    short = rng.random(c["num_seqs"]) < c["short_frac"]
+    lens = np.where(short, rng.integers(1, c["k_tokens"] + 1, size=c["num_seqs"]), lens)
+    return make_attn_custom(lens, c["rows_per_seq"], c["kv_heads"], c["group"], c["head_dim"],
+                            c["k_tokens"], page_size=c["page_size"],
+                            seed=BASE_SEED + 200 + seed_offset, host_caches=c["host_caches"],
+                            q_scale=c.get("q_scale", 1.0), name=name)
