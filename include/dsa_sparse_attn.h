@@ -1,0 +1,101 @@
+/*
+ * dsa_sparse_attn.h -- C ABI of the sparse attention over each query row's
+ * selected tokens on MI355X (gfx950).
+ *
+ * The page on vllm PR #57273 ("Qwen4Exp QSA: sm_90 tuning table", Purpose)
+ * describes the consumer of the 2048 selected tokens per query: grouped-query
+ * attention over those tokens alone, read from a paged bf16 K/V cache, split
+ * over several programs and merged, with a fused output gate; the page on
+ * vllm PR #48726 ("LiteDSA: grouped masked sparse attention") requires each
+ * query to attend exactly its own selected set and reports the log-sum-exp.
+ * Per query row r and query head h (kv head g = h / group):
+ *   P(r)  = the row's token ids that are >= 0 (positions of sequence
+ *           n = r / rows_per_seq), each mapped to a cache slot:
+ *           slot = page_table[n * pages_per_seq + pos / page_size] * page_size
+ *                  + pos % page_size   (page_table NULL: slot = pos);
+ *   s_j   = sm_scale * dot(q[r, h, :], K[slot_j, g, :]);
+ *   lse   = ln sum_j exp(s_j);  o = sum_j exp(s_j - lse) * V[slot_j, g, :];
+ *   out[r, h, :] = o * sigmoid(gate[r, h, :])   (gate NULL: o);
+ *   lse[r, h] = lse.  An empty P(r) gives out = 0 and lse = -inf.
+ * Ids whose page lies beyond the table, whose table entry is negative or
+ * whose slot is not below num_slots are skipped and set status bit 0.
+ *
+ * Layout (all device pointers, caller-owned): q, gate, out bf16 [rows,
+ * kv_heads * group, head_dim] contiguous; k_cache and v_cache bf16, element
+ * (slot, g, d) at slot * slot_stride + g * head_stride + d (strides in
+ * elements, multiples of 8, pointers 16-byte aligned); token_ids int32 [rows,
+ * k_tokens] contiguous (the selection's output: ascending, -1 pads, though any
+ * order works); page_table int32 [num_seqs, pages_per_seq] or NULL; lse fp32
+ * [rows, kv_heads * group] or NULL.  Inputs are bf16 codes, computation is
+ * fp32 with bf16 products on the matrix cores (the softmax weights are
+ * rounded to bf16 before they multiply V), the output is rounded to bf16.
+ *
+ * Limits: head_dim 128 or 256; group 1..16; kv_heads >= 1; page_size a power
+ * of two; num_slots < 2^31.
+ *
+ * dsa_sparse_attn enqueues one launch on `stream`, allocates nothing, never
+ * synchronizes and can be captured in a HIP graph.  When a row's tokens are
+ * split over several workgroups (chunks > 1), each writes a partial
+ * (maximum, sum, unnormalised output) to the context's workspace and the last
+ * one to arrive merges them; the arrival counters reset themselves, so calls
+ * on one context must be ordered on one stream.  Returns DSA_OK or a negative
+ * dsa_status (see dsa_select.h); the message is dsa_sparse_attn_last_error().
+ */
+#ifndef DSA_SPARSE_ATTN_H
+#define DSA_SPARSE_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#include "dsa_select.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dsa_attn_shape {
+  int32_t rows;           /* query rows, >= 0 */
+  int32_t kv_heads;       /* >= 1 */
+  int32_t group;          /* query heads per kv head, 1..16 */
+  int32_t head_dim;       /* 128 or 256 */
+  int32_t k_tokens;       /* ids per row, >= 1 */
+  int32_t rows_per_seq;   /* rows sharing one page-table row, >= 1 */
+  int32_t page_size;      /* power of two, >= 1 (ignored without a table) */
+  int32_t pages_per_seq;  /* page-table row length (ignored without a table) */
+  int64_t num_slots;      /* cache slots, < 2^31 */
+  int64_t k_slot_stride, k_head_stride;   /* elements */
+  int64_t v_slot_stride, v_head_stride;   /* elements */
+  int32_t chunks;         /* workgroups per (row, kv head); 0 = chosen at init */
+} dsa_attn_shape;
+
+typedef struct dsa_attn_ctx dsa_attn_ctx;
+
+/* Validates the shape, fixes the chunks per (row, kv head) from the shape
+ * and the device's CU count, and allocates and zeroes the workspace on
+ * `device` (not while capturing). */
+int dsa_sparse_attn_init(const dsa_attn_shape* shape, int device, dsa_attn_ctx** out);
+
+/* Frees the workspace (after the device finished using it). */
+int dsa_sparse_attn_destroy(dsa_attn_ctx* ctx);
+
+/* Chunks per (row, kv head) chosen at init (> 0), or a negative dsa_status. */
+int dsa_sparse_attn_chunks(const dsa_attn_ctx* ctx);
+
+int dsa_sparse_attn(dsa_attn_ctx* ctx, const uint16_t* q, const uint16_t* k_cache,
+                    const uint16_t* v_cache, const int32_t* token_ids,
+                    const int32_t* page_table, const uint16_t* gate, float sm_scale,
+                    uint16_t* out, float* lse, hipStream_t stream);
+
+/* Sticky status bits of the context (bit 0: some id was not addressable and
+ * was skipped).  Synchronizes the device; not for use under capture. */
+int dsa_sparse_attn_read_status(dsa_attn_ctx* ctx, uint32_t* status);
+
+/* Clears the status word (synchronous). */
+int dsa_sparse_attn_reset_status(dsa_attn_ctx* ctx);
+
+const char* dsa_sparse_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_SPARSE_ATTN_H */

@@ -33,6 +33,9 @@ EXPORTED = (
     "dsa_indexer_select", "dsa_indexer_last_error",
     "dsa_row_topk_init", "dsa_row_topk_destroy", "dsa_row_topk_pieces", "dsa_row_topk",
     "dsa_row_topk_last_error",
+    "dsa_sparse_attn_init", "dsa_sparse_attn_destroy", "dsa_sparse_attn_chunks",
+    "dsa_sparse_attn", "dsa_sparse_attn_read_status", "dsa_sparse_attn_reset_status",
+    "dsa_sparse_attn_last_error",
 )
 
 
@@ -78,6 +81,18 @@ class TopkShape(ctypes.Structure):
     ]
 
 
+class AttnShape(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("k_tokens", ctypes.c_int32),
+        ("rows_per_seq", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("pages_per_seq", ctypes.c_int32), ("num_slots", ctypes.c_int64),
+        ("k_slot_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
+        ("v_slot_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
+        ("chunks", ctypes.c_int32),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -117,6 +132,13 @@ def load() -> ctypes.CDLL:
         lib.dsa_row_topk_pieces.argtypes = [vp]
         lib.dsa_row_topk.argtypes = [vp, vp, vp, vp, vp, vp]
         lib.dsa_row_topk_last_error.restype = ctypes.c_char_p
+        lib.dsa_sparse_attn_init.argtypes = [ctypes.POINTER(AttnShape), i32, ctypes.POINTER(vp)]
+        lib.dsa_sparse_attn_destroy.argtypes = [vp]
+        lib.dsa_sparse_attn_chunks.argtypes = [vp]
+        lib.dsa_sparse_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+        lib.dsa_sparse_attn_read_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
+        lib.dsa_sparse_attn_reset_status.argtypes = [vp]
+        lib.dsa_sparse_attn_last_error.restype = ctypes.c_char_p
         lib.dsa_last_error.restype = ctypes.c_char_p
         for name in EXPORTED:
             if not name.endswith("last_error"):
@@ -446,6 +468,108 @@ class RowTopk:
     def close(self) -> None:
         if getattr(self, "_h", None) is not None and self._h.value:
             self._check(load().dsa_row_topk_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class SparseAttn:
+    """Sparse attention over each row's selected tokens (include/dsa_sparse_attn.h).
+
+    The caches are bf16 tensors [num_slots, kv_heads, head_dim] (any slot and
+    head strides that are multiples of 8 elements, innermost dimension
+    contiguous); q and gate are bf16 [rows, kv_heads * group, head_dim]."""
+
+    def __init__(self, rows: int, kv_heads: int, group: int, head_dim: int, k_tokens: int,
+                 num_slots: int, rows_per_seq: int = 1, page_size: int = 1,
+                 pages_per_seq: int = 0, k_strides=None, v_strides=None, chunks: int = 0,
+                 device: int = 0):
+        lib = load()
+        ks = (kv_heads * head_dim, head_dim) if k_strides is None else tuple(k_strides)
+        vs = (kv_heads * head_dim, head_dim) if v_strides is None else tuple(v_strides)
+        self.shape = AttnShape(rows, kv_heads, group, head_dim, k_tokens, rows_per_seq,
+                               page_size, pages_per_seq, num_slots, ks[0], ks[1], vs[0], vs[1],
+                               chunks)
+        self.device = device
+        h = ctypes.c_void_p()
+        self._check(lib.dsa_sparse_attn_init(ctypes.byref(self.shape), device, ctypes.byref(h)))
+        self._h = h
+
+    @staticmethod
+    def _check(rc: int) -> None:
+        if rc != 0:
+            raise DsaError(rc, load().dsa_sparse_attn_last_error().decode(errors="replace"))
+
+    def chunks(self) -> int:
+        n = load().dsa_sparse_attn_chunks(self._h)
+        if n < 0:
+            self._check(n)
+        return n
+
+    def read_status(self) -> int:
+        v = ctypes.c_uint32(0)
+        self._check(load().dsa_sparse_attn_read_status(self._h, ctypes.byref(v)))
+        return v.value
+
+    def reset_status(self) -> None:
+        self._check(load().dsa_sparse_attn_reset_status(self._h))
+
+    def __call__(self, q, k_cache, v_cache, token_ids, page_table=None, gate=None,
+                 sm_scale=None, out=None, lse=None, stream=None):
+        import torch
+        sh = self.shape
+        hq = sh.kv_heads * sh.group
+        D = sh.head_dim
+        for t, name in ((q, "q"), (gate, "gate")):
+            if t is None:
+                continue
+            if (t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous()
+                    or tuple(t.shape) != (sh.rows, hq, D)):
+                raise ValueError(f"{name} must be contiguous bf16 {(sh.rows, hq, D)}")
+        for t, name, st in ((k_cache, "k_cache", (sh.k_slot_stride, sh.k_head_stride)),
+                            (v_cache, "v_cache", (sh.v_slot_stride, sh.v_head_stride))):
+            if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3:
+                raise ValueError(f"{name} must be a 3-d bf16 device tensor")
+            if t.shape[0] < sh.num_slots or t.shape[1] != sh.kv_heads or t.shape[2] != D:
+                raise ValueError(f"{name} shape {tuple(t.shape)} does not hold "
+                                 f"{(sh.num_slots, sh.kv_heads, D)}")
+            if t.stride(2) != 1 or (t.stride(0), t.stride(1)) != st:
+                raise ValueError(f"{name} strides {t.stride()} differ from the context's {st}")
+        if (token_ids.dtype != torch.int32 or not token_ids.is_contiguous()
+                or tuple(token_ids.shape) != (sh.rows, sh.k_tokens)):
+            raise ValueError(f"token_ids must be contiguous int32 {(sh.rows, sh.k_tokens)}")
+        if page_table is not None:
+            nseq = -(-sh.rows // sh.rows_per_seq)
+            if (page_table.dtype != torch.int32 or not page_table.is_contiguous()
+                    or page_table.dim() != 2 or page_table.shape[0] < nseq
+                    or page_table.shape[1] != sh.pages_per_seq):
+                raise ValueError(f"page_table must be contiguous int32 [>= {nseq}, "
+                                 f"{sh.pages_per_seq}]")
+        if sm_scale is None:
+            sm_scale = 1.0 / (D ** 0.5)
+        if out is None:
+            out = torch.empty((sh.rows, hq, D), dtype=torch.bfloat16, device=q.device)
+        if (out.dtype != torch.bfloat16 or not out.is_contiguous()
+                or tuple(out.shape) != (sh.rows, hq, D)):
+            raise ValueError(f"out must be contiguous bf16 {(sh.rows, hq, D)}")
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                                or tuple(lse.shape) != (sh.rows, hq)):
+            raise ValueError(f"lse must be contiguous float32 {(sh.rows, hq)}")
+        if stream is None:
+            stream = torch.cuda.current_stream(self.device)
+        self._check(load().dsa_sparse_attn(
+            self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(token_ids), _ptr(page_table),
+            _ptr(gate), ctypes.c_float(sm_scale), _ptr(out), _ptr(lse),
+            ctypes.c_void_p(stream.cuda_stream)))
+        return out
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._check(load().dsa_sparse_attn_destroy(self._h))
             self._h = None
 
     def __del__(self):

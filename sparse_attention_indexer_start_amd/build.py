@@ -3,11 +3,12 @@
 Run ``python -m sparse_attention_indexer_start_amd.build`` (or call
 :func:`build`).  hipcc cross-compiles without a GPU.
 
-The library is linked from eleven objects compiled in parallel: the host unit
+The library is linked from twelve objects compiled in parallel: the host unit
 (``dsa_select.hip``: the C ABI and the block top-k kernel), the fused FP8
 indexer unit (``dsa_indexer.hip``), the cooperative row top-k unit
-(``dsa_row_topk.hip``) and one unit per specialised block size (``dsa_bs_unit.hip`` with ``-DDSA_BS=<size>``, 0 being
-the generic code for every other size).  Objects go to ``_build/`` beside the
+(``dsa_row_topk.hip``), the sparse attention unit (``dsa_sparse_attn.hip``)
+and one unit per specialised block size (``dsa_bs_unit.hip`` with
+``-DDSA_BS=<size>``, 0 being the generic code for every other size).  Objects go to ``_build/`` beside the
 sources' package.
 """
 from __future__ import annotations
@@ -31,11 +32,12 @@ HOST_SOURCE = os.path.join(CSRC, "dsa_select.hip")
 BS_SOURCE = os.path.join(CSRC, "dsa_bs_unit.hip")
 INDEXER_SOURCE = os.path.join(CSRC, "dsa_indexer.hip")
 ROW_TOPK_SOURCE = os.path.join(CSRC, "dsa_row_topk.hip")
+ATTN_SOURCE = os.path.join(CSRC, "dsa_sparse_attn.hip")
 BLOCK_SIZES = (0, 1, 2, 4, 8, 16, 32, 64)
-SOURCES = [HOST_SOURCE, BS_SOURCE, INDEXER_SOURCE, ROW_TOPK_SOURCE]
+SOURCES = [HOST_SOURCE, BS_SOURCE, INDEXER_SOURCE, ROW_TOPK_SOURCE, ATTN_SOURCE]
 HEADERS = [os.path.join(CSRC, "dsa_device.hpp"), os.path.join(CSRC, "dsa_kernels.hpp"),
            os.path.join(INCLUDE, "dsa_select.h"), os.path.join(INCLUDE, "dsa_indexer.h"),
-           os.path.join(INCLUDE, "dsa_row_topk.h")]
+           os.path.join(INCLUDE, "dsa_row_topk.h"), os.path.join(INCLUDE, "dsa_sparse_attn.h")]
 
 
 def hipcc() -> str:
@@ -63,7 +65,9 @@ def units(extra=()) -> list:
             # matrix-core results straight into VGPRs (no accumulator copies)
             [*_common(), *extra, "-mllvm", "-amdgpu-mfma-vgpr-form", "-c", INDEXER_SOURCE]),
            (os.path.join(BUILD_DIR, "dsa_row_topk.o"),
-            [*_common(), *extra, "-c", ROW_TOPK_SOURCE])]
+            [*_common(), *extra, "-c", ROW_TOPK_SOURCE]),
+           (os.path.join(BUILD_DIR, "dsa_sparse_attn.o"),
+            [*_common(), *extra, "-c", ATTN_SOURCE])]
     for bs in BLOCK_SIZES:
         out.append((os.path.join(BUILD_DIR, f"dsa_bs{bs}.o"),
                     [*_common(), *extra, f"-DDSA_BS={bs}", "-c", BS_SOURCE]))

@@ -1,0 +1,553 @@
+// Sparse attention over each query row's selected tokens (MI355X, gfx950).
+//
+// The page on vllm PR #57273 ("Qwen4Exp QSA: sm_90 tuning table", Purpose)
+// describes the consumer of the selection: grouped-query attention of each
+// query over its 2048 selected tokens, read from a paged bf16 K/V cache,
+// split over several programs and merged, with a fused output gate.  The page
+// on vllm PR #48726 ("LiteDSA: grouped masked sparse attention") requires the
+// attention to stay query-exact and reports the log-sum-exp beside the output.
+//
+// Work unit: one workgroup of four waves per (row, kv head, chunk), a chunk
+// being a run of 32-token steps of the row's id list; wave w takes steps w,
+// w + 4, ...  Per step a wave gathers 32 tokens' K and V rows straight from
+// the cache into registers, already in the layout of the matrix instructions
+// (no LDS): S^T = K Q^T on v_mfma_f32_16x16x32_bf16 gives each lane one
+// query head (lane % 16) and eight tokens, which is both the layout of the
+// online softmax (one head per lane, a maximum over the four 16-lane groups)
+// and the B operand of O^T = V^T P^T.  The V operand needs eight tokens of one
+// dimension per lane; lanes load 16-byte pieces (eight dimensions of one
+// token) and byte permutes regroup them.  The four waves merge through LDS;
+// with one chunk the workgroup writes the gated bf16 output and the LSE, else
+// it writes a partial (maximum, sum, unnormalised output) and the last
+// workgroup of the (row, kv head) to arrive merges the partials.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "dsa_sparse_attn.h"
+
+#define SA_DEV __device__ __forceinline__
+
+namespace dsa {
+namespace sa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVES = 4;
+constexpr int NT = 64 * WAVES;
+constexpr int STEP = 32;          // tokens per wave step
+constexpr int GMAX = 16;          // query heads per kv head (one matrix tile)
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+struct Args {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* ids;
+  const int32_t* table;
+  const uint16_t* gate;
+  uint16_t* out;
+  float* lse;
+  float* part_o;        // [pairs * chunks][G][D]
+  float* part_ml;       // [pairs * chunks][G][2]
+  uint32_t* tickets;    // [pairs]
+  uint32_t* status;
+  int64_t k_ss, k_hs, v_ss, v_hs, num_slots;
+  int32_t rows, hkv, G, K, rows_per_seq, page_shift, pps, chunks, spc;
+  float c2;             // sm_scale * log2(e)
+};
+
+SA_DEV uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Cache slot of position `pos` of sequence `seq`; -1 for padding (pos < 0) and
+// for positions that are not addressable (`bad` is then set).
+SA_DEV int slot_of(const Args& a, int seq, int pos, bool& bad) {
+  if (pos < 0) return -1;
+  int64_t slot = pos;
+  if (a.table) {
+    const int page = pos >> a.page_shift;
+    if (page >= a.pps) { bad = true; return -1; }
+    const int phys = a.table[(int64_t)seq * a.pps + page];
+    if (phys < 0) { bad = true; return -1; }
+    slot = ((int64_t)phys << a.page_shift) | (pos & ((1 << a.page_shift) - 1));
+  }
+  if (slot >= a.num_slots) { bad = true; return -1; }
+  return (int)slot;
+}
+
+// Agent-scope relaxed 64-bit accesses for words one workgroup writes and
+// another reads: they compile to coherent loads and stores on gfx950, across
+// the XCDs' separate L2 caches.
+SA_DEV void st_coh64(float* p, float x, float y) {
+  const uint64_t v = (uint64_t)__float_as_uint(x) | ((uint64_t)__float_as_uint(y) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+SA_DEV float2 ld_coh64(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+SA_DEV uint32_t word_of(const uint4 x, int k) {
+  return k == 0 ? x.x : k == 1 ? x.y : k == 2 ? x.z : x.w;
+}
+
+SA_DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to bf16, nearest even (inputs are finite or +-inf).
+SA_DEV uint32_t f2bf(float f) {
+  const __bf16 h = (__bf16)f;
+  return (uint32_t)__builtin_bit_cast(unsigned short, h);
+}
+
+template <int D>
+struct __align__(16) Smem {
+  float o[WAVES][GMAX][D];
+  float m[WAVES][GMAX];
+  float l[WAVES][GMAX];
+  uint32_t last;
+};
+
+// Normalise, gate and store four consecutive dimensions of one head.
+SA_DEV void store_out(const Args& a, int row, int h, int d, float4 o, float L, float M, int D) {
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float v[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
+  const int hq = a.hkv * a.G;
+  const int64_t base = ((int64_t)row * hq + h) * D + d;
+  if (a.gate) {
+    const uint2 g = *reinterpret_cast<const uint2*>(a.gate + base);
+    const float gv[4] = {bf2f(g.x & 0xFFFFu), bf2f(g.x >> 16), bf2f(g.y & 0xFFFFu), bf2f(g.y >> 16)};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = v[i] / (1.f + __expf(-gv[i]));
+  }
+  uint2 w;
+  w.x = f2bf(v[0]) | (f2bf(v[1]) << 16);
+  w.y = f2bf(v[2]) | (f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2*>(a.out + base) = w;
+  if (d == 0 && a.lse)
+    a.lse[(int64_t)row * hq + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : NEG_INF;
+}
+
+template <int D>
+__global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
+  constexpr int KS = D / 32;      // 32-dimension steps of q.k
+  constexpr int NC = D / 128;     // 128-dimension halves of V
+  constexpr int OT = D / 16;      // 16-dimension output tiles
+  __shared__ Smem<D> sm;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int pair = blockIdx.x / a.chunks, chunk = blockIdx.x - pair * a.chunks;
+  const int row = pair / a.hkv, g = pair - row * a.hkv;
+  const int seq = row / a.rows_per_seq;
+  const int hq = a.hkv * a.G;
+
+  // Query operand: lane (head n, group j) holds q[row, g*G + n, 32s + 8j .. +8].
+  uint4 qr[KS];
+  {
+    const uint16_t* qp = a.q + ((int64_t)row * hq + g * a.G + min(n, a.G - 1)) * D + 8 * j;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qr[s] = n < a.G ? ld16(qp + 32 * s) : make_uint4(0, 0, 0, 0);
+  }
+  f32x4 oacc[OT];
+#pragma unroll
+  for (int t = 0; t < OT; ++t) oacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = NEG_INF, l_run = 0.f;
+  bool bad = false;
+
+  const int steps = (a.K + STEP - 1) / STEP;
+  const int st0 = chunk * a.spc, st1 = min(steps, st0 + a.spc);
+  const int32_t* idrow = a.ids + (int64_t)row * a.K;
+  const uint16_t* kbase = a.kc + (int64_t)g * a.k_hs;
+  const uint16_t* vbase = a.vc + (int64_t)g * a.v_hs;
+
+  for (int st = st0 + w; st < st1; st += WAVES) {
+    const int tix = st * STEP + (lane & 31);
+    const int slot = tix < a.K ? slot_of(a, seq, idrow[tix], bad) : -1;
+    if (__ballot(slot >= 0) == 0) continue;       // nothing to attend in this step
+    // Slots of this lane's tokens: K rows n and 16 + n; V and score tokens
+    // 4j + e and 16 + 4j + e (e < 4).
+    const int sk0 = __shfl(slot, n), sk1 = __shfl(slot, 16 + n);
+    int sv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv[e] = __shfl(slot, 4 * j + e);
+      sv[4 + e] = __shfl(slot, 16 + 4 * j + e);
+    }
+    uint4 ka[KS], kb[KS];
+    {
+      const uint16_t* p0 = kbase + (int64_t)max(sk0, 0) * a.k_ss + 8 * j;
+      const uint16_t* p1 = kbase + (int64_t)max(sk1, 0) * a.k_ss + 8 * j;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        ka[s] = sk0 >= 0 ? ld16(p0 + 32 * s) : make_uint4(0, 0, 0, 0);
+        kb[s] = sk1 >= 0 ? ld16(p1 + 32 * s) : make_uint4(0, 0, 0, 0);
+      }
+    }
+    uint4 vq[8][NC];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t* vp = vbase + (int64_t)max(sv[e], 0) * a.v_ss + 8 * n;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vq[e][c] = sv[e] >= 0 ? ld16(vp + 128 * c) : make_uint4(0, 0, 0, 0);
+    }
+    // Scores S^T[token][head]: lane (n, j) receives tokens 4j + r and 16 + 4j + r.
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]),
+                                                   __builtin_bit_cast(bf16x8, qr[s]), s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[s]),
+                                                   __builtin_bit_cast(bf16x8, qr[s]), s1, 0, 0, 0);
+    }
+    float sc[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sc[r] = sv[r] >= 0 ? s0[r] * a.c2 : NEG_INF;
+      sc[4 + r] = sv[4 + r] >= 0 ? s1[r] * a.c2 : NEG_INF;
+    }
+    float tmax = sc[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sc[e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == NEG_INF ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(sc[e] - m_use);
+      psum += p[e];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int t = 0; t < OT; ++t) oacc[t] *= alpha;
+    }
+    uint4 pw;
+    pw.x = f2bf(p[0]) | (f2bf(p[1]) << 16);
+    pw.y = f2bf(p[2]) | (f2bf(p[3]) << 16);
+    pw.z = f2bf(p[4]) | (f2bf(p[5]) << 16);
+    pw.w = f2bf(p[6]) | (f2bf(p[7]) << 16);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+    // O^T[dim][head] += V^T P^T.  Tile (c, i) holds dimensions 128c + 8m + i
+    // (m = row of the tile); its A operand on lane (m = n, j) is the eight
+    // tokens' values of dimension 128c + 8n + i, regrouped from vq.
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        // bf16 of dimension i: low half of word i/2 (i even) or high half (i odd)
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        uint4 av;
+        av.x = __builtin_amdgcn_perm(word_of(vq[1][c], i >> 1), word_of(vq[0][c], i >> 1), sel);
+        av.y = __builtin_amdgcn_perm(word_of(vq[3][c], i >> 1), word_of(vq[2][c], i >> 1), sel);
+        av.z = __builtin_amdgcn_perm(word_of(vq[5][c], i >> 1), word_of(vq[4][c], i >> 1), sel);
+        av.w = __builtin_amdgcn_perm(word_of(vq[7][c], i >> 1), word_of(vq[6][c], i >> 1), sel);
+        oacc[c * 8 + i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, av), pb, oacc[c * 8 + i], 0, 0, 0);
+      }
+    }
+  }
+  if (__ballot(bad) && lane == 0) atomicOr(a.status, 1u);
+
+  // Merge the four waves through LDS.  Lane (n, j) holds, for tile (c, i) and
+  // element r, head n and dimension 128c + 8(4j + r) + i.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (n < a.G) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float* dst = &sm.o[w][n][128 * c + 32 * j + 8 * r];
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(oacc[c * 8 + 0][r], oacc[c * 8 + 1][r], oacc[c * 8 + 2][r], oacc[c * 8 + 3][r]);
+        *reinterpret_cast<float4*>(dst + 4) =
+            make_float4(oacc[c * 8 + 4][r], oacc[c * 8 + 5][r], oacc[c * 8 + 6][r], oacc[c * 8 + 7][r]);
+      }
+    if (j == 0) {
+      sm.m[w][n] = m_run;
+      sm.l[w][n] = l_run;
+    }
+  }
+  __syncthreads();
+
+  constexpr int D4 = D / 4;
+  const int n4 = a.G * D4;
+  const int unit = pair * a.chunks + chunk;
+  for (int e = threadIdx.x; e < n4; e += NT) {
+    const int h = e / D4, d = (e - h * D4) * 4;
+    float M = NEG_INF;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sm.m[v][h]);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) {
+      const float f = sm.m[v][h] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(sm.m[v][h] - M);
+      L += sm.l[v][h] * f;
+      const float4 x = *reinterpret_cast<const float4*>(&sm.o[v][h][d]);
+      o.x += x.x * f; o.y += x.y * f; o.z += x.z * f; o.w += x.w * f;
+    }
+    if (a.chunks == 1) {
+      store_out(a, row, g * a.G + h, d, o, L, M, D);
+    } else {
+      float* po = a.part_o + ((int64_t)unit * a.G + h) * D + d;
+      st_coh64(po, o.x, o.y);
+      st_coh64(po + 2, o.z, o.w);
+      if (d == 0) st_coh64(a.part_ml + ((int64_t)unit * a.G + h) * 2, M, L);
+    }
+  }
+  if (a.chunks == 1) return;
+
+  // Last of the (row, kv head)'s chunks to arrive merges the partials.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) sm.last = atomicAdd(&a.tickets[pair], 1u) == (uint32_t)(a.chunks - 1);
+  __syncthreads();
+  if (!sm.last) return;
+  const int u0 = pair * a.chunks;
+  for (int e = threadIdx.x; e < n4; e += NT) {
+    const int h = e / D4, d = (e - h * D4) * 4;
+    float M = NEG_INF;
+    for (int ch = 0; ch < a.chunks; ++ch)
+      M = fmaxf(M, ld_coh64(a.part_ml + ((int64_t)(u0 + ch) * a.G + h) * 2).x);
+    float L = 0.f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int ch = 0; ch < a.chunks; ++ch) {
+      const float2 ml = ld_coh64(a.part_ml + ((int64_t)(u0 + ch) * a.G + h) * 2);
+      const float f = ml.x == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+      L += ml.y * f;
+      const float* po = a.part_o + ((int64_t)(u0 + ch) * a.G + h) * D + d;
+      const float2 x0 = ld_coh64(po), x1 = ld_coh64(po + 2);
+      o.x += x0.x * f; o.y += x0.y * f; o.z += x1.x * f; o.w += x1.y * f;
+    }
+    store_out(a, row, g * a.G + h, d, o, L, M, D);
+  }
+  if (threadIdx.x == 0)
+    __hip_atomic_store(&a.tickets[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace sa
+}  // namespace dsa
+
+// ===========================================================================
+// Host side
+// ===========================================================================
+using namespace dsa::sa;
+
+struct dsa_attn_ctx {
+  dsa_attn_shape sh;
+  int device;
+  int chunks, spc;
+  void* ws;
+  size_t ws_bytes;
+  float *part_o, *part_ml;
+  uint32_t *tickets, *status;
+  uint32_t magic;
+};
+
+namespace {
+
+constexpr uint32_t SA_MAGIC = 0x44534154u;
+thread_local std::string g_sa_err;
+
+int sa_fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_sa_err = buf;
+  return code;
+}
+
+int sa_hip(hipError_t e, const char* what) {
+  return sa_fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+struct DeviceScope {
+  int prev = -1;
+  bool switched = false;
+  hipError_t e = hipSuccess;
+  explicit DeviceScope(int device) {
+    e = hipGetDevice(&prev);
+    if (e == hipSuccess && prev != device) {
+      e = hipSetDevice(device);
+      switched = e == hipSuccess;
+    }
+  }
+  ~DeviceScope() {
+    if (switched) (void)hipSetDevice(prev);
+  }
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_sparse_attn_last_error(void) { return g_sa_err.c_str(); }
+
+int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out) {
+  if (!out) return sa_fail(DSA_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  if (!s) return sa_fail(DSA_ERR_INVALID_ARG, "shape is null");
+  if (s->rows < 0) return sa_fail(DSA_ERR_INVALID_ARG, "rows must be >= 0");
+  if (s->kv_heads < 1) return sa_fail(DSA_ERR_INVALID_ARG, "kv_heads must be >= 1");
+  if (s->group < 1 || s->group > GMAX)
+    return sa_fail(DSA_ERR_UNSUPPORTED, "group must be in 1..%d (got %d)", GMAX, s->group);
+  if (s->head_dim != 128 && s->head_dim != 256)
+    return sa_fail(DSA_ERR_UNSUPPORTED, "head_dim must be 128 or 256 (got %d)", s->head_dim);
+  if (s->k_tokens < 1) return sa_fail(DSA_ERR_INVALID_ARG, "k_tokens must be >= 1");
+  if (s->rows_per_seq < 1) return sa_fail(DSA_ERR_INVALID_ARG, "rows_per_seq must be >= 1");
+  if (s->page_size < 1 || (s->page_size & (s->page_size - 1)) || s->page_size > (1 << 24))
+    return sa_fail(DSA_ERR_INVALID_ARG, "page_size must be a power of two in [1, 2^24]");
+  if (s->pages_per_seq < 0) return sa_fail(DSA_ERR_INVALID_ARG, "pages_per_seq must be >= 0");
+  if (s->num_slots < 0 || s->num_slots >= ((int64_t)1 << 31))
+    return sa_fail(DSA_ERR_UNSUPPORTED, "num_slots must be in [0, 2^31)");
+  const int64_t D = s->head_dim;
+  if (s->k_slot_stride % 8 || s->k_head_stride % 8 || s->v_slot_stride % 8 || s->v_head_stride % 8)
+    return sa_fail(DSA_ERR_INVALID_ARG, "cache strides must be multiples of 8 elements");
+  if (s->k_head_stride < D || s->v_head_stride < D ||
+      s->k_slot_stride < (s->kv_heads - 1) * s->k_head_stride + D ||
+      s->v_slot_stride < (s->kv_heads - 1) * s->v_head_stride + D)
+    return sa_fail(DSA_ERR_INVALID_ARG, "cache strides overlap heads or slots");
+  if (s->chunks < 0) return sa_fail(DSA_ERR_INVALID_ARG, "chunks must be >= 0");
+  const int64_t pairs = (int64_t)s->rows * s->kv_heads;
+  if (pairs > ((int64_t)1 << 30)) return sa_fail(DSA_ERR_UNSUPPORTED, "too many rows");
+  if (device < 0) return sa_fail(DSA_ERR_INVALID_ARG, "device must be >= 0");
+  DeviceScope ds(device);
+  if (ds.e != hipSuccess) return sa_hip(ds.e, "hipSetDevice");
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return sa_hip(e, "hipDeviceGetAttribute(CU count)");
+
+  dsa_attn_ctx* c = new (std::nothrow) dsa_attn_ctx;
+  if (!c) return sa_fail(DSA_ERR_HIP, "host allocation failed");
+  std::memset(c, 0, sizeof(*c));
+  c->sh = *s;
+  c->device = device;
+  c->magic = SA_MAGIC;
+  // Chunks per (row, kv head): enough workgroups for two per CU over all
+  // pairs, each chunk at least one step per wave.
+  const int64_t steps = (s->k_tokens + STEP - 1) / STEP;
+  const int64_t maxc = std::max<int64_t>(1, steps / WAVES);
+  int64_t ch = s->chunks > 0 ? s->chunks
+                             : (2 * (int64_t)cus + std::max<int64_t>(pairs, 1) - 1) / std::max<int64_t>(pairs, 1);
+  ch = std::max<int64_t>(1, std::min<int64_t>(ch, s->chunks > 0 ? steps : maxc));
+  const int64_t spc = (steps + ch - 1) / ch;
+  ch = (steps + spc - 1) / spc;
+  if (pairs * ch > ((int64_t)1 << 31) - 1) { delete c; return sa_fail(DSA_ERR_UNSUPPORTED, "grid too large"); }
+  c->chunks = (int)ch;
+  c->spc = (int)spc;
+  const int64_t units = ch > 1 ? pairs * ch : 0;
+  const int64_t floats = units * s->group * (D + 2);
+  c->ws_bytes = (size_t)floats * 4 + (size_t)(pairs + 1) * 4 + 256;
+  e = hipMalloc(&c->ws, c->ws_bytes);
+  if (e != hipSuccess) { delete c; return sa_hip(e, "hipMalloc(workspace)"); }
+  e = hipMemset(c->ws, 0, c->ws_bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) { (void)hipFree(c->ws); delete c; return sa_hip(e, "hipMemset(workspace)"); }
+  float* f = static_cast<float*>(c->ws);
+  c->part_o = f;
+  c->part_ml = f + units * s->group * D;
+  c->tickets = reinterpret_cast<uint32_t*>(c->part_ml + units * s->group * 2);
+  c->status = c->tickets + pairs;
+  *out = c;
+  return DSA_OK;
+}
+
+int dsa_sparse_attn_destroy(dsa_attn_ctx* c) {
+  if (!c || c->magic != SA_MAGIC) return sa_fail(DSA_ERR_INVALID_ARG, "bad context");
+  c->magic = 0;
+  int rc = DSA_OK;
+  if (c->ws) {
+    DeviceScope ds(c->device);
+    const hipError_t e = hipFree(c->ws);
+    if (e != hipSuccess) rc = sa_hip(e, "hipFree(workspace)");
+  }
+  delete c;
+  return rc;
+}
+
+int dsa_sparse_attn_chunks(const dsa_attn_ctx* c) {
+  if (!c || c->magic != SA_MAGIC) return sa_fail(DSA_ERR_INVALID_ARG, "bad context");
+  return c->chunks;
+}
+
+int dsa_sparse_attn(dsa_attn_ctx* c, const uint16_t* q, const uint16_t* k_cache,
+                    const uint16_t* v_cache, const int32_t* token_ids,
+                    const int32_t* page_table, const uint16_t* gate, float sm_scale,
+                    uint16_t* out, float* lse, hipStream_t stream) {
+  if (!c || c->magic != SA_MAGIC) return sa_fail(DSA_ERR_INVALID_ARG, "bad context");
+  const dsa_attn_shape& s = c->sh;
+  if (s.rows == 0) return DSA_OK;
+  if (!q || !k_cache || !v_cache || !token_ids || !out)
+    return sa_fail(DSA_ERR_INVALID_ARG, "q, k_cache, v_cache, token_ids and out must be non-null");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)out & 7u) ||
+      (gate && ((uintptr_t)gate & 7u)))
+    return sa_fail(DSA_ERR_INVALID_ARG, "q and the caches must be 16-byte aligned, out and gate 8-byte aligned");
+  if (page_table && s.pages_per_seq < 1)
+    return sa_fail(DSA_ERR_INVALID_ARG, "a page table needs pages_per_seq >= 1");
+  if (!std::isfinite(sm_scale)) return sa_fail(DSA_ERR_INVALID_ARG, "sm_scale must be finite");
+  DeviceScope ds(c->device);
+  if (ds.e != hipSuccess) return sa_hip(ds.e, "hipSetDevice");
+  Args a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.ids = token_ids; a.table = page_table;
+  a.gate = gate; a.out = out; a.lse = lse;
+  a.part_o = c->part_o; a.part_ml = c->part_ml; a.tickets = c->tickets; a.status = c->status;
+  a.k_ss = s.k_slot_stride; a.k_hs = s.k_head_stride;
+  a.v_ss = s.v_slot_stride; a.v_hs = s.v_head_stride; a.num_slots = s.num_slots;
+  a.rows = s.rows; a.hkv = s.kv_heads; a.G = s.group; a.K = s.k_tokens;
+  a.rows_per_seq = s.rows_per_seq;
+  int shift = 0;
+  while ((1 << shift) < s.page_size) ++shift;
+  a.page_shift = shift;
+  a.pps = s.pages_per_seq;
+  a.chunks = c->chunks; a.spc = c->spc;
+  a.c2 = sm_scale * 1.4426950408889634f;
+  const unsigned grid = (unsigned)((int64_t)s.rows * s.kv_heads * c->chunks);
+  if (s.head_dim == 256)
+    hipLaunchKernelGGL(k_sparse_attn<256>, dim3(grid), dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_sparse_attn<128>, dim3(grid), dim3(NT), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return sa_hip(e, "launch k_sparse_attn");
+  return DSA_OK;
+}
+
+int dsa_sparse_attn_read_status(dsa_attn_ctx* c, uint32_t* status) {
+  if (!c || c->magic != SA_MAGIC || !status) return sa_fail(DSA_ERR_INVALID_ARG, "bad context or status");
+  DeviceScope ds(c->device);
+  if (ds.e != hipSuccess) return sa_hip(ds.e, "hipSetDevice");
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(status, c->status, 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return sa_hip(e, "read status");
+  return DSA_OK;
+}
+
+int dsa_sparse_attn_reset_status(dsa_attn_ctx* c) {
+  if (!c || c->magic != SA_MAGIC) return sa_fail(DSA_ERR_INVALID_ARG, "bad context");
+  DeviceScope ds(c->device);
+  if (ds.e != hipSuccess) return sa_hip(ds.e, "hipSetDevice");
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemset(c->status, 0, 4);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return sa_hip(e, "reset status");
+  return DSA_OK;
+}
+
+}  // extern "C"
