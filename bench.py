@@ -14,8 +14,11 @@ launch stream; ms_per_step is the events' time over K.  The roofline
 fraction divides the algorithmic bytes of one call (4*L read per row, the
 -inf stores, the index stores and 8 bytes of bounds per row) by ms_per_step.
 The same run also times the long-decode workload (32 rows x 1M width, the
-bandwidth-bound case) under the key "long_decode", and the C oracle is timed
-on all host threads over whole passes of the default workload.
+bandwidth-bound case) under the key "long_decode", the fused FP8 indexer on a
+prefill chunk ("indexer_prefill"), the cooperative top-k of 16M-column rows
+("row_topk") and the sparse attention over the selected tokens at decode
+("sparse_attn"), and the C oracle is timed on all host threads over whole
+passes of the default workload.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one GPU.
 """
@@ -311,6 +314,88 @@ def run_row_topk(rows: int, width: int, k: int, steps: int, warmup: int) -> dict
                                    "times: three digit passes, count, emit)"})
 
 
+def attn_device_caches(case):
+    """K/V caches of a configuration, drawn on the device (bf16 N(0, 1))."""
+    import torch
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(int(case.cache_seed))
+    shape = (case.num_slots, case.kv_heads, case.head_dim)
+    k = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    v = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+    return k, v
+
+
+def run_attn(name: str, steps: int, warmup: int) -> dict:
+    """Graph replay of `steps` sparse-attention calls over a configuration."""
+    import numpy as np
+    import torch
+    from sparse_attention_indexer_start_amd import binding
+    from sparse_attention_indexer_start_amd import workloads as wl
+
+    log(f"{name}: generating")
+    case = wl.make_attn_config(name)
+    dev = torch.device("cuda", 0)
+    kd, vd = attn_device_caches(case)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    q, gate = bf(case.q), bf(case.gate)
+    ids = torch.from_numpy(case.token_ids).to(dev)
+    table = torch.from_numpy(case.page_table).to(dev)
+    hq = case.kv_heads * case.group
+    out = torch.empty((case.rows, hq, case.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((case.rows, hq), dtype=torch.float32, device=dev)
+    op = binding.SparseAttn(case.rows, case.kv_heads, case.group, case.head_dim, case.k_tokens,
+                            case.num_slots, rows_per_seq=case.rows_per_seq,
+                            page_size=case.page_size, pages_per_seq=case.page_table.shape[1])
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        op(q, kd, vd, ids, table, gate, case.sm_scale, out, lse)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            call()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    status = op.read_status()
+    chunks = op.chunks()
+    op.close()
+    if status != 0:
+        raise RuntimeError(f"{name}: status word {status} after the timed calls")
+    n_valid = int((case.token_ids >= 0).sum())
+    D = case.head_dim
+    gathered = n_valid * case.kv_heads * D * 2 * 2
+    per_row = case.rows * (hq * D * 2 * 3 + case.k_tokens * 4 + hq * 4)
+    alg = gathered + per_row
+    achieved = alg / (ms * 1e-3) / 1e9
+    del kd, vd
+    torch.cuda.empty_cache()
+    return dict(
+        ms_per_step=ms, rows_per_s=case.rows / (ms * 1e-3),
+        config={"workload": name, "rows": case.rows, "rows_per_seq": case.rows_per_seq,
+                "kv_heads": case.kv_heads, "group": case.group, "head_dim": D,
+                "k_tokens": case.k_tokens, "page_size": case.page_size, "gate": True,
+                "chunks": chunks, "dtype": "bf16 in, fp32 accumulate, bf16 out",
+                "graph": True},
+        attended_tokens_per_call=n_valid, alg_bytes_per_call=alg,
+        roofline={"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                  "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                  "basis": "K and V rows of every attended token (2 * kv_heads * head_dim "
+                           "bf16 each) + q, gate and out (bf16) + ids + lse, over the graph "
+                           "replay's time per call; page-table reads not counted"},
+    )
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -335,6 +420,10 @@ def main() -> int:
                     help="do not also time the cooperative row top-k (16M-column rows)")
     ap.add_argument("--row-topk-only", action="store_true",
                     help="time only the cooperative row top-k")
+    ap.add_argument("--no-attn", action="store_true",
+                    help="do not also time the sparse attention over the selected tokens")
+    ap.add_argument("--attn-only", action="store_true",
+                    help="time only the sparse attention")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -359,6 +448,11 @@ def main() -> int:
               for kk in (2048, 2**20)]
         print(json.dumps({"row_topk": rt}), flush=True)
         return 0
+    if args.attn_only:
+        at = [run_attn(n, min(args.steps, 20), min(args.warmup, 2))
+              for n in ("attn_decode", "attn_c1")]
+        print(json.dumps({"sparse_attn": at}), flush=True)
+        return 0
     if args.indexer_only:
         ix = run_indexer("indexer_prefill", min(args.steps, 10), min(args.warmup, 2))
         print(json.dumps({"indexer_prefill": ix}), flush=True)
@@ -379,6 +473,11 @@ def main() -> int:
     if not args.no_row_topk and args.width is None:
         row_topk = [run_row_topk(1, 16 * 2**20, kk, min(args.steps, 20), min(args.warmup, 2))
                     for kk in (2048, 2**20)]
+
+    attn = None
+    if not args.no_attn and args.width is None:
+        attn = [run_attn(n, min(args.steps, 20), min(args.warmup, 2))
+                for n in ("attn_decode", "attn_c1")]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -420,6 +519,8 @@ def main() -> int:
         out["indexer_prefill"] = indexer
     if row_topk is not None:
         out["row_topk"] = row_topk
+    if attn is not None:
+        out["sparse_attn"] = attn
     print(json.dumps(out), flush=True)
     return 0
 

@@ -7,9 +7,11 @@
 // on vllm PR #48726 ("LiteDSA: grouped masked sparse attention") requires the
 // attention to stay query-exact and reports the log-sum-exp beside the output.
 //
-// Work unit: one workgroup of four waves per (row, kv head, chunk), a chunk
-// being a run of 32-token steps of the row's id list; wave w takes steps w,
-// w + 4, ...  Per step a wave gathers 32 tokens' K and V rows straight from
+// Work unit: one workgroup of four waves per (row, group of 1, 2 or 4 kv
+// heads, chunk), a chunk being a run of 32-token steps of the row's id list;
+// the waves of one kv head share the steps (with one kv head per workgroup,
+// wave w takes steps w, w + 4, ...), so the waves of different heads read the
+// same tokens at once.  Per step a wave gathers 32 tokens' K and V rows straight from
 // the cache into registers, already in the layout of the matrix instructions
 // (no LDS): S^T = K Q^T on v_mfma_f32_16x16x32_bf16 gives each lane one
 // query head (lane % 16) and eight tokens, which is both the layout of the
@@ -57,10 +59,11 @@ struct Args {
   float* lse;
   float* part_o;        // [pairs * chunks][G][D]
   float* part_ml;       // [pairs * chunks][G][2]
-  uint32_t* tickets;    // [pairs]
+  uint32_t* tickets;    // [rows * hkv / hw]
   uint32_t* status;
   int64_t k_ss, k_hs, v_ss, v_hs, num_slots;
   int32_t rows, hkv, G, K, rows_per_seq, page_shift, pps, chunks, spc;
+  int32_t hw;           // kv heads per workgroup (1, 2 or 4; divides hkv)
   float c2;             // sm_scale * log2(e)
 };
 
@@ -144,8 +147,24 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, j = lane >> 4;
-  const int pair = blockIdx.x / a.chunks, chunk = blockIdx.x - pair * a.chunks;
-  const int row = pair / a.hkv, g = pair - row * a.hkv;
+  // Workgroups are dealt to the eight XCDs in turn (block b to XCD b % 8).
+  // XCD x takes the x-th contiguous eighth of the work units instead, so the
+  // rows of one sequence (and their cache pages) share one XCD's L2 and
+  // address-translation caches.
+  int unit;
+  {
+    const int nb = gridDim.x, per = nb >> 3, rem = nb & 7;
+    const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+    unit = x * per + min(x, rem) + k;
+  }
+  // A workgroup covers hw kv heads of one row over one chunk: wave w works
+  // on kv head gb*hw + w % hw, and the waves of one head share the chunk's
+  // steps, so the waves of different heads read the same tokens' cache rows
+  // (the same pages) at the same time.
+  const int gblocks = a.hkv / a.hw, wph = WAVES / a.hw;
+  const int wgp = unit / a.chunks, chunk = unit - wgp * a.chunks;
+  const int row = wgp / gblocks, gb = wgp - row * gblocks;
+  const int g = gb * a.hw + w % a.hw, wi = w / a.hw;
   const int seq = row / a.rows_per_seq;
   const int hq = a.hkv * a.G;
 
@@ -168,7 +187,7 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   const uint16_t* kbase = a.kc + (int64_t)g * a.k_hs;
   const uint16_t* vbase = a.vc + (int64_t)g * a.v_hs;
 
-  for (int st = st0 + w; st < st1; st += WAVES) {
+  for (int st = st0 + wi; st < st1; st += wph) {
     const int tix = st * STEP + (lane & 31);
     const int slot = tix < a.K ? slot_of(a, seq, idrow[tix], bad) : -1;
     if (__ballot(slot >= 0) == 0) continue;       // nothing to attend in this step
@@ -284,28 +303,28 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
 
   constexpr int D4 = D / 4;
   const int n4 = a.G * D4;
-  const int unit = pair * a.chunks + chunk;
-  for (int e = threadIdx.x; e < n4; e += NT) {
-    const int h = e / D4, d = (e - h * D4) * 4;
+  for (int e = threadIdx.x; e < a.hw * n4; e += NT) {
+    const int gl = e / n4, e2 = e - gl * n4;
+    const int h = e2 / D4, d = (e2 - h * D4) * 4;
+    const int gh = gb * a.hw + gl;
     float M = NEG_INF;
-#pragma unroll
-    for (int v = 0; v < WAVES; ++v) M = fmaxf(M, sm.m[v][h]);
+    for (int v = gl; v < WAVES; v += a.hw) M = fmaxf(M, sm.m[v][h]);
     float L = 0.f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int v = 0; v < WAVES; ++v) {
+    for (int v = gl; v < WAVES; v += a.hw) {
       const float f = sm.m[v][h] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(sm.m[v][h] - M);
       L += sm.l[v][h] * f;
       const float4 x = *reinterpret_cast<const float4*>(&sm.o[v][h][d]);
       o.x += x.x * f; o.y += x.y * f; o.z += x.z * f; o.w += x.w * f;
     }
     if (a.chunks == 1) {
-      store_out(a, row, g * a.G + h, d, o, L, M, D);
+      store_out(a, row, gh * a.G + h, d, o, L, M, D);
     } else {
-      float* po = a.part_o + ((int64_t)unit * a.G + h) * D + d;
+      const int64_t pu = ((int64_t)row * a.hkv + gh) * a.chunks + chunk;
+      float* po = a.part_o + (pu * a.G + h) * D + d;
       st_coh64(po, o.x, o.y);
       st_coh64(po + 2, o.z, o.w);
-      if (d == 0) st_coh64(a.part_ml + ((int64_t)unit * a.G + h) * 2, M, L);
+      if (d == 0) st_coh64(a.part_ml + (pu * a.G + h) * 2, M, L);
     }
   }
   if (a.chunks == 1) return;
@@ -313,12 +332,14 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   // Last of the (row, kv head)'s chunks to arrive merges the partials.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) sm.last = atomicAdd(&a.tickets[pair], 1u) == (uint32_t)(a.chunks - 1);
+  if (threadIdx.x == 0) sm.last = atomicAdd(&a.tickets[wgp], 1u) == (uint32_t)(a.chunks - 1);
   __syncthreads();
   if (!sm.last) return;
-  const int u0 = pair * a.chunks;
-  for (int e = threadIdx.x; e < n4; e += NT) {
-    const int h = e / D4, d = (e - h * D4) * 4;
+  for (int e = threadIdx.x; e < a.hw * n4; e += NT) {
+    const int gl = e / n4, e2 = e - gl * n4;
+    const int h = e2 / D4, d = (e2 - h * D4) * 4;
+    const int gh = gb * a.hw + gl;
+    const int64_t u0 = ((int64_t)row * a.hkv + gh) * a.chunks;
     float M = NEG_INF;
     for (int ch = 0; ch < a.chunks; ++ch)
       M = fmaxf(M, ld_coh64(a.part_ml + ((int64_t)(u0 + ch) * a.G + h) * 2).x);
@@ -332,10 +353,10 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
       const float2 x0 = ld_coh64(po), x1 = ld_coh64(po + 2);
       o.x += x0.x * f; o.y += x0.y * f; o.z += x1.x * f; o.w += x1.y * f;
     }
-    store_out(a, row, g * a.G + h, d, o, L, M, D);
+    store_out(a, row, gh * a.G + h, d, o, L, M, D);
   }
   if (threadIdx.x == 0)
-    __hip_atomic_store(&a.tickets[pair], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.tickets[wgp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace sa
@@ -349,7 +370,7 @@ using namespace dsa::sa;
 struct dsa_attn_ctx {
   dsa_attn_shape sh;
   int device;
-  int chunks, spc;
+  int chunks, spc, hw;
   void* ws;
   size_t ws_bytes;
   float *part_o, *part_ml;
@@ -440,18 +461,21 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   c->sh = *s;
   c->device = device;
   c->magic = SA_MAGIC;
-  // Chunks per (row, kv head): enough workgroups for two per CU over all
-  // pairs, each chunk at least one step per wave.
+  // kv heads per workgroup, and chunks per (row, group of kv heads): enough
+  // workgroups for two per CU, each chunk at least one step per wave.
+  const int hw = s->kv_heads % 4 == 0 ? 4 : s->kv_heads % 2 == 0 ? 2 : 1;
+  const int64_t wgp = (int64_t)s->rows * (s->kv_heads / hw);
   const int64_t steps = (s->k_tokens + STEP - 1) / STEP;
-  const int64_t maxc = std::max<int64_t>(1, steps / WAVES);
+  const int64_t maxc = std::max<int64_t>(1, steps / (WAVES / hw));
   int64_t ch = s->chunks > 0 ? s->chunks
-                             : (2 * (int64_t)cus + std::max<int64_t>(pairs, 1) - 1) / std::max<int64_t>(pairs, 1);
+                             : (2 * (int64_t)cus + std::max<int64_t>(wgp, 1) - 1) / std::max<int64_t>(wgp, 1);
   ch = std::max<int64_t>(1, std::min<int64_t>(ch, s->chunks > 0 ? steps : maxc));
   const int64_t spc = (steps + ch - 1) / ch;
   ch = (steps + spc - 1) / spc;
-  if (pairs * ch > ((int64_t)1 << 31) - 1) { delete c; return sa_fail(DSA_ERR_UNSUPPORTED, "grid too large"); }
+  if (wgp * ch > ((int64_t)1 << 31) - 1) { delete c; return sa_fail(DSA_ERR_UNSUPPORTED, "grid too large"); }
   c->chunks = (int)ch;
   c->spc = (int)spc;
+  c->hw = hw;
   const int64_t units = ch > 1 ? pairs * ch : 0;
   const int64_t floats = units * s->group * (D + 2);
   c->ws_bytes = (size_t)floats * 4 + (size_t)(pairs + 1) * 4 + 256;
@@ -517,9 +541,9 @@ int dsa_sparse_attn(dsa_attn_ctx* c, const uint16_t* q, const uint16_t* k_cache,
   while ((1 << shift) < s.page_size) ++shift;
   a.page_shift = shift;
   a.pps = s.pages_per_seq;
-  a.chunks = c->chunks; a.spc = c->spc;
+  a.chunks = c->chunks; a.spc = c->spc; a.hw = c->hw;
   a.c2 = sm_scale * 1.4426950408889634f;
-  const unsigned grid = (unsigned)((int64_t)s.rows * s.kv_heads * c->chunks);
+  const unsigned grid = (unsigned)((int64_t)s.rows * (s.kv_heads / c->hw) * c->chunks);
   if (s.head_dim == 256)
     hipLaunchKernelGGL(k_sparse_attn<256>, dim3(grid), dim3(NT), 0, stream, a);
   else

@@ -128,6 +128,9 @@ def test_attn_small_config_every_row():
     (128, 16, 1, 64, 2, True, False, True),
     (256, 12, 2, 2048, 64, True, True, True),
     (128, 5, 3, 1, 0, True, True, True),
+    (128, 2, 4, 700, 0, True, True, True),
+    (256, 4, 6, 200, 2, True, True, True),
+    (256, 8, 8, 2048, 0, True, False, True),
 ])
 def test_attn_shapes(D, G, hkv, K, chunks, paged, gate, with_lse):
     rng = np.random.default_rng(D + 7 * G + 11 * K)
