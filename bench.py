@@ -424,6 +424,8 @@ def main() -> int:
                     help="do not also time the sparse attention over the selected tokens")
     ap.add_argument("--attn-only", action="store_true",
                     help="time only the sparse attention")
+    ap.add_argument("--attn-workloads", default="attn_decode,attn_c1",
+                    help="comma-separated sparse-attention workloads to time")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -450,7 +452,7 @@ def main() -> int:
         return 0
     if args.attn_only:
         at = [run_attn(n, min(args.steps, 20), min(args.warmup, 2))
-              for n in ("attn_decode", "attn_c1")]
+              for n in args.attn_workloads.split(",")]
         print(json.dumps({"sparse_attn": at}), flush=True)
         return 0
     if args.indexer_only:
@@ -477,7 +479,7 @@ def main() -> int:
     attn = None
     if not args.no_attn and args.width is None:
         attn = [run_attn(n, min(args.steps, 20), min(args.warmup, 2))
-                for n in ("attn_decode", "attn_c1")]
+                for n in args.attn_workloads.split(",")]
 
     cpu = None
     if not args.no_cpu_baseline:

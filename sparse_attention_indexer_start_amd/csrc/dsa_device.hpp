@@ -127,7 +127,7 @@ struct __align__(16) Smem {
   uint32_t kid[2 * LIST_CAP];   // [0, LIST_CAP): keys, [LIST_CAP, 2*LIST_CAP): ids
   uint32_t sel[SEL_CAP];
   uint32_t tkey[TK_CAP];
-  uint32_t bits[CHUNK_CAP / 32];
+  uint32_t bits[CHUNK_CAP / 32];  // a short row's dropped-block bitmap
   uint32_t wv[64];
   uint32_t misc[16];
   uint64_t pfx[514];            // long-row block prefix over rows, then the chunk

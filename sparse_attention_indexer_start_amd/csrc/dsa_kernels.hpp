@@ -726,6 +726,14 @@ DSA_DEV void token_stage(const Params& p, int r, const Row& rb, const float* row
   for (int i = Kt + threadIdx.x; i < p.k_tokens; i += NT) tout[i] = -1;
 }
 
+// -inf over the blocks of a short row marked in sm.bits.
+template <int BS>
+DSA_DEV void mask_dropped_short(float* rowp, int64_t cs, int B, int L, int nlb, bool vec,
+                                Smem& sm) {
+  mask_blocks<BS>(rowp, cs, B, L, 0, nlb, vec,
+                  [&](int b) { return ((sm.bits[b >> 5] >> (b & 31)) & 1u) != 0u; });
+}
+
 // ---------------------------------------------------------------------------
 // A row with nlb <= LIST_CAP: the whole chain in one workgroup, keys in LDS.
 // ---------------------------------------------------------------------------
@@ -739,7 +747,7 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
   uint32_t* sel = Kp <= SEL_CAP ? sm.sel : p.ws_sel + (int64_t)r * p.k_blocks;
   const bool need_keys = nlb > p.k_blocks || p.scores != nullptr;
   uint32_t T = 0, q = 0xFFFFFFFFu;
-  bool no_low = false;
+  bool no_low = false, do_mask = false, mask_late = false;
   int n_nonkept = 0;
   if (!need_keys) {
     // Every live block is kept; the result follows from the bounds.
@@ -756,6 +764,8 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
     const bool do_select = nlb > Kp;
     if (do_select) {
       for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
+      if (!vec)
+        for (int j = threadIdx.x; j < (nlb + 31) / 32; j += NT) sm.bits[j] = 0;
       __syncthreads();
     }
     score_blocks<BS>(rowp, p.col_stride, B, L, 0, nlb, nlb, vec, [&](int b, uint32_t k) {
@@ -782,8 +792,15 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
     int32_t* tout = p.token_ids + (int64_t)r * p.k_tokens;
     const int32_t s32 = (int32_t)rb.s;
     // One ordered pass: kept ids out, the lowest non-kept ids listed (for the
-    // token fill), and each non-kept block masked by the lane that owns it.
-    const bool do_mask = (p.flags & DSA_WRITE_MASK) && nlb > Kp;
+    // token fill), and each non-kept block masked.  On a contiguous row the
+    // lane that owns a block stores it with 16-byte stores as it goes.  On a
+    // strided row that would write one word into each of 64 lines per store
+    // instruction (and every partial-line write costs a read-modify-write),
+    // so the block is marked in a bitmap instead and the -inf stores run
+    // column by column across the workgroup at the end (the token stage reads
+    // kept columns only).
+    do_mask = (p.flags & DSA_WRITE_MASK) && nlb > Kp;
+    mask_late = do_mask && !vec;
     uint32_t* nonkept = sm.tkey;
     wg_rule_emit<NT>(nlb, T, q, getk, [&](int i, uint32_t rank, bool kept) {
       const int n = (int)min((int64_t)B, (int64_t)L - (int64_t)i * B);
@@ -810,18 +827,27 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
           const int m = (int)min((int64_t)n, qt - (int64_t)nk * B);
           for (int e = 0; e < m; ++e) tout[(int64_t)i * B + e] = s32 + i * B + e;
         }
-        if (do_mask) mask_block_lane<BS>(rowp, p.col_stride, B, L, vec, i);
+        if (mask_late) atomicOr(&sm.bits[i >> 5], 1u << (i & 31));
+        else if (do_mask) mask_block_lane<BS>(rowp, p.col_stride, B, L, vec, i);
       }
     }, sm);
     n_nonkept = min(nlb - Kp, TK_CAP);
     for (int i = Kp + threadIdx.x; i < p.k_blocks; i += NT) bout[i] = -1;
     if (fuse_tok) {
       for (int i = Kt + threadIdx.x; i < p.k_tokens; i += NT) tout[i] = -1;
+      if (mask_late) {
+        __syncthreads();
+        mask_dropped_short<BS>(rowp, p.col_stride, B, L, nlb, vec, sm);
+      }
       return;
     }
   }
   __syncthreads();
   token_stage<BS>(p, r, rb, rowp, sel, Kp, T, true, no_low, sm, sm.tkey, n_nonkept);
+  if (mask_late) {
+    __syncthreads();
+    mask_dropped_short<BS>(rowp, p.col_stride, B, L, nlb, vec, sm);
+  }
 }
 
 // Workgroup-wide ticket on a workspace counter: true in the last of `total`

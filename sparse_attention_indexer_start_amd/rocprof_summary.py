@@ -35,6 +35,12 @@ def _one(pattern: str) -> str:
     return hits[0]
 
 
+def short_name(name: str, limit: int = 120) -> str:
+    """Kernel names of library code (torch's templated kernels) cut to a
+    readable length."""
+    return name if len(name) <= limit else name[:limit] + "..."
+
+
 def kernel_table(d: str, cmd: str) -> str:
     path = _one(os.path.join(d, "**", "*kernel_stats.csv"))
     rows = list(csv.DictReader(open(path)))
@@ -42,7 +48,7 @@ def kernel_table(d: str, cmd: str) -> str:
              "| kernel | calls | average us | min us | max us | share % |",
              "|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        lines.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                      f"{float(r['Percentage']):.1f} |")
     return "\n".join(lines) + "\n"
