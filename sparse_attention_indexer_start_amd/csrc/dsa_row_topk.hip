@@ -11,19 +11,22 @@
 // Each row is cut into P pieces (P fixed by the shape and the CU count; the
 // pieces follow the row's own live length), and every step is a launch of its
 // own on the caller's stream, so no workgroup ever waits on another:
-//   hist  (rows x P)  a 12-, 12- then 8-bit digit histogram of the pieces'
-//                     keys (only keys matching the digits found so far),
-//                     merged into the row's histogram with atomics;
-//   find  (rows)      the digit holding the K-th key, from the row's
-//                     histogram; after the third digit (or once a whole bin is
-//                     taken) the row's rule (T, q) is fixed: keep key > T, and
-//                     the first q keys equal to T in column order;
-//   count (rows x P)  each piece's keys above T and equal to T;
-//   scan  (rows)      each piece's output offset and its share of the ties;
-//   emit  (rows x P)  each piece's kept columns, in column order.
-// Passes whose digit is already settled return at once.  The workspace (one
-// histogram, a few state words and two counts per piece, per row) does not
-// depend on the row length.
+//   hist  (rows x P, three launches)  a 12-, 12- then 8-bit digit histogram
+//         of the pieces' keys (only keys matching the digits found so far),
+//         merged into the row's histogram with atomics; the last piece of the
+//         row to arrive finds the digit holding the K-th key.  After the
+//         third digit (or once a whole bin is taken) the row's rule (T, q) is
+//         fixed: keep key > T, and the first q keys equal to T in column
+//         order.  The third pass also keeps each piece's counts above every
+//         last digit, so its finder can place every piece's output at once;
+//   count (rows x P)  only for rows settled before the third digit: each
+//         piece's keys above and equal to T, the last to arrive placing the
+//         pieces;
+//   emit  (rows x P)  each piece's kept columns, in column order, and the -1
+//         padding.
+// Passes whose row is already settled return at once.  The workspace (one
+// histogram, a few state words, per-piece counts and the third pass's
+// per-piece suffix counts, per row) does not depend on the row length.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -39,10 +42,12 @@
 namespace dsa {
 namespace rt {
 
-constexpr int NT = 256;
-constexpr int FNT = 512;          // the find step (a 4096-bin search needs 8 bins per thread)
-constexpr int MIN_PIECE = 4096;   // columns per piece at least (when the row has them)
-constexpr int STATE = 8;          // [0] prefix [1] krem [2] done [3] T [4] q [5] Kt
+constexpr int NT = 512;
+constexpr int MIN_PIECE = 8192;   // columns per piece at least (when the row has them)
+constexpr int SFX = 257;          // per-piece suffix counts of the last digit, and the sentinel
+// State words of a row.  [0] prefix [1] krem [2] done [3] T [4] q [5] Kt
+// [6] pieces placed (offsets written by the third pass) [7] arrival ticket
+constexpr int STATE = 8;
 
 struct Args {
   const float* logits;
@@ -55,6 +60,7 @@ struct Args {
   uint32_t* state;   // [rows][STATE]
   uint32_t* cnt;     // [rows][P][2]  keys above T, keys equal to T
   uint32_t* off;     // [rows][P][2]  output offset, ties taken
+  uint32_t* sfx;     // [rows][P][SFX]  third pass: keys above each last digit
 };
 
 struct Live {
@@ -73,19 +79,52 @@ DSA_DEV Live live_range(const Args& a, int r) {
   return lv;
 }
 
-// Columns [c0, c1) of the live range that piece j of P covers.
+// Columns [c0, c1) of the live range that piece j of P covers (pieces are a
+// multiple of 4 columns long, so a 16-byte aligned row keeps them aligned).
 DSA_DEV void piece_range(int64_t L, int P, int j, int64_t& c0, int64_t& c1) {
-  const int64_t C = (L + P - 1) / P;
+  const int64_t C = ((L + P - 1) / P + 3) & ~(int64_t)3;
   c0 = min(L, (int64_t)j * C);
   c1 = min(L, c0 + C);
 }
 
-// Visits the keys of columns [c0, c1) of a row: f(column, key), four
-// columns per thread per round, loads issued together.
+// Whether columns from c0 on can be read as aligned float4 vectors.
+DSA_DEV bool vec_cols(const Args& a, const float* rowp, int64_t c0) {
+  return a.col_stride == 1 && (reinterpret_cast<uintptr_t>(rowp + c0) & 15u) == 0;
+}
+
+// Visits the keys of columns [c0, c1) of a row: f(column, key).  Contiguous
+// aligned rows are read as float4 vectors, four per thread in flight (the
+// last partial vector column by column); other rows column by column, four
+// loads per thread in flight.
 template <class F>
 DSA_DEV void for_keys(const Args& a, const float* rowp, int64_t c0, int64_t c1, F f) {
   const int64_t cs = a.col_stride;
   constexpr int U = 4;
+  if (vec_cols(a, rowp, c0)) {
+    const int64_t n4 = (c1 - c0) >> 2;
+    const float4* vp = reinterpret_cast<const float4*>(rowp + c0);
+    for (int64_t b = threadIdx.x; b < n4; b += (int64_t)NT * U) {
+      float4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = b + (int64_t)u * NT;
+        v[u] = vp[i < n4 ? i : 0];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = b + (int64_t)u * NT;
+        if (i < n4) {
+          const int64_t c = c0 + 4 * i;
+          f(c, f2key(v[u].x));
+          f(c + 1, f2key(v[u].y));
+          f(c + 2, f2key(v[u].z));
+          f(c + 3, f2key(v[u].w));
+        }
+      }
+    }
+    for (int64_t c = c0 + 4 * n4 + threadIdx.x; c < c1; c += NT) f(c, f2key(rowp[c]));
+    return;
+  }
   for (int64_t b = c0 + (int64_t)threadIdx.x; b < c1; b += (int64_t)NT * U) {
     float v[U];
 #pragma unroll
@@ -101,22 +140,134 @@ DSA_DEV void for_keys(const Args& a, const float* rowp, int64_t c0, int64_t c1, 
   }
 }
 
+// Block-wide exclusive scan of one value per thread (NT threads); also the
+// total.  wv needs NT / 64 words; two barriers.
+DSA_DEV uint32_t block_excl_scan(uint32_t x, uint32_t* wv, uint32_t& total) {
+  constexpr int NW = NT / 64;
+  const uint32_t inc = wave_incl_scan(x);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 63) wv[threadIdx.x >> 6] = inc;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+  const int w = (int)(threadIdx.x >> 6);
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t v = wv[i];
+    off += i < w ? v : 0u;
+    tot += v;
+  }
+  total = tot;
+  return off + inc - x;
+}
+
+// The digit d of bins h[0, nb) (nb <= 8 * NT) holding the krem-th largest
+// key: count(bins > d) < krem <= count(bins >= d).  Also that count above d
+// and h[d].  Each thread sums up to eight consecutive bins.
+DSA_DEV void find_digit(const uint32_t* h, int nb, uint32_t krem, uint32_t* wv, uint32_t* misc,
+                        uint32_t& d, uint32_t& above, uint32_t& in_bin) {
+  const int per = nb >= NT ? nb / NT : 1;
+  const int lo = (int)threadIdx.x * per;
+  uint32_t v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (i < per && lo + i < nb) ? h[lo + i] : 0u;
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c += v[i];
+  if (threadIdx.x == 0) { misc[0] = 0; misc[1] = 0; misc[2] = 0; }
+  uint32_t total;
+  const uint32_t excl = block_excl_scan(c, wv, total);
+  const uint32_t sfx = total - excl - c;   // keys in the bins above this thread's
+  if (sfx < krem && krem <= sfx + c) {
+    uint32_t acc = sfx;
+    bool found = false;
+#pragma unroll
+    for (int i = 7; i >= 0; --i) {
+      if (!found && i < per) {
+        if (acc + v[i] >= krem) {
+          misc[0] = (uint32_t)(lo + i);
+          misc[1] = acc;
+          misc[2] = v[i];
+          found = true;
+        } else {
+          acc += v[i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  d = misc[0];
+  above = misc[1];
+  in_bin = misc[2];
+}
+
+// Output offsets of the row's P pieces from their counts (keys above T and
+// equal to T), each piece taking its share of the q ties in column order.
+template <class Counts>
+DSA_DEV void place_pieces(const Args& a, int r, uint32_t q, uint32_t* wv, Counts counts) {
+  uint32_t base_gt = 0, base_eq = 0;
+  for (int j0 = 0; j0 < a.P; j0 += NT) {
+    const int j = j0 + (int)threadIdx.x;
+    uint32_t gt = 0, eq = 0;
+    if (j < a.P) counts(j, gt, eq);
+    uint32_t tg, te;
+    const uint32_t xg = block_excl_scan(gt, wv, tg) + base_gt;
+    const uint32_t xe = block_excl_scan(eq, wv, te) + base_eq;
+    if (j < a.P) {
+      const uint32_t before = min(xe, q);
+      uint32_t* op = a.off + ((int64_t)r * a.P + j) * 2;
+      op[0] = xg + before;
+      op[1] = min(eq, q - before);
+    }
+    base_gt += tg;
+    base_eq += te;
+  }
+}
+
+// Last of the row's P pieces to arrive (each wave's stores and atomics
+// drained first).  The last one resets the ticket.
+DSA_DEV bool last_piece(uint32_t* ticket, int P, uint32_t* misc) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t n = atomicAdd(ticket, 1u);
+    misc[3] = n == (uint32_t)(P - 1);
+    if (misc[3]) st_shared(ticket, 0u);
+  }
+  __syncthreads();
+  return misc[3] != 0;
+}
+
 __global__ __launch_bounds__(NT) void k_rt_hist(Args a) {
   __shared__ uint32_t h[HIST_WORDS];
+  __shared__ uint32_t wv[NT / 64];
+  __shared__ uint32_t misc[8];
   const int r = (int)(blockIdx.x / (unsigned)a.P), j = (int)(blockIdx.x % (unsigned)a.P);
   const Live lv = live_range(a, r);
-  if (lv.L == 0) return;
-  const uint32_t* st = a.state + (int64_t)r * STATE;
-  uint32_t prefix = 0;
-  if (a.pass > 0) {
+  uint32_t* st = a.state + (int64_t)r * STATE;
+  const int64_t Kt = min((int64_t)a.k, lv.L);
+  uint32_t prefix = 0, krem = (uint32_t)Kt;
+  if (a.pass == 0) {
+    if (lv.L == 0 || Kt == lv.L) {
+      // Nothing to select: an empty row keeps nothing, a short one everything.
+      if (j == 0 && threadIdx.x == 0) {
+        st[0] = 0; st[1] = 0; st[2] = 1;
+        st[3] = lv.L == 0 ? 0xFFFFFFFFu : 0u;
+        st[4] = lv.L == 0 ? 0u : 0xFFFFFFFFu;
+        st[5] = (uint32_t)Kt; st[6] = 0;
+      }
+      return;
+    }
+  } else {
     if (st[2]) return;                    // the rule is already fixed
     prefix = st[0];
+    krem = st[1];
   }
   for (int i = threadIdx.x; i < HIST_WORDS; i += NT) h[i] = 0;
   __syncthreads();
   int64_t c0, c1;
   piece_range(lv.L, a.P, j, c0, c1);
   const float* rowp = a.logits + (int64_t)r * a.row_stride + lv.s * a.col_stride;
+  uint32_t above = 0;   // third pass: keys above the 24-bit prefix
   if (a.pass == 0) {
     for_keys(a, rowp, c0, c1, [&](int64_t, uint32_t k) { atomicAdd(&h[k >> 20], 1u); });
   } else if (a.pass == 1) {
@@ -128,88 +279,79 @@ __global__ __launch_bounds__(NT) void k_rt_hist(Args a) {
     const uint32_t p = prefix >> 8;
     for_keys(a, rowp, c0, c1, [&](int64_t, uint32_t k) {
       if ((k >> 8) == p) atomicAdd(&h[k & 0xFFu], 1u);
+      above += (k >> 8) > p;
     });
   }
+  uint32_t tot_above = 0;
+  if (a.pass == 2) (void)block_excl_scan(above, wv, tot_above);
   __syncthreads();
-  uint32_t* gh = a.hist + (int64_t)r * HIST_WORDS;
-  for (int i = threadIdx.x; i < HIST_WORDS; i += NT)
-    if (h[i]) atomicAdd(&gh[i], h[i]);
-}
-
-__global__ __launch_bounds__(FNT) void k_rt_find(Args a) {
-  __shared__ Smem sm;
-  const int r = (int)blockIdx.x;
-  const Live lv = live_range(a, r);
-  uint32_t* st = a.state + (int64_t)r * STATE;
-  uint32_t* gh = a.hist + (int64_t)r * HIST_WORDS;
-  const int64_t Kt = min((int64_t)a.k, lv.L);
-  uint32_t prefix, krem, done;
-  if (a.pass == 0) {
-    prefix = 0;
-    krem = (uint32_t)Kt;
-    done = 0;
-  } else {
-    prefix = st[0];
-    krem = st[1];
-    done = st[2];
-  }
-  if (lv.L == 0 || done) {
-    if (a.pass == 0 && threadIdx.x == 0) {   // an empty row keeps nothing
-      st[2] = 1; st[3] = 0xFFFFFFFFu; st[4] = 0; st[5] = 0;
-    }
-    return;
-  }
   const int nb = a.pass == 2 ? 256 : HIST_WORDS;
+  uint32_t* gh = a.hist + (int64_t)r * HIST_WORDS;
+  for (int i = threadIdx.x; i < nb; i += NT)
+    if (h[i]) atomicAdd(&gh[i], h[i]);
+  if (a.pass == 2) {
+    // Suffix counts: S[b] = keys above the prefix + keys of digits >= b.
+    uint32_t* sp = a.sfx + ((int64_t)r * a.P + j) * SFX;
+    const uint32_t x = threadIdx.x < 256 ? h[255 - threadIdx.x] : 0u;
+    uint32_t t2;
+    const uint32_t ex = block_excl_scan(x, wv, t2);   // over digits 255, 254, ...
+    if (threadIdx.x < 256) st_shared(&sp[255 - threadIdx.x], tot_above + ex + x);
+    if (threadIdx.x == 0) st_shared(&sp[256], tot_above);
+  }
+  if (!last_piece(&st[7], a.P, misc)) return;
+
+  // The row's last piece: its digit.
+  for (int i = threadIdx.x; i < nb; i += NT) {
+    h[i] = ld_shared(&gh[i]);
+    st_shared(&gh[i], 0u);                // cleared for the next pass and call
+  }
+  __syncthreads();
+  uint32_t d, ab, in_bin;
+  find_digit(h, nb, krem, wv, misc, d, ab, in_bin);
   const int shift = a.pass == 0 ? 20 : (a.pass == 1 ? 8 : 0);
-  uint32_t T = 0, q = 0;
-  if (a.pass == 0 && Kt == lv.L) {
-    // every column is kept
+  prefix |= d << shift;
+  krem -= ab;
+  uint32_t done = 0, T = 0, q = 0, placed = 0;
+  if (a.pass == 2) {
     done = 1;
-    T = 0;
-    q = 0xFFFFFFFFu;
-  } else {
-    for (int i = threadIdx.x; i < nb; i += FNT) sm.hist[i] = gh[i];
-    __syncthreads();
-    uint32_t d, above, in_bin;
-    find_bin<FNT>(sm.hist, nb, krem, sm, d, above, in_bin);
-    prefix |= d << shift;
-    krem -= above;
-    if (a.pass == 2) {
-      done = 1;
-      T = prefix;
-      q = krem;
-    } else if (in_bin == krem) {
-      // the whole bin is kept: every key from the bin's lowest value up
-      done = 1;
-      if (prefix == 0) {
-        T = 0;
-        q = 0xFFFFFFFFu;
-      } else {
-        T = prefix - 1;
-        q = 0;
-      }
+    T = prefix;
+    q = krem;
+    // Every piece's keys above T and equal to T, from its suffix counts.
+    place_pieces(a, r, q, wv, [&](int jj, uint32_t& gt, uint32_t& eq) {
+      const uint32_t* sp = a.sfx + ((int64_t)r * a.P + jj) * SFX;
+      const uint32_t ge = ld_shared(&sp[d]);
+      gt = ld_shared(&sp[d + 1]);
+      eq = ge - gt;
+    });
+    placed = 1;
+  } else if (in_bin == krem) {
+    // the whole bin is kept: every key from the bin's lowest value up
+    done = 1;
+    if (prefix == 0) {
+      T = 0;
+      q = 0xFFFFFFFFu;
+    } else {
+      T = prefix - 1;
+      q = 0;
     }
   }
-  // clear the row's histogram for the next pass (and the next call)
-  for (int i = threadIdx.x; i < HIST_WORDS; i += FNT) gh[i] = 0;
   if (threadIdx.x == 0) {
-    st[0] = prefix;
-    st[1] = krem;
-    st[2] = done;
-    st[3] = T;
-    st[4] = q;
-    st[5] = (uint32_t)Kt;
+    st[0] = prefix; st[1] = krem; st[2] = done; st[3] = T; st[4] = q;
+    st[5] = (uint32_t)Kt; st[6] = placed;
   }
 }
 
+// Rows settled before the third digit: each piece's keys above and equal to
+// T; the last piece to arrive places the pieces.
 __global__ __launch_bounds__(NT) void k_rt_count(Args a) {
-  __shared__ uint32_t wv[64];
+  __shared__ uint32_t wv[NT / 64];
+  __shared__ uint32_t misc[8];
   const int r = (int)(blockIdx.x / (unsigned)a.P), j = (int)(blockIdx.x % (unsigned)a.P);
   const Live lv = live_range(a, r);
-  uint32_t* cp = a.cnt + ((int64_t)r * a.P + j) * 2;
   if (lv.L == 0) return;
-  const uint32_t* st = a.state + (int64_t)r * STATE;
-  const uint32_t T = st[3];
+  uint32_t* st = a.state + (int64_t)r * STATE;
+  if (st[6]) return;                      // placed by the third pass
+  const uint32_t T = st[3], q = st[4];
   int64_t c0, c1;
   piece_range(lv.L, a.P, j, c0, c1);
   const float* rowp = a.logits + (int64_t)r * a.row_stride + lv.s * a.col_stride;
@@ -219,49 +361,33 @@ __global__ __launch_bounds__(NT) void k_rt_count(Args a) {
     eq += k == T;
   });
   uint32_t tg, te;
-  (void)wg_excl_scan<NT>(gt, wv, tg);
-  (void)wg_excl_scan<NT>(eq, wv, te);
+  (void)block_excl_scan(gt, wv, tg);
+  (void)block_excl_scan(eq, wv, te);
+  uint32_t* cp = a.cnt + ((int64_t)r * a.P + j) * 2;
   if (threadIdx.x == 0) {
-    cp[0] = tg;
-    cp[1] = te;
+    st_shared(&cp[0], tg);
+    st_shared(&cp[1], te);
   }
-}
-
-__global__ __launch_bounds__(NT) void k_rt_scan(Args a) {
-  __shared__ uint32_t wv[64];
-  const int r = (int)blockIdx.x;
-  const Live lv = live_range(a, r);
-  const uint32_t* st = a.state + (int64_t)r * STATE;
-  int32_t* outp = a.out + (int64_t)r * a.k;
-  const int64_t Kt = lv.L == 0 ? 0 : min((int64_t)a.k, lv.L);
-  for (int64_t i = Kt + threadIdx.x; i < a.k; i += NT) outp[i] = -1;
-  if (lv.L == 0) return;
-  const uint32_t q = st[4];
-  uint32_t base_gt = 0, base_eq = 0;
-  for (int j0 = 0; j0 < a.P; j0 += NT) {
-    const int j = j0 + (int)threadIdx.x;
-    const uint32_t* cp = a.cnt + ((int64_t)r * a.P + (j < a.P ? j : 0)) * 2;
-    const uint32_t gt = j < a.P ? cp[0] : 0u, eq = j < a.P ? cp[1] : 0u;
-    uint32_t tg, te;
-    const uint32_t xg = wg_excl_scan<NT>(gt, wv, tg) + base_gt;
-    const uint32_t xe = wg_excl_scan<NT>(eq, wv, te) + base_eq;
-    if (j < a.P) {
-      // ties before this piece: xe; this piece takes the ones still allowed
-      const uint32_t before = min(xe, q);
-      const uint32_t take = min(eq, q - before);
-      uint32_t* op = a.off + ((int64_t)r * a.P + j) * 2;
-      op[0] = xg + before;
-      op[1] = take;
-    }
-    base_gt += tg;
-    base_eq += te;
-  }
+  if (!last_piece(&st[7], a.P, misc)) return;
+  place_pieces(a, r, q, wv, [&](int jj, uint32_t& g, uint32_t& e) {
+    const uint32_t* c = a.cnt + ((int64_t)r * a.P + jj) * 2;
+    g = ld_shared(&c[0]);
+    e = ld_shared(&c[1]);
+  });
 }
 
 __global__ __launch_bounds__(NT) void k_rt_emit(Args a) {
-  __shared__ uint32_t wv[64];
+  __shared__ uint32_t wv[NT / 64];
   const int r = (int)(blockIdx.x / (unsigned)a.P), j = (int)(blockIdx.x % (unsigned)a.P);
   const Live lv = live_range(a, r);
+  int32_t* outp = a.out + (int64_t)r * a.k;
+  const int64_t Kt = min((int64_t)a.k, lv.L);
+  {
+    // -1 over [Kt, k), split over the row's pieces
+    const int64_t n = a.k - Kt, per = (n + a.P - 1) / a.P;
+    const int64_t p0 = Kt + min(n, (int64_t)j * per), p1 = Kt + min(n, ((int64_t)j + 1) * per);
+    for (int64_t i = p0 + threadIdx.x; i < p1; i += NT) outp[i] = -1;
+  }
   if (lv.L == 0) return;
   const uint32_t* st = a.state + (int64_t)r * STATE;
   const uint32_t T = st[3];
@@ -272,27 +398,41 @@ __global__ __launch_bounds__(NT) void k_rt_emit(Args a) {
   int64_t c0, c1;
   piece_range(lv.L, a.P, j, c0, c1);
   const float* rowp = a.logits + (int64_t)r * a.row_stride + lv.s * a.col_stride;
-  int32_t* outp = a.out + (int64_t)r * a.k;
   const int64_t cs = a.col_stride;
   const int32_t s32 = (int32_t)lv.s;
   uint32_t ties = 0;   // ties of this piece before the current round
-  // Rounds of NT * 4 columns; thread t takes 4 consecutive columns, so the
+  // Rounds of NT * 16 columns; thread t takes 16 consecutive columns, so the
   // workgroup's exclusive scans give every kept column its place in order.
-  constexpr int U = 4;
+  constexpr int U = 16;
+  const bool vec = vec_cols(a, rowp, c0);
   for (int64_t b = c0; b < c1; b += (int64_t)NT * U) {
     const int64_t cb = b + (int64_t)threadIdx.x * U;
     uint32_t k[U];
+    if (vec && cb + U <= c1) {
+      const float4* vp = reinterpret_cast<const float4*>(rowp + cb);
+      float4 v[U / 4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = cb + u;
-      const float v = rowp[(c < c1 ? c : c0) * cs];
-      k[u] = c < c1 ? f2key(v) : 0u;
+      for (int u = 0; u < U / 4; ++u) v[u] = vp[u];
+#pragma unroll
+      for (int u = 0; u < U / 4; ++u) {
+        k[4 * u] = f2key(v[u].x);
+        k[4 * u + 1] = f2key(v[u].y);
+        k[4 * u + 2] = f2key(v[u].z);
+        k[4 * u + 3] = f2key(v[u].w);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t c = cb + u;
+        const float v = rowp[(c < c1 ? c : c0) * cs];
+        k[u] = c < c1 ? f2key(v) : 0u;
+      }
     }
     uint32_t ne = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) ne += (cb + u < c1) && k[u] == T;
     uint32_t te;
-    uint32_t xe = wg_excl_scan<NT>(ne, wv, te) + ties;
+    uint32_t xe = block_excl_scan(ne, wv, te) + ties;
     bool kept[U];
     uint32_t nk = 0;
 #pragma unroll
@@ -304,7 +444,7 @@ __global__ __launch_bounds__(NT) void k_rt_emit(Args a) {
       nk += kept[u];
     }
     uint32_t tk;
-    uint32_t xk = wg_excl_scan<NT>(nk, wv, tk) + pos;
+    uint32_t xk = block_excl_scan(nk, wv, tk) + pos;
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (kept[u]) {
@@ -330,7 +470,7 @@ struct dsa_topk_ctx {
   int P;
   void* ws;
   size_t ws_bytes;
-  uint32_t *hist, *state, *cnt, *off;
+  uint32_t *hist, *state, *cnt, *off, *sfx;
   uint32_t magic;
 };
 
@@ -398,16 +538,18 @@ int dsa_row_topk_init(const dsa_topk_shape* s, int device, dsa_topk_ctx** out) {
   c->sh = *s;
   c->device = device;
   c->magic = RT_MAGIC;
-  // Pieces per row: about eight workgroups per CU over all rows, each piece
-  // at least MIN_PIECE columns of the widest row, at most 4096.
+  // Pieces per row: about two workgroups per CU over all rows (each piece's
+  // histogram is merged into its row's with atomics, so fewer, longer pieces
+  // contend less), each piece at least MIN_PIECE columns of the widest row,
+  // at most 4096.
   const int64_t R = std::max<int64_t>(1, s->rows);
-  int64_t P = (8 * (int64_t)cus + R - 1) / R;
+  int64_t P = (2 * (int64_t)cus + R - 1) / R;
   P = std::min<int64_t>(P, std::max<int64_t>(1, (s->width + MIN_PIECE - 1) / MIN_PIECE));
   P = std::max<int64_t>(1, std::min<int64_t>(P, 4096));
   if (P * R > ((int64_t)1 << 31) - 1) { delete c; return rt_fail(DSA_ERR_UNSUPPORTED, "too many rows"); }
   c->P = (int)P;
   if (s->rows > 0 && s->width > 0) {
-    const int64_t words = R * dsa::HIST_WORDS + R * STATE + 2 * R * P + 2 * R * P;
+    const int64_t words = R * dsa::HIST_WORDS + R * STATE + 2 * R * P + 2 * R * P + R * P * SFX;
     c->ws_bytes = (size_t)words * 4;
     e = hipMalloc(&c->ws, c->ws_bytes);
     if (e != hipSuccess) { delete c; return rt_hip(e, "hipMalloc(workspace)"); }
@@ -419,6 +561,7 @@ int dsa_row_topk_init(const dsa_topk_shape* s, int device, dsa_topk_ctx** out) {
     c->state = c->hist + R * dsa::HIST_WORDS;
     c->cnt = c->state + R * STATE;
     c->off = c->cnt + 2 * R * P;
+    c->sfx = c->off + 2 * R * P;
   }
   *out = c;
   return DSA_OK;
@@ -455,15 +598,13 @@ int dsa_row_topk(dsa_topk_ctx* c, const float* logits, const int32_t* starts,
   a.width = c->sh.width; a.row_stride = c->sh.row_stride; a.col_stride = c->sh.col_stride;
   a.rows = c->sh.rows; a.k = c->sh.k; a.starts_repeat = c->sh.starts_repeat;
   a.ends_repeat = c->sh.ends_repeat; a.P = c->P;
-  a.hist = c->hist; a.state = c->state; a.cnt = c->cnt; a.off = c->off;
-  const unsigned pieces = (unsigned)((int64_t)c->sh.rows * c->P), rows = (unsigned)c->sh.rows;
+  a.hist = c->hist; a.state = c->state; a.cnt = c->cnt; a.off = c->off; a.sfx = c->sfx;
+  const unsigned pieces = (unsigned)((int64_t)c->sh.rows * c->P);
   for (int pass = 0; pass < 3; ++pass) {
     a.pass = pass;
     hipLaunchKernelGGL(k_rt_hist, dim3(pieces), dim3(NT), 0, stream, a);
-    hipLaunchKernelGGL(k_rt_find, dim3(rows), dim3(FNT), 0, stream, a);
   }
   hipLaunchKernelGGL(k_rt_count, dim3(pieces), dim3(NT), 0, stream, a);
-  hipLaunchKernelGGL(k_rt_scan, dim3(rows), dim3(NT), 0, stream, a);
   hipLaunchKernelGGL(k_rt_emit, dim3(pieces), dim3(NT), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return rt_hip(e, "row top-k launch");
