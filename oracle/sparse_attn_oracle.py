@@ -29,12 +29,17 @@ Readings taken where the pages print no formula:
   * Output gate: o * sigmoid(gate[r, h]) elementwise, when a gate is given.
   * Inputs q, K, V and the gate are bf16 (the upper 16 bits of an IEEE fp32);
     this oracle decodes them exactly and computes in float64.
+  * fp8 caches (the page's other K/V format): K and V hold OCP E4M3 codes
+    with one scale per tensor, K = e4m3(k) * k_scale and V = e4m3(v) *
+    v_scale (decoded by the indexer oracle's pinned E4M3 decoder).
 """
 from __future__ import annotations
 
 import math
 
 import numpy as np
+
+from .indexer_oracle import e4m3_decode
 
 
 # ---------------------------------------------------------------------------
@@ -104,11 +109,12 @@ def sigmoid(x: np.ndarray) -> np.ndarray:
 
 def sparse_attention(q, k_cache, v_cache, token_ids, sm_scale: float, group: int,
                      page_table=None, page_size: int = 1, rows_per_seq: int = 1,
-                     gate=None, rows=None):
+                     gate=None, rows=None, k_scale=None, v_scale=None):
     """Outputs of the sparse attention.
 
     q: uint16 bf16 [R, Hkv * G, D]; k_cache, v_cache: uint16 bf16
-    [num_slots, Hkv, D]; token_ids: int32 [R, K] (positions, -1 pads);
+    [num_slots, Hkv, D], or uint8 E4M3 codes with k_scale and v_scale given
+    (fp8 caches); token_ids: int32 [R, K] (positions, -1 pads);
     page_table: int32 [num_seqs, pages_per_seq] or None; gate: uint16 bf16
     [R, Hkv * G, D] or None.  ``rows`` limits the work to some rows.
 
@@ -118,6 +124,15 @@ def sparse_attention(q, k_cache, v_cache, token_ids, sm_scale: float, group: int
     R, hq, d = q.shape
     num_slots, hkv, _ = k_cache.shape
     assert hq == hkv * group
+    fp8 = k_cache.dtype == np.uint8
+    assert fp8 == (k_scale is not None) == (v_scale is not None) == (v_cache.dtype == np.uint8)
+
+    def kv(cache, sl, g, scale):
+        if not sl.size:
+            return np.zeros((0, d))
+        if fp8:
+            return e4m3_decode(cache[sl, g, :]) * float(scale)
+        return bf16_decode(cache[sl, g, :])
     out = np.zeros((R, hq, d))
     lse = np.full((R, hq), -np.inf)
     bad = np.zeros(R, dtype=np.int64)
@@ -135,8 +150,8 @@ def sparse_attention(q, k_cache, v_cache, token_ids, sm_scale: float, group: int
         slots = np.asarray(slots, dtype=np.int64)
         qd = bf16_decode(q[r])                            # [Hq, D]
         for g in range(hkv):
-            kk = bf16_decode(k_cache[slots, g, :]) if slots.size else np.zeros((0, d))
-            vv = bf16_decode(v_cache[slots, g, :]) if slots.size else np.zeros((0, d))
+            kk = kv(k_cache, slots, g, k_scale)
+            vv = kv(v_cache, slots, g, v_scale)
             heads = slice(g * group, (g + 1) * group)
             o, ls = attend(qd[heads], kk, vv, sm_scale)
             out[r, heads] = o

@@ -400,6 +400,12 @@ class AttnCase:
     num_slots: int
     seq_lens: np.ndarray
     cache_seed: int = 0
+    k_scale: Optional[float] = None   # fp8 caches: uint8 E4M3 codes times these scales
+    v_scale: Optional[float] = None
+
+    @property
+    def kv_fp8(self) -> bool:
+        return self.k_scale is not None
 
     @property
     def rows(self) -> int:
@@ -425,7 +431,7 @@ def _sorted_sample(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
 def make_attn_custom(seq_lens, rows_per_seq: int, kv_heads: int, group: int, head_dim: int,
                      k_tokens: int, page_size: int = 16, paged: bool = True,
                      with_gate: bool = True, seed: int = 1, q_scale: float = 1.0,
-                     host_caches: bool = True, spare_pages: int = 3,
+                     host_caches: bool = True, spare_pages: int = 3, kv_fp8: bool = False,
                      name: str = "attn_custom") -> AttnCase:
     """Seeded synthetic attention inputs.
 
@@ -437,7 +443,9 @@ def make_attn_custom(seq_lens, rows_per_seq: int, kv_heads: int, group: int, hea
     (plus ``spare_pages`` never mapped) backs the sequences, and table
     entries past a sequence's length are -1.  q, K, V and the gate are
     N(0, 1) rounded to bf16 (q times ``q_scale``); the softmax scale is
-    1 / sqrt(head_dim).
+    1 / sqrt(head_dim).  With ``kv_fp8`` the caches hold E4M3 codes (random
+    sign, exponent field 3..9, random mantissa: magnitudes 1/16..7.5) with
+    k_scale 1/4 and v_scale 1/2.
     """
     rng = np.random.default_rng([seed, 57273])
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
@@ -468,11 +476,17 @@ def make_attn_custom(seq_lens, rows_per_seq: int, kv_heads: int, group: int, hea
     gate = bf16_bits(rng.standard_normal((R, hq, head_dim), dtype=np.float32)) if with_gate else None
     kc = vc = None
     if host_caches:
-        kc = bf16_bits(rng.standard_normal((num_slots, kv_heads, head_dim), dtype=np.float32))
-        vc = bf16_bits(rng.standard_normal((num_slots, kv_heads, head_dim), dtype=np.float32))
+        shape = (num_slots, kv_heads, head_dim)
+        if kv_fp8:
+            kc = e4m3_codes(rng, shape, 3, 9)
+            vc = e4m3_codes(rng, shape, 3, 9)
+        else:
+            kc = bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+            vc = bf16_bits(rng.standard_normal(shape, dtype=np.float32))
     return AttnCase(name, q, kc, vc, ids, table, page_size, rows_per_seq, gate, kv_heads, group,
                     head_dim, 1.0 / math.sqrt(head_dim), num_slots, seq_lens,
-                    cache_seed=seed)
+                    cache_seed=seed, k_scale=0.25 if kv_fp8 else None,
+                    v_scale=0.5 if kv_fp8 else None)
 
 
 ATTN_CONFIGS = {
@@ -484,6 +498,10 @@ ATTN_CONFIGS = {
     "attn_decode": dict(num_seqs=128, rows_per_seq=4, kv_heads=2, group=12, head_dim=256,
                         k_tokens=2048, page_size=64, ctx=(32768, 131072), short_frac=0.05,
                         host_caches=False),
+    # the same decode batch over fp8 (E4M3) K/V caches with per-tensor scales
+    "attn_decode_fp8": dict(num_seqs=128, rows_per_seq=4, kv_heads=2, group=12, head_dim=256,
+                            k_tokens=2048, page_size=64, ctx=(32768, 131072), short_frac=0.05,
+                            host_caches=False, kv_fp8=True),
     # one request (4 rows), 1 kv head with 3 query heads: the latency case
     "attn_c1": dict(num_seqs=1, rows_per_seq=4, kv_heads=1, group=3, head_dim=256,
                     k_tokens=2048, page_size=64, ctx=(65536, 65536), short_frac=0.0,
@@ -506,4 +524,5 @@ def make_attn_config(name: str, seed_offset: int = 0) -> AttnCase:
     return make_attn_custom(lens, c["rows_per_seq"], c["kv_heads"], c["group"], c["head_dim"],
                             c["k_tokens"], page_size=c["page_size"],
                             seed=BASE_SEED + 200 + seed_offset, host_caches=c["host_caches"],
-                            q_scale=c.get("q_scale", 1.0), name=name)
+                            q_scale=c.get("q_scale", 1.0), kv_fp8=c.get("kv_fp8", False),
+                            name=name)

@@ -202,6 +202,22 @@ def pin_softmax_bounds(o):
     assert np.allclose(out, out2, rtol=0, atol=1e-13) and np.allclose(lse, lse2, atol=1e-13)
 
 
+def pin_fp8_cache_scales(o):
+    """fp8 caches: E4M3 codes 0x38 = 1, 0x40 = 2, 0x30 = 0.5, 0x44 = 3;
+    k_scale 0.5, v_scale 4.  q = (1, 0); keys (2, 1) and (1, 3) -> 2*0.5 = 1
+    and 1*0.5 = 0.5; scale ln(3)/0.5 = 2 ln 3 makes the scores ln 9 and
+    ln 3: weights 3/4 and 1/4.  V codes (1, 0.5) and (3, 2) times 4 ->
+    (4, 2) and (12, 8): o = (3/4*4 + 1/4*12, 3/4*2 + 1/4*8) = (6, 3.5);
+    lse = ln(9 + 3) = ln 12."""
+    q = _b([[1.0, 0.0]])[None]
+    k = np.array([[[0x40, 0x38]], [[0x38, 0x44]]], np.uint8)
+    v = np.array([[[0x38, 0x30]], [[0x44, 0x40]]], np.uint8)
+    out, lse, _ = o.sparse_attention(q, k, v, np.array([[0, 1]], np.int32), 2.0 * math.log(3.0),
+                                     1, k_scale=0.5, v_scale=4.0)
+    assert np.allclose(out[0, 0], [6.0, 3.5], rtol=0, atol=1e-13), out
+    assert abs(lse[0, 0] - math.log(12.0)) < 1e-13
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
 
 
@@ -233,6 +249,8 @@ MUTANTS = {
     "empty_lse_zero": ("return np.zeros((hg, d)), np.full(hg, -np.inf)",
                        "return np.zeros((hg, d)), np.zeros(hg)"),
     "bad_ids_read_last_slot": ("bad[r] += 1\n                continue", "bad[r] += 1"),
+    "fp8_scale_ignored": ("return e4m3_decode(cache[sl, g, :]) * float(scale)",
+                          "return e4m3_decode(cache[sl, g, :])"),
 }
 
 
@@ -240,7 +258,8 @@ def _mutant(name):
     old, new = MUTANTS[name]
     src = open(ORACLE_PATH).read()
     assert src.count(old) == 1, f"mutant {name}: anchor not found once"
-    mod = types.ModuleType(f"sparse_attn_mut_{name}")
+    mod = types.ModuleType(f"oracle.sparse_attn_mut_{name}")
+    mod.__package__ = "oracle"
     exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
     return mod
 
