@@ -315,14 +315,26 @@ def run_row_topk(rows: int, width: int, k: int, steps: int, warmup: int) -> dict
 
 
 def attn_device_caches(case):
-    """K/V caches of a configuration, drawn on the device (bf16 N(0, 1))."""
+    """K/V caches of a configuration, drawn on the device: bf16 N(0, 1), or
+    E4M3 codes with a random sign, exponent field 3..9 and mantissa."""
     import torch
     gen = torch.Generator(device="cuda")
     gen.manual_seed(int(case.cache_seed))
     shape = (case.num_slots, case.kv_heads, case.head_dim)
-    k = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
-    v = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
-    return k, v
+    if not case.kv_fp8:
+        k = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+        v = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
+        return k, v
+
+    def codes():
+        c = torch.randint(0, 2, shape, generator=gen, device="cuda", dtype=torch.uint8)
+        c.bitwise_left_shift_(7)
+        e = torch.randint(3, 10, shape, generator=gen, device="cuda", dtype=torch.uint8)
+        c.bitwise_or_(e.bitwise_left_shift_(3))
+        del e
+        c.bitwise_or_(torch.randint(0, 8, shape, generator=gen, device="cuda", dtype=torch.uint8))
+        return c
+    return codes(), codes()
 
 
 def run_attn(name: str, steps: int, warmup: int) -> dict:
@@ -350,7 +362,8 @@ def run_attn(name: str, steps: int, warmup: int) -> dict:
     stream = torch.cuda.current_stream(dev)
 
     def call():
-        op(q, kd, vd, ids, table, gate, case.sm_scale, out, lse)
+        op(q, kd, vd, ids, table, gate, case.sm_scale, out, lse, k_scale=case.k_scale,
+           v_scale=case.v_scale)
 
     for _ in range(warmup):
         call()
@@ -374,7 +387,8 @@ def run_attn(name: str, steps: int, warmup: int) -> dict:
         raise RuntimeError(f"{name}: status word {status} after the timed calls")
     n_valid = int((case.token_ids >= 0).sum())
     D = case.head_dim
-    gathered = n_valid * case.kv_heads * D * 2 * 2
+    elem = 1 if case.kv_fp8 else 2
+    gathered = n_valid * case.kv_heads * D * elem * 2
     per_row = case.rows * (hq * D * 2 * 3 + case.k_tokens * 4 + hq * 4)
     alg = gathered + per_row
     achieved = alg / (ms * 1e-3) / 1e9
@@ -385,14 +399,15 @@ def run_attn(name: str, steps: int, warmup: int) -> dict:
         config={"workload": name, "rows": case.rows, "rows_per_seq": case.rows_per_seq,
                 "kv_heads": case.kv_heads, "group": case.group, "head_dim": D,
                 "k_tokens": case.k_tokens, "page_size": case.page_size, "gate": True,
-                "chunks": chunks, "dtype": "bf16 in, fp32 accumulate, bf16 out",
+                "chunks": chunks,
+                "dtype": ("fp8 e4m3 K/V, " if case.kv_fp8 else "") + "bf16 in, fp32 accumulate, bf16 out",
                 "graph": True},
         attended_tokens_per_call=n_valid, alg_bytes_per_call=alg,
         roofline={"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                   "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                   "basis": "K and V rows of every attended token (2 * kv_heads * head_dim "
-                           "bf16 each) + q, gate and out (bf16) + ids + lse, over the graph "
-                           "replay's time per call; page-table reads not counted"},
+                           "elements, bf16 or fp8) + q, gate and out (bf16) + ids + lse, over "
+                           "the graph replay's time per call; page-table reads not counted"},
     )
 
 
@@ -424,7 +439,7 @@ def main() -> int:
                     help="do not also time the sparse attention over the selected tokens")
     ap.add_argument("--attn-only", action="store_true",
                     help="time only the sparse attention")
-    ap.add_argument("--attn-workloads", default="attn_decode,attn_c1",
+    ap.add_argument("--attn-workloads", default="attn_decode,attn_decode_fp8,attn_c1",
                     help="comma-separated sparse-attention workloads to time")
     args = ap.parse_args()
 

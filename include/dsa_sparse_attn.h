@@ -86,6 +86,19 @@ int dsa_sparse_attn(dsa_attn_ctx* ctx, const uint16_t* q, const uint16_t* k_cach
                     const int32_t* page_table, const uint16_t* gate, float sm_scale,
                     uint16_t* out, float* lse, hipStream_t stream);
 
+/* The same attention over fp8 caches ([57273] names bf16 and fp8 K/V): k_cache
+ * and v_cache hold OCP E4M3 codes (1 byte per element, same layout and strides
+ * in elements, pointers 8-byte aligned) with one scale per tensor, K = e4m3(k)
+ * * k_scale and V = e4m3(v) * v_scale.  The codes are converted to bf16
+ * exactly on load; k_scale joins the score scale and v_scale the final
+ * normalisation, both in fp32.  E4M3 NaN codes are outside the contract.
+ * Same context as dsa_sparse_attn (a context may serve both). */
+int dsa_sparse_attn_fp8(dsa_attn_ctx* ctx, const uint16_t* q, const uint8_t* k_cache,
+                        const uint8_t* v_cache, float k_scale, float v_scale,
+                        const int32_t* token_ids, const int32_t* page_table,
+                        const uint16_t* gate, float sm_scale, uint16_t* out, float* lse,
+                        hipStream_t stream);
+
 /* Sticky status bits of the context (bit 0: some id was not addressable and
  * was skipped).  Synchronizes the device; not for use under capture. */
 int dsa_sparse_attn_read_status(dsa_attn_ctx* ctx, uint32_t* status);

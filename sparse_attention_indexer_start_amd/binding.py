@@ -34,7 +34,8 @@ EXPORTED = (
     "dsa_row_topk_init", "dsa_row_topk_destroy", "dsa_row_topk_pieces", "dsa_row_topk",
     "dsa_row_topk_last_error",
     "dsa_sparse_attn_init", "dsa_sparse_attn_destroy", "dsa_sparse_attn_chunks",
-    "dsa_sparse_attn", "dsa_sparse_attn_read_status", "dsa_sparse_attn_reset_status",
+    "dsa_sparse_attn", "dsa_sparse_attn_fp8", "dsa_sparse_attn_read_status",
+    "dsa_sparse_attn_reset_status",
     "dsa_sparse_attn_last_error",
 )
 
@@ -136,6 +137,8 @@ def load() -> ctypes.CDLL:
         lib.dsa_sparse_attn_destroy.argtypes = [vp]
         lib.dsa_sparse_attn_chunks.argtypes = [vp]
         lib.dsa_sparse_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+        f32 = ctypes.c_float
+        lib.dsa_sparse_attn_fp8.argtypes = [vp, vp, vp, vp, f32, f32, vp, vp, vp, f32, vp, vp, vp]
         lib.dsa_sparse_attn_read_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
         lib.dsa_sparse_attn_reset_status.argtypes = [vp]
         lib.dsa_sparse_attn_last_error.restype = ctypes.c_char_p
@@ -480,8 +483,9 @@ class RowTopk:
 class SparseAttn:
     """Sparse attention over each row's selected tokens (include/dsa_sparse_attn.h).
 
-    The caches are bf16 tensors [num_slots, kv_heads, head_dim] (any slot and
-    head strides that are multiples of 8 elements, innermost dimension
+    The caches are bf16 tensors [num_slots, kv_heads, head_dim], or uint8
+    tensors of E4M3 codes with k_scale and v_scale given (any slot and head
+    strides that are multiples of 8 elements, innermost dimension
     contiguous); q and gate are bf16 [rows, kv_heads * group, head_dim]."""
 
     def __init__(self, rows: int, kv_heads: int, group: int, head_dim: int, k_tokens: int,
@@ -519,9 +523,13 @@ class SparseAttn:
         self._check(load().dsa_sparse_attn_reset_status(self._h))
 
     def __call__(self, q, k_cache, v_cache, token_ids, page_table=None, gate=None,
-                 sm_scale=None, out=None, lse=None, stream=None):
+                 sm_scale=None, out=None, lse=None, stream=None, k_scale=None, v_scale=None):
         import torch
         sh = self.shape
+        fp8 = k_cache.dtype == torch.uint8
+        if fp8 != (v_cache.dtype == torch.uint8) or fp8 != (k_scale is not None) \
+                or fp8 != (v_scale is not None):
+            raise ValueError("fp8 caches are uint8 (both) and need k_scale and v_scale")
         hq = sh.kv_heads * sh.group
         D = sh.head_dim
         for t, name in ((q, "q"), (gate, "gate")):
@@ -532,8 +540,8 @@ class SparseAttn:
                 raise ValueError(f"{name} must be contiguous bf16 {(sh.rows, hq, D)}")
         for t, name, st in ((k_cache, "k_cache", (sh.k_slot_stride, sh.k_head_stride)),
                             (v_cache, "v_cache", (sh.v_slot_stride, sh.v_head_stride))):
-            if t.dtype != torch.bfloat16 or not t.is_cuda or t.dim() != 3:
-                raise ValueError(f"{name} must be a 3-d bf16 device tensor")
+            if t.dtype not in (torch.bfloat16, torch.uint8) or not t.is_cuda or t.dim() != 3:
+                raise ValueError(f"{name} must be a 3-d bf16 or uint8 device tensor")
             if t.shape[0] < sh.num_slots or t.shape[1] != sh.kv_heads or t.shape[2] != D:
                 raise ValueError(f"{name} shape {tuple(t.shape)} does not hold "
                                  f"{(sh.num_slots, sh.kv_heads, D)}")
@@ -561,10 +569,17 @@ class SparseAttn:
             raise ValueError(f"lse must be contiguous float32 {(sh.rows, hq)}")
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        self._check(load().dsa_sparse_attn(
-            self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(token_ids), _ptr(page_table),
-            _ptr(gate), ctypes.c_float(sm_scale), _ptr(out), _ptr(lse),
-            ctypes.c_void_p(stream.cuda_stream)))
+        if fp8:
+            self._check(load().dsa_sparse_attn_fp8(
+                self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache), ctypes.c_float(k_scale),
+                ctypes.c_float(v_scale), _ptr(token_ids), _ptr(page_table), _ptr(gate),
+                ctypes.c_float(sm_scale), _ptr(out), _ptr(lse),
+                ctypes.c_void_p(stream.cuda_stream)))
+        else:
+            self._check(load().dsa_sparse_attn(
+                self._h, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(token_ids),
+                _ptr(page_table), _ptr(gate), ctypes.c_float(sm_scale), _ptr(out), _ptr(lse),
+                ctypes.c_void_p(stream.cuda_stream)))
         return out
 
     def close(self) -> None:

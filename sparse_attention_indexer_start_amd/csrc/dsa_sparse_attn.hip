@@ -50,8 +50,8 @@ constexpr float NEG_INF = -__builtin_huge_valf();
 
 struct Args {
   const uint16_t* q;
-  const uint16_t* kc;
-  const uint16_t* vc;
+  const void* kc;       // bf16 or E4M3 codes
+  const void* vc;
   const int32_t* ids;
   const int32_t* table;
   const uint16_t* gate;
@@ -64,10 +64,43 @@ struct Args {
   int64_t k_ss, k_hs, v_ss, v_hs, num_slots;
   int32_t rows, hkv, G, K, rows_per_seq, page_shift, pps, chunks, spc;
   int32_t hw;           // kv heads per workgroup (1, 2 or 4; divides hkv)
-  float c2;             // sm_scale * log2(e)
+  float c2;             // sm_scale * log2(e) (times k_scale for fp8 caches)
+  float vscale;         // v_scale for fp8 caches, else 1
 };
 
 SA_DEV uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Eight cache elements at an element offset, as the raw bits a load returns
+// and as eight bf16 (E4M3 converts to bf16 exactly; the hardware conversion
+// with a unit scale was checked on all 256 codes).
+template <bool FP8>
+struct KV;
+template <>
+struct KV<false> {
+  typedef uint4 raw;
+  static SA_DEV raw ld(const void* base, int64_t off) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+  }
+  static SA_DEV uint4 bf(raw r) { return r; }
+  static SA_DEV raw zero() { return make_uint4(0, 0, 0, 0); }
+};
+template <>
+struct KV<true> {
+  typedef uint2 raw;
+  static SA_DEV raw ld(const void* base, int64_t off) {
+    return *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(base) + off);
+  }
+  template <bool HI>
+  static SA_DEV uint32_t pk(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  }
+  static SA_DEV uint4 bf(raw r) {
+    return make_uint4(pk<false>(r.x), pk<true>(r.x), pk<false>(r.y), pk<true>(r.y));
+  }
+  static SA_DEV raw zero() { return make_uint2(0, 0); }
+};
 
 // Cache slot of position `pos` of sequence `seq`; -1 for padding (pos < 0) and
 // for positions that are not addressable (`bad` is then set).
@@ -120,7 +153,7 @@ struct __align__(16) Smem {
 
 // Normalise, gate and store four consecutive dimensions of one head.
 SA_DEV void store_out(const Args& a, int row, int h, int d, float4 o, float L, float M, int D) {
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float inv = L > 0.f ? a.vscale / L : 0.f;
   float v[4] = {o.x * inv, o.y * inv, o.z * inv, o.w * inv};
   const int hq = a.hkv * a.G;
   const int64_t base = ((int64_t)row * hq + h) * D + d;
@@ -138,8 +171,9 @@ SA_DEV void store_out(const Args& a, int row, int h, int d, float4 o, float L, f
     a.lse[(int64_t)row * hq + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : NEG_INF;
 }
 
-template <int D>
+template <int D, bool FP8>
 __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
+  typedef KV<FP8> T;
   constexpr int KS = D / 32;      // 32-dimension steps of q.k
   constexpr int NC = D / 128;     // 128-dimension halves of V
   constexpr int OT = D / 16;      // 16-dimension output tiles
@@ -184,8 +218,6 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   const int steps = (a.K + STEP - 1) / STEP;
   const int st0 = chunk * a.spc, st1 = min(steps, st0 + a.spc);
   const int32_t* idrow = a.ids + (int64_t)row * a.K;
-  const uint16_t* kbase = a.kc + (int64_t)g * a.k_hs;
-  const uint16_t* vbase = a.vc + (int64_t)g * a.v_hs;
 
   for (int st = st0 + wi; st < st1; st += wph) {
     const int tix = st * STEP + (lane & 31);
@@ -200,30 +232,30 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
       sv[e] = __shfl(slot, 4 * j + e);
       sv[4 + e] = __shfl(slot, 16 + 4 * j + e);
     }
-    uint4 ka[KS], kb[KS];
+    typename T::raw ka[KS], kb[KS];
     {
-      const uint16_t* p0 = kbase + (int64_t)max(sk0, 0) * a.k_ss + 8 * j;
-      const uint16_t* p1 = kbase + (int64_t)max(sk1, 0) * a.k_ss + 8 * j;
+      const int64_t o0 = (int64_t)max(sk0, 0) * a.k_ss + (int64_t)g * a.k_hs + 8 * j;
+      const int64_t o1 = (int64_t)max(sk1, 0) * a.k_ss + (int64_t)g * a.k_hs + 8 * j;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        ka[s] = sk0 >= 0 ? ld16(p0 + 32 * s) : make_uint4(0, 0, 0, 0);
-        kb[s] = sk1 >= 0 ? ld16(p1 + 32 * s) : make_uint4(0, 0, 0, 0);
+        ka[s] = sk0 >= 0 ? T::ld(a.kc, o0 + 32 * s) : T::zero();
+        kb[s] = sk1 >= 0 ? T::ld(a.kc, o1 + 32 * s) : T::zero();
       }
     }
-    uint4 vq[8][NC];
+    typename T::raw vr[8][NC];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint16_t* vp = vbase + (int64_t)max(sv[e], 0) * a.v_ss + 8 * n;
+      const int64_t ov = (int64_t)max(sv[e], 0) * a.v_ss + (int64_t)g * a.v_hs + 8 * n;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) vq[e][c] = sv[e] >= 0 ? ld16(vp + 128 * c) : make_uint4(0, 0, 0, 0);
+      for (int c = 0; c < NC; ++c) vr[e][c] = sv[e] >= 0 ? T::ld(a.vc, ov + 128 * c) : T::zero();
     }
     // Scores S^T[token][head]: lane (n, j) receives tokens 4j + r and 16 + 4j + r.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka[s]),
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T::bf(ka[s])),
                                                    __builtin_bit_cast(bf16x8, qr[s]), s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[s]),
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, T::bf(kb[s])),
                                                    __builtin_bit_cast(bf16x8, qr[s]), s1, 0, 0, 0);
     }
     float sc[8];
@@ -258,6 +290,11 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
     pw.z = f2bf(p[4]) | (f2bf(p[5]) << 16);
     pw.w = f2bf(p[6]) | (f2bf(p[7]) << 16);
     const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+    uint4 vq[8][NC];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vq[e][c] = T::bf(vr[e][c]);
     // O^T[dim][head] += V^T P^T.  Tile (c, i) holds dimensions 128c + 8m + i
     // (m = row of the tile); its A operand on lane (m = n, j) is the eight
     // tokens' values of dimension 128c + 8n + i, regrouped from vq.
@@ -511,18 +548,26 @@ int dsa_sparse_attn_chunks(const dsa_attn_ctx* c) {
   return c->chunks;
 }
 
-int dsa_sparse_attn(dsa_attn_ctx* c, const uint16_t* q, const uint16_t* k_cache,
-                    const uint16_t* v_cache, const int32_t* token_ids,
-                    const int32_t* page_table, const uint16_t* gate, float sm_scale,
-                    uint16_t* out, float* lse, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int sa_launch(dsa_attn_ctx* c, const uint16_t* q, const void* k_cache, const void* v_cache,
+              bool fp8, float k_scale, float v_scale, const int32_t* token_ids,
+              const int32_t* page_table, const uint16_t* gate, float sm_scale, uint16_t* out,
+              float* lse, hipStream_t stream) {
   if (!c || c->magic != SA_MAGIC) return sa_fail(DSA_ERR_INVALID_ARG, "bad context");
   const dsa_attn_shape& s = c->sh;
   if (s.rows == 0) return DSA_OK;
   if (!q || !k_cache || !v_cache || !token_ids || !out)
     return sa_fail(DSA_ERR_INVALID_ARG, "q, k_cache, v_cache, token_ids and out must be non-null");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)out & 7u) ||
-      (gate && ((uintptr_t)gate & 7u)))
-    return sa_fail(DSA_ERR_INVALID_ARG, "q and the caches must be 16-byte aligned, out and gate 8-byte aligned");
+  const uintptr_t cache_align = fp8 ? 7u : 15u;
+  if (!aligned16(q) || ((uintptr_t)k_cache & cache_align) || ((uintptr_t)v_cache & cache_align) ||
+      ((uintptr_t)out & 7u) || (gate && ((uintptr_t)gate & 7u)))
+    return sa_fail(DSA_ERR_INVALID_ARG, "q must be 16-byte aligned, the caches 16-byte (bf16) or "
+                   "8-byte (fp8) aligned, out and gate 8-byte aligned");
+  if (fp8 && (!std::isfinite(k_scale) || !std::isfinite(v_scale)))
+    return sa_fail(DSA_ERR_INVALID_ARG, "k_scale and v_scale must be finite");
   if (page_table && s.pages_per_seq < 1)
     return sa_fail(DSA_ERR_INVALID_ARG, "a page table needs pages_per_seq >= 1");
   if (!std::isfinite(sm_scale)) return sa_fail(DSA_ERR_INVALID_ARG, "sm_scale must be finite");
@@ -542,15 +587,40 @@ int dsa_sparse_attn(dsa_attn_ctx* c, const uint16_t* q, const uint16_t* k_cache,
   a.page_shift = shift;
   a.pps = s.pages_per_seq;
   a.chunks = c->chunks; a.spc = c->spc; a.hw = c->hw;
-  a.c2 = sm_scale * 1.4426950408889634f;
+  a.c2 = sm_scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
+  a.vscale = fp8 ? v_scale : 1.0f;
   const unsigned grid = (unsigned)((int64_t)s.rows * (s.kv_heads / c->hw) * c->chunks);
-  if (s.head_dim == 256)
-    hipLaunchKernelGGL(k_sparse_attn<256>, dim3(grid), dim3(NT), 0, stream, a);
-  else
-    hipLaunchKernelGGL(k_sparse_attn<128>, dim3(grid), dim3(NT), 0, stream, a);
+  if (s.head_dim == 256) {
+    if (fp8) hipLaunchKernelGGL((k_sparse_attn<256, true>), dim3(grid), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((k_sparse_attn<256, false>), dim3(grid), dim3(NT), 0, stream, a);
+  } else {
+    if (fp8) hipLaunchKernelGGL((k_sparse_attn<128, true>), dim3(grid), dim3(NT), 0, stream, a);
+    else hipLaunchKernelGGL((k_sparse_attn<128, false>), dim3(grid), dim3(NT), 0, stream, a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sa_hip(e, "launch k_sparse_attn");
   return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_sparse_attn(dsa_attn_ctx* c, const uint16_t* q, const uint16_t* k_cache,
+                    const uint16_t* v_cache, const int32_t* token_ids,
+                    const int32_t* page_table, const uint16_t* gate, float sm_scale,
+                    uint16_t* out, float* lse, hipStream_t stream) {
+  return sa_launch(c, q, k_cache, v_cache, false, 1.0f, 1.0f, token_ids, page_table, gate,
+                   sm_scale, out, lse, stream);
+}
+
+int dsa_sparse_attn_fp8(dsa_attn_ctx* c, const uint16_t* q, const uint8_t* k_cache,
+                        const uint8_t* v_cache, float k_scale, float v_scale,
+                        const int32_t* token_ids, const int32_t* page_table,
+                        const uint16_t* gate, float sm_scale, uint16_t* out, float* lse,
+                        hipStream_t stream) {
+  return sa_launch(c, q, k_cache, v_cache, true, k_scale, v_scale, token_ids, page_table, gate,
+                   sm_scale, out, lse, stream);
 }
 
 int dsa_sparse_attn_read_status(dsa_attn_ctx* c, uint32_t* status) {

@@ -25,7 +25,7 @@ def declared_functions():
     names = set()
     for h in HEADERS:
         text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names.update(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text))
+        names.update(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", text))
     return sorted(names)
 
 

@@ -54,11 +54,19 @@ def _f(codes):
     return (codes.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
+def _cache_dev(a):
+    """A host cache (bf16 codes or E4M3 bytes) on the device."""
+    import torch
+    if a.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    return _bf(a)
+
+
 def _run(case, k_dev=None, v_dev=None, chunks=0, with_gate=True, with_lse=True, graph=False):
     import torch
     hq = case.kv_heads * case.group
-    kd = _bf(case.k_cache) if k_dev is None else k_dev
-    vd = _bf(case.v_cache) if v_dev is None else v_dev
+    kd = _cache_dev(case.k_cache) if k_dev is None else k_dev
+    vd = _cache_dev(case.v_cache) if v_dev is None else v_dev
     pps = 0 if case.page_table is None else case.page_table.shape[1]
     op = binding.SparseAttn(case.rows, case.kv_heads, case.group, case.head_dim, case.k_tokens,
                             case.num_slots, rows_per_seq=case.rows_per_seq,
@@ -71,11 +79,13 @@ def _run(case, k_dev=None, v_dev=None, chunks=0, with_gate=True, with_lse=True, 
     table = None if case.page_table is None else torch.from_numpy(case.page_table).cuda()
     out = torch.empty((case.rows, hq, case.head_dim), dtype=torch.bfloat16, device="cuda")
     lse = torch.full((case.rows, hq), float("nan"), device="cuda") if with_lse else None
-    op(q, kd, vd, ids, table, gate, case.sm_scale, out, lse)
+    op(q, kd, vd, ids, table, gate, case.sm_scale, out, lse, k_scale=case.k_scale,
+       v_scale=case.v_scale)
     torch.cuda.synchronize()
     status = op.read_status()
     gh.log(f"  attention: {case.rows} rows, {case.kv_heads}x{case.group} heads, D={case.head_dim}, "
-           f"K={case.k_tokens}, {op.chunks()} chunks, status {status}")
+           f"K={case.k_tokens}, {'fp8' if case.kv_fp8 else 'bf16'} K/V, {op.chunks()} chunks, "
+           f"status {status}")
     op.close()
     return _codes(out), (None if lse is None else lse.cpu().numpy()), status
 
@@ -84,12 +94,18 @@ def _check(case, got_codes, got_lse, rows=None, with_gate=True):
     gate = case.gate if with_gate else None
     args = (case.q, case.k_cache, case.v_cache, case.token_ids, case.sm_scale, case.group,
             case.page_table, case.page_size, case.rows_per_seq)
-    ref, ref_lse, bad = so.sparse_attention(*args, gate=gate, rows=rows)
-    vabs = case.v_cache & np.uint16(0x7FFF)
-    A, _, _ = so.sparse_attention(case.q, case.k_cache, vabs, *args[3:], gate=gate, rows=rows)
+    sc = dict(k_scale=case.k_scale, v_scale=case.v_scale)
+    ref, ref_lse, bad = so.sparse_attention(*args, gate=gate, rows=rows, **sc)
+    sign_off = np.uint8(0x7F) if case.kv_fp8 else np.uint16(0x7FFF)
+    A, _, _ = so.sparse_attention(case.q, case.k_cache, case.v_cache & sign_off, *args[3:],
+                                  gate=gate, rows=rows, **sc)
     got = _f(got_codes)
     rows = range(case.rows) if rows is None else rows
-    kd = so.bf16_decode(case.k_cache)
+    if case.kv_fp8:
+        from oracle import indexer_oracle
+        kd = indexer_oracle.e4m3_decode(case.k_cache) * case.k_scale
+    else:
+        kd = so.bf16_decode(case.k_cache)
     for r in rows:
         tol = 2.0 ** -7 * A[r] + 2.0 ** -8 * np.abs(ref[r])
         err = np.abs(got[r] - ref[r])
@@ -214,13 +230,8 @@ def test_attn_graph_replay_with_new_ids():
 
 
 def _device_caches(case):
-    import torch
-    gen = torch.Generator(device="cuda")
-    gen.manual_seed(int(case.cache_seed))
-    shape = (case.num_slots, case.kv_heads, case.head_dim)
-    k = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
-    v = torch.randn(shape, generator=gen, device="cuda", dtype=torch.bfloat16)
-    return k, v
+    import bench
+    return bench.attn_device_caches(case)
 
 
 def _gathered_case(case, kd, vd, rows):
@@ -236,16 +247,20 @@ def _gathered_case(case, kd, vd, rows):
         ids[i, :len(s)] = np.arange(len(slots), len(slots) + len(s))
         slots.extend(s)
     idx = torch.tensor(slots if slots else [0], dtype=torch.int64, device="cuda")
-    kc = _codes(kd.index_select(0, idx))
-    vc = _codes(vd.index_select(0, idx))
+    if case.kv_fp8:
+        kc = kd.index_select(0, idx).cpu().numpy()
+        vc = vd.index_select(0, idx).cpu().numpy()
+    else:
+        kc = _codes(kd.index_select(0, idx))
+        vc = _codes(vd.index_select(0, idx))
     rows = list(rows)
     return wl.AttnCase("gathered", case.q[rows], kc, vc, ids, None, 1, 1,
                        None if case.gate is None else case.gate[rows], case.kv_heads,
                        case.group, case.head_dim, case.sm_scale, max(1, len(slots)),
-                       case.seq_lens)
+                       case.seq_lens, k_scale=case.k_scale, v_scale=case.v_scale)
 
 
-@pytest.mark.parametrize("name", ["attn_decode", "attn_c1"])
+@pytest.mark.parametrize("name", ["attn_decode", "attn_c1", "attn_decode_fp8"])
 def test_attn_full_size_sampled_rows(name):
     import torch
     case = wl.make_attn_config(name)
@@ -265,6 +280,19 @@ def test_attn_full_size_sampled_rows(name):
     assert np.array_equal(np.isfinite(lse).all(1), valid > 0)
     del kd, vd
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("D,G,hkv,K,chunks", [
+    (256, 12, 2, 2048, 0), (256, 3, 1, 300, 4), (128, 16, 2, 700, 0), (128, 5, 3, 33, 1),
+])
+def test_attn_fp8_caches(D, G, hkv, K, chunks):
+    rng = np.random.default_rng(D + G + K)
+    lens = rng.integers(1, 3 * K + 40, size=3)
+    case = wl.make_attn_custom(lens, 2, hkv, G, D, K, page_size=32, seed=G + K, q_scale=0.5,
+                               kv_fp8=True)
+    got, lse, status = _run(case, chunks=chunks)
+    assert status == 0
+    _check(case, got, lse)
 
 
 def test_attn_rejects_unsupported_shapes():
