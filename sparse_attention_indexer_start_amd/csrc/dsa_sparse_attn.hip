@@ -219,10 +219,19 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   const int st0 = chunk * a.spc, st1 = min(steps, st0 + a.spc);
   const int32_t* idrow = a.ids + (int64_t)row * a.K;
 
-  for (int st = st0 + wi; st < st1; st += wph) {
+  // Token position of step st for this lane (-1 past the chunk or the list).
+  auto pos_of = [&](int st) -> int {
     const int tix = st * STEP + (lane & 31);
-    const int slot = tix < a.K ? slot_of(a, seq, idrow[tix], bad) : -1;
-    if (__ballot(slot >= 0) == 0) continue;       // nothing to attend in this step
+    return (st < st1 && tix < a.K) ? idrow[tix] : -1;
+  };
+  // The next step's id is loaded while this step's K/V loads are in flight,
+  // so a step waits for two memory round trips (page table, K/V) instead of
+  // three.
+  int pos = pos_of(st0 + wi);
+  for (int st = st0 + wi; st < st1; st += wph) {
+    const int slot = slot_of(a, seq, pos, bad);
+    pos = pos_of(st + wph);
+    if (__ballot(slot >= 0) == 0) continue;        // nothing to attend in this step
     // Slots of this lane's tokens: K rows n and 16 + n; V and score tokens
     // 4j + e and 16 + 4j + e (e < 4).
     const int sk0 = __shfl(slot, n), sk1 = __shfl(slot, 16 + n);
