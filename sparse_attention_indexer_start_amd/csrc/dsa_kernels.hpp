@@ -737,7 +737,11 @@ DSA_DEV void mask_dropped_short(float* rowp, int64_t cs, int B, int L, int nlb, 
 // ---------------------------------------------------------------------------
 // A row with nlb <= LIST_CAP: the whole chain in one workgroup, keys in LDS.
 // ---------------------------------------------------------------------------
-template <int BS>
+// FUSE_TOK: the token top-k in closed form inside the block emit pass (see
+// below).  It costs registers, so it is compiled into the balanced-split
+// kernel (decode batches) only; without it the short-row path of the
+// per-row-split kernel stays free of scratch.
+template <int BS, bool FUSE_TOK>
 DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
   float* rowp = row_ptr(p, r, rb);
   const bool vec = vec_ok(p, rowp);
@@ -787,7 +791,7 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
     // fill sits at position c - s (every block before it is taken whole).
     const int Kt = min(p.k_tokens, L);
     const int64_t C = (int64_t)(Kp - 1) * B + (L - (int64_t)(nlb - 1) * B);
-    const bool fuse_tok = no_low && T < KEY_POS_INF && L > p.k_tokens && C <= Kt;
+    const bool fuse_tok = FUSE_TOK && no_low && T < KEY_POS_INF && L > p.k_tokens && C <= Kt;
     const int64_t qt = (int64_t)Kt - C;
     int32_t* tout = p.token_ids + (int64_t)r * p.k_tokens;
     const int32_t s32 = (int32_t)rb.s;
@@ -1575,14 +1579,14 @@ DSA_DEV void final_wg(const Params& p, int r, const Row& rb, int npieces, Smem& 
 // The fused kernel.  Grid index g + phase_base < G: pass 1 (and the whole of
 // a short row); otherwise pass 2.
 // ---------------------------------------------------------------------------
-template <int BS>
+template <int BS, bool FUSE_TOK>
 DSA_DEV void own_short_row(const Params& p, int r, const Row& rb, Smem& sm) {
   if (rb.bad && threadIdx.x == 0) atomicOr(p.status, 1u);
   if (rb.L == 0) {
     write_empty_row(p, r);
     return;
   }
-  small_row<BS>(p, r, rb, sm);
+  small_row<BS, FUSE_TOK>(p, r, rb, sm);
 }
 
 // sm.pfx[0..rows]: blocks of long rows before each row; sm.row_s / row_L:
@@ -1696,7 +1700,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   const Row rb = row_bounds(p, r);
   if (p.one_group(rb.nlb, rb.L) || rb.L == 0) {
     if (pass2 || part != 0) return;
-    own_short_row<BS>(p, r, rb, sm);
+    own_short_row<BS, false>(p, r, rb, sm);
     return;
   }
   int b0, b1;
@@ -1711,7 +1715,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void k_
   int g = (int)blockIdx.x + p.phase_base;
   if (g < p.rows) {
     const Row rb = row_bounds(p, g);
-    if (p.one_group(rb.nlb, rb.L) || rb.L == 0) own_short_row<BS>(p, g, rb, sm);
+    if (p.one_group(rb.nlb, rb.L) || rb.L == 0) own_short_row<BS, true>(p, g, rb, sm);
     return;
   }
   g -= p.rows;
