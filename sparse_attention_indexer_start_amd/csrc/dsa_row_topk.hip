@@ -10,23 +10,26 @@
 //
 // Each row is cut into P pieces (P fixed by the shape and the CU count; the
 // pieces follow the row's own live length), and every step is a launch of its
-// own on the caller's stream, so no workgroup ever waits on another:
+// own on the caller's stream:
 //   hist  (rows x P, three launches)  a 12-, 12- then 8-bit digit histogram
 //         of the pieces' keys (only keys matching the digits found so far),
-//         merged into the row's histogram with atomics; the last piece of the
-//         row to arrive finds the digit holding the K-th key.  After the
-//         third digit (or once a whole bin is taken) the row's rule (T, q) is
-//         fixed: keep key > T, and the first q keys equal to T in column
-//         order.  The third pass also keeps each piece's counts above every
-//         last digit, so its finder can place every piece's output at once;
-//   count (rows x P)  only for rows settled before the third digit: each
-//         piece's keys above and equal to T, the last to arrive placing the
-//         pieces;
+//         merged into the row's histogram of that digit with atomics.  Each
+//         piece of the next launch finds the previous digit itself from that
+//         histogram (all find the same one), so no piece waits for another.
+//         The third launch also keeps each piece's suffix counts over the
+//         last digit.  A row whose K-th key's bin is taken whole is settled
+//         early: keep every key from that bin up;
+//   count (rows x P)  places every piece's output: from the suffix counts
+//         after three digits (no read of the row), or, for a row settled
+//         early, from each piece's keys above and equal to T, the last piece
+//         to arrive placing the pieces;
 //   emit  (rows x P)  each piece's kept columns, in column order, and the -1
 //         padding.
-// Passes whose row is already settled return at once.  The workspace (one
-// histogram, a few state words, per-piece counts and the third pass's
-// per-piece suffix counts, per row) does not depend on the row length.
+// The rule is: keep key > T, and the first q keys equal to T in column
+// order.  Each digit's histogram is cleared by a later launch that no longer
+// reads it, so consecutive calls and graph replays need no clearing launch.
+// The workspace (three histograms, a few state words, per-piece counts and
+// suffix counts, per row) does not depend on the row length.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -45,9 +48,13 @@ namespace rt {
 constexpr int NT = 512;
 constexpr int MIN_PIECE = 8192;   // columns per piece at least (when the row has them)
 constexpr int SFX = 257;          // per-piece suffix counts of the last digit, and the sentinel
-// State words of a row.  [0] prefix [1] krem [2] done [3] T [4] q [5] Kt
-// [6] pieces placed (offsets written by the third pass) [7] arrival ticket
+constexpr int ROW_HIST = 2 * HIST_WORDS + 256;   // the three digits' histograms of a row
+// State words of a row.  [0] prefix [1] krem [2] mode [3] T [4] q [5] Kt
+// [7] arrival ticket of the count pass
 constexpr int STATE = 8;
+// Row modes: selection running; empty; every column kept; settled before the
+// third digit (the count pass places the pieces).
+constexpr uint32_t M_RUN = 0, M_EMPTY = 1, M_ALL = 2, M_COUNT = 3;
 
 struct Args {
   const float* logits;
@@ -56,7 +63,7 @@ struct Args {
   int32_t* out;
   int64_t width, row_stride, col_stride;
   int32_t rows, k, starts_repeat, ends_repeat, P, pass;
-  uint32_t* hist;    // [rows][4096]
+  uint32_t* hist;    // [rows][ROW_HIST]  first, second and last digit histograms
   uint32_t* state;   // [rows][STATE]
   uint32_t* cnt;     // [rows][P][2]  keys above T, keys equal to T
   uint32_t* off;     // [rows][P][2]  output offset, ties taken
@@ -237,6 +244,13 @@ DSA_DEV bool last_piece(uint32_t* ticket, int P, uint32_t* misc) {
   return misc[3] != 0;
 }
 
+// Words [0, n) of a row's buffer that piece j of P clears.
+DSA_DEV void clear_slice(uint32_t* buf, int n, int P, int j) {
+  const int per = (n + P - 1) / P;
+  const int b0 = min(n, j * per), b1 = min(n, b0 + per);
+  for (int i = b0 + (int)threadIdx.x; i < b1; i += NT) buf[i] = 0u;
+}
+
 __global__ __launch_bounds__(NT) void k_rt_hist(Args a) {
   __shared__ uint32_t h[HIST_WORDS];
   __shared__ uint32_t wv[NT / 64];
@@ -244,23 +258,44 @@ __global__ __launch_bounds__(NT) void k_rt_hist(Args a) {
   const int r = (int)(blockIdx.x / (unsigned)a.P), j = (int)(blockIdx.x % (unsigned)a.P);
   const Live lv = live_range(a, r);
   uint32_t* st = a.state + (int64_t)r * STATE;
+  uint32_t* h0 = a.hist + (int64_t)r * ROW_HIST;
+  uint32_t* h1 = h0 + HIST_WORDS;
+  uint32_t* h2 = h1 + HIST_WORDS;
   const int64_t Kt = min((int64_t)a.k, lv.L);
   uint32_t prefix = 0, krem = (uint32_t)Kt;
   if (a.pass == 0) {
-    if (lv.L == 0 || Kt == lv.L) {
-      // Nothing to select: an empty row keeps nothing, a short one everything.
+    clear_slice(h2, 256, a.P, j);          // the last call's third digit
+    const uint32_t mode = lv.L == 0 ? M_EMPTY : (Kt == lv.L ? M_ALL : M_RUN);
+    if (j == 0 && threadIdx.x == 0) {
+      st[0] = 0; st[1] = (uint32_t)Kt; st[2] = mode; st[5] = (uint32_t)Kt;
+    }
+    if (mode != M_RUN) return;
+  } else {
+    if (a.pass == 2) clear_slice(h0, HIST_WORDS, a.P, j);   // no longer read
+    if (st[2] != M_RUN) return;
+    if (a.pass == 2) {
+      prefix = st[0];
+      krem = st[1];
+    }
+    // The previous digit, from the previous pass's histogram (every piece
+    // finds the same one).
+    uint32_t d, above, in_bin;
+    find_digit(a.pass == 1 ? h0 : h1, HIST_WORDS, krem, wv, misc, d, above, in_bin);
+    prefix |= d << (a.pass == 1 ? 20 : 8);
+    krem -= above;
+    if (in_bin == krem) {
+      // the whole bin is kept: every key from the bin's lowest value up
       if (j == 0 && threadIdx.x == 0) {
-        st[0] = 0; st[1] = 0; st[2] = 1;
-        st[3] = lv.L == 0 ? 0xFFFFFFFFu : 0u;
-        st[4] = lv.L == 0 ? 0u : 0xFFFFFFFFu;
-        st[5] = (uint32_t)Kt; st[6] = 0;
+        st[2] = M_COUNT;
+        st[3] = prefix == 0 ? 0u : prefix - 1;
+        st[4] = prefix == 0 ? 0xFFFFFFFFu : 0u;
       }
       return;
     }
-  } else {
-    if (st[2]) return;                    // the rule is already fixed
-    prefix = st[0];
-    krem = st[1];
+    if (j == 0 && threadIdx.x == 0) {
+      st[0] = prefix;
+      st[1] = krem;
+    }
   }
   for (int i = threadIdx.x; i < HIST_WORDS; i += NT) h[i] = 0;
   __syncthreads();
@@ -286,63 +321,26 @@ __global__ __launch_bounds__(NT) void k_rt_hist(Args a) {
   if (a.pass == 2) (void)block_excl_scan(above, wv, tot_above);
   __syncthreads();
   const int nb = a.pass == 2 ? 256 : HIST_WORDS;
-  uint32_t* gh = a.hist + (int64_t)r * HIST_WORDS;
+  uint32_t* gh = a.pass == 0 ? h0 : (a.pass == 1 ? h1 : h2);
   for (int i = threadIdx.x; i < nb; i += NT)
     if (h[i]) atomicAdd(&gh[i], h[i]);
   if (a.pass == 2) {
-    // Suffix counts: S[b] = keys above the prefix + keys of digits >= b.
+    // Suffix counts: S[b] = keys above the prefix + keys of last digits >= b.
     uint32_t* sp = a.sfx + ((int64_t)r * a.P + j) * SFX;
     const uint32_t x = threadIdx.x < 256 ? h[255 - threadIdx.x] : 0u;
     uint32_t t2;
     const uint32_t ex = block_excl_scan(x, wv, t2);   // over digits 255, 254, ...
-    if (threadIdx.x < 256) st_shared(&sp[255 - threadIdx.x], tot_above + ex + x);
-    if (threadIdx.x == 0) st_shared(&sp[256], tot_above);
-  }
-  if (!last_piece(&st[7], a.P, misc)) return;
-
-  // The row's last piece: its digit.
-  for (int i = threadIdx.x; i < nb; i += NT) {
-    h[i] = ld_shared(&gh[i]);
-    st_shared(&gh[i], 0u);                // cleared for the next pass and call
-  }
-  __syncthreads();
-  uint32_t d, ab, in_bin;
-  find_digit(h, nb, krem, wv, misc, d, ab, in_bin);
-  const int shift = a.pass == 0 ? 20 : (a.pass == 1 ? 8 : 0);
-  prefix |= d << shift;
-  krem -= ab;
-  uint32_t done = 0, T = 0, q = 0, placed = 0;
-  if (a.pass == 2) {
-    done = 1;
-    T = prefix;
-    q = krem;
-    // Every piece's keys above T and equal to T, from its suffix counts.
-    place_pieces(a, r, q, wv, [&](int jj, uint32_t& gt, uint32_t& eq) {
-      const uint32_t* sp = a.sfx + ((int64_t)r * a.P + jj) * SFX;
-      const uint32_t ge = ld_shared(&sp[d]);
-      gt = ld_shared(&sp[d + 1]);
-      eq = ge - gt;
-    });
-    placed = 1;
-  } else if (in_bin == krem) {
-    // the whole bin is kept: every key from the bin's lowest value up
-    done = 1;
-    if (prefix == 0) {
-      T = 0;
-      q = 0xFFFFFFFFu;
-    } else {
-      T = prefix - 1;
-      q = 0;
-    }
-  }
-  if (threadIdx.x == 0) {
-    st[0] = prefix; st[1] = krem; st[2] = done; st[3] = T; st[4] = q;
-    st[5] = (uint32_t)Kt; st[6] = placed;
+    if (threadIdx.x < 256) sp[255 - threadIdx.x] = tot_above + ex + x;
+    if (threadIdx.x == 0) sp[256] = tot_above;
   }
 }
 
-// Rows settled before the third digit: each piece's keys above and equal to
-// T; the last piece to arrive places the pieces.
+// Places every piece's output.  Rows that ran three digits: the last digit
+// from the third histogram, and this piece's place from every piece's suffix
+// counts (keys above T in the pieces before it, then its share of the q ties
+// in column order); no read of the row.  Rows settled before the third
+// digit: each piece's keys above and equal to T, the last piece to arrive
+// placing the pieces.
 __global__ __launch_bounds__(NT) void k_rt_count(Args a) {
   __shared__ uint32_t wv[NT / 64];
   __shared__ uint32_t misc[8];
@@ -350,7 +348,32 @@ __global__ __launch_bounds__(NT) void k_rt_count(Args a) {
   const Live lv = live_range(a, r);
   if (lv.L == 0) return;
   uint32_t* st = a.state + (int64_t)r * STATE;
-  if (st[6]) return;                      // placed by the third pass
+  if (st[2] == M_RUN) {
+    const uint32_t* h2 = a.hist + (int64_t)r * ROW_HIST + 2 * HIST_WORDS;
+    uint32_t d, above, in_bin;
+    find_digit(h2, 256, st[1], wv, misc, d, above, in_bin);
+    const uint32_t q = st[1] - above;
+    const uint32_t* sf = a.sfx + (int64_t)r * a.P * SFX;
+    uint32_t gt = 0, eq = 0;
+    for (int i = threadIdx.x; i < j; i += NT) {
+      const uint32_t g1 = sf[(int64_t)i * SFX + d + 1];
+      gt += g1;
+      eq += sf[(int64_t)i * SFX + d] - g1;
+    }
+    uint32_t xg, xe;
+    (void)block_excl_scan(gt, wv, xg);
+    (void)block_excl_scan(eq, wv, xe);
+    if (threadIdx.x == 0) {
+      const uint32_t* me = sf + (int64_t)j * SFX;
+      const uint32_t before = min(xe, q);
+      uint32_t* op = a.off + ((int64_t)r * a.P + j) * 2;
+      op[0] = xg + before;
+      op[1] = min(me[d] - me[d + 1], q - before);
+      if (j == 0) st[3] = st[0] | d;
+    }
+    return;
+  }
+  if (st[2] != M_COUNT) return;
   const uint32_t T = st[3], q = st[4];
   int64_t c0, c1;
   piece_range(lv.L, a.P, j, c0, c1);
@@ -388,15 +411,25 @@ __global__ __launch_bounds__(NT) void k_rt_emit(Args a) {
     const int64_t p0 = Kt + min(n, (int64_t)j * per), p1 = Kt + min(n, ((int64_t)j + 1) * per);
     for (int64_t i = p0 + threadIdx.x; i < p1; i += NT) outp[i] = -1;
   }
+  uint32_t* h1 = a.hist + (int64_t)r * ROW_HIST + HIST_WORDS;
+  clear_slice(h1, HIST_WORDS, a.P, j);        // read by the third pass only
   if (lv.L == 0) return;
   const uint32_t* st = a.state + (int64_t)r * STATE;
-  const uint32_t T = st[3];
+  const uint32_t mode = st[2];
   const uint32_t kt = st[5];   // kept columns of the row (bounds every store below)
-  const uint32_t* op = a.off + ((int64_t)r * a.P + j) * 2;
-  uint32_t pos = op[0];
-  const uint32_t take = op[1];
   int64_t c0, c1;
   piece_range(lv.L, a.P, j, c0, c1);
+  uint32_t T, pos, take;
+  if (mode == M_ALL) {
+    T = 0;                     // every column kept, in order
+    pos = (uint32_t)c0;
+    take = 0xFFFFFFFFu;
+  } else {                     // placed by the count pass
+    T = st[3];
+    const uint32_t* op = a.off + ((int64_t)r * a.P + j) * 2;
+    pos = op[0];
+    take = op[1];
+  }
   const float* rowp = a.logits + (int64_t)r * a.row_stride + lv.s * a.col_stride;
   const int64_t cs = a.col_stride;
   const int32_t s32 = (int32_t)lv.s;
@@ -549,7 +582,7 @@ int dsa_row_topk_init(const dsa_topk_shape* s, int device, dsa_topk_ctx** out) {
   if (P * R > ((int64_t)1 << 31) - 1) { delete c; return rt_fail(DSA_ERR_UNSUPPORTED, "too many rows"); }
   c->P = (int)P;
   if (s->rows > 0 && s->width > 0) {
-    const int64_t words = R * dsa::HIST_WORDS + R * STATE + 2 * R * P + 2 * R * P + R * P * SFX;
+    const int64_t words = R * ROW_HIST + R * STATE + 2 * R * P + 2 * R * P + R * P * SFX;
     c->ws_bytes = (size_t)words * 4;
     e = hipMalloc(&c->ws, c->ws_bytes);
     if (e != hipSuccess) { delete c; return rt_hip(e, "hipMalloc(workspace)"); }
@@ -558,7 +591,7 @@ int dsa_row_topk_init(const dsa_topk_shape* s, int device, dsa_topk_ctx** out) {
     if (e != hipSuccess) { (void)hipFree(c->ws); delete c; return rt_hip(e, "hipMemset(workspace)"); }
     uint32_t* base = static_cast<uint32_t*>(c->ws);
     c->hist = base;
-    c->state = c->hist + R * dsa::HIST_WORDS;
+    c->state = c->hist + R * ROW_HIST;
     c->cnt = c->state + R * STATE;
     c->off = c->cnt + 2 * R * P;
     c->sfx = c->off + 2 * R * P;
