@@ -49,9 +49,14 @@ constexpr int NT = 512;
 constexpr int MIN_PIECE = 8192;   // columns per piece at least (when the row has them)
 constexpr int SFX = 257;          // per-piece suffix counts of the last digit, and the sentinel
 constexpr int ROW_HIST = 2 * HIST_WORDS + 256;   // the three digits' histograms of a row
-// State words of a row.  [0] prefix [1] krem [2] mode [3] T [4] q [5] Kt
-// [7] arrival ticket of the count pass
-constexpr int STATE = 8;
+// State words of a row.  [0] prefix [1] krem after the first digit, [2] mode,
+// [3] T [4] q [5] Kt, [7] arrival ticket of the count pass, [8] prefix [9]
+// krem after the second digit.  A pass reads only words that earlier
+// launches wrote: the pieces of one launch start at different times, so a
+// word one piece writes must not be one another piece of the launch reads
+// (the one exception, the mode set to "settled early", is a value every
+// piece of that launch reaches on its own).
+constexpr int STATE = 12;
 // Row modes: selection running; empty; every column kept; settled before the
 // third digit (the count pass places the pieces).
 constexpr uint32_t M_RUN = 0, M_EMPTY = 1, M_ALL = 2, M_COUNT = 3;
@@ -277,6 +282,7 @@ __global__ __launch_bounds__(NT) void k_rt_hist(Args a) {
       prefix = st[0];
       krem = st[1];
     }
+    uint32_t* out_pk = a.pass == 1 ? &st[0] : &st[8];
     // The previous digit, from the previous pass's histogram (every piece
     // finds the same one).
     uint32_t d, above, in_bin;
@@ -293,8 +299,8 @@ __global__ __launch_bounds__(NT) void k_rt_hist(Args a) {
       return;
     }
     if (j == 0 && threadIdx.x == 0) {
-      st[0] = prefix;
-      st[1] = krem;
+      out_pk[0] = prefix;
+      out_pk[1] = krem;
     }
   }
   for (int i = threadIdx.x; i < HIST_WORDS; i += NT) h[i] = 0;
@@ -351,8 +357,8 @@ __global__ __launch_bounds__(NT) void k_rt_count(Args a) {
   if (st[2] == M_RUN) {
     const uint32_t* h2 = a.hist + (int64_t)r * ROW_HIST + 2 * HIST_WORDS;
     uint32_t d, above, in_bin;
-    find_digit(h2, 256, st[1], wv, misc, d, above, in_bin);
-    const uint32_t q = st[1] - above;
+    find_digit(h2, 256, st[9], wv, misc, d, above, in_bin);
+    const uint32_t q = st[9] - above;
     const uint32_t* sf = a.sfx + (int64_t)r * a.P * SFX;
     uint32_t gt = 0, eq = 0;
     for (int i = threadIdx.x; i < j; i += NT) {
@@ -369,7 +375,7 @@ __global__ __launch_bounds__(NT) void k_rt_count(Args a) {
       uint32_t* op = a.off + ((int64_t)r * a.P + j) * 2;
       op[0] = xg + before;
       op[1] = min(me[d] - me[d + 1], q - before);
-      if (j == 0) st[3] = st[0] | d;
+      if (j == 0) st[3] = st[8] | d;
     }
     return;
   }
