@@ -156,3 +156,30 @@ def test_row_topk_graph_replay_changing_ends():
         want = _want(case.logits, None, np.array(new, np.int32), k)
         assert np.array_equal(out.cpu().numpy(), want), new
     op.close()
+
+
+def test_row_topk_replays_bit_identical():
+    """30 graph replays of a 16M-column row with k = 2^20 (all three digits
+    and the suffix-count placement), each equal to the oracle: a check on
+    anything that depends on when the pieces of one launch start."""
+    import torch
+    W, k = 16 * 2**20, 2**20
+    case = wl.make_custom(1, W, 8, 1, 1, [W - 3], seed=17, dup_frac=0.02)
+    buf = torch.from_numpy(case.buf).cuda()
+    ends = torch.from_numpy(case.ends).cuda()
+    op = binding.RowTopk(1, W, k)
+    out = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    op(buf, None, ends, out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        op(buf, None, ends, out)
+    torch.cuda.synchronize()
+    want = _want(case.logits, None, case.ends, k)
+    for it in range(30):
+        out.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want), f"replay {it} differs"
+    op.close()
