@@ -21,12 +21,11 @@
  * ranked by the order-preserving key (u >= 2^31 ? ~u : u | 2^31 on its bits):
  * infinities rank as values, a NaN ranks by its bit pattern.
  *
- * The context owns a workspace of (4096 + 8 + 4 P) words per row, P pieces
+ * The context owns a workspace of (8448 + 12 + 261 P) words per row, P pieces
  * per row fixed at init from the shape and the device's CU count (it does not
- * grow with the row length).  dsa_row_topk enqueues nine short launches on
- * `stream` (three digit passes of two launches each, then count, scan and
- * emit); it allocates nothing, never synchronizes and can be captured in a
- * HIP graph.  Calls on one context must be ordered on one stream.  Returns
+ * grow with the row length).  dsa_row_topk enqueues five launches on `stream`
+ * (three digit passes, the placement of every piece's output, the emit); it
+ * allocates nothing, never synchronizes and can be captured in a HIP graph.  Calls on one context must be ordered on one stream.  Returns
  * DSA_OK or a negative dsa_status (see dsa_select.h); the message is
  * dsa_row_topk_last_error().
  */
