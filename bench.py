@@ -310,8 +310,9 @@ def run_row_topk(rows: int, width: int, k: int, steps: int, warmup: int) -> dict
                 roofline={"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                           "basis": "4*L read + 4*k index stores + 8 B bounds per row over the "
-                                   "graph replay's time per call (the row is read up to five "
-                                   "times: three digit passes, count, emit)"})
+                                   "graph replay's time per call (the row is read four times: "
+                                   "three digit passes and the emit; a count pass reads it once "
+                                   "more only for rows settled before the third digit)"})
 
 
 def attn_device_caches(case):
