@@ -32,6 +32,11 @@ Readings taken where the pages print no formula:
   * fp8 caches (the page's other K/V format): K and V hold OCP E4M3 codes
     with one scale per tensor, K = e4m3(k) * k_scale and V = e4m3(v) *
     v_scale (decoded by the indexer oracle's pinned E4M3 decoder).
+  * A position a row lists more than once is attended once per listing,
+    unless ``distinct`` is set: then each row's ids are taken as a set, the
+    reading the grouped form of the LiteDSA page needs (it runs one product
+    over the union of neighbouring queries' selected positions, each query
+    keeping exactly its own set).
 """
 from __future__ import annotations
 
@@ -109,7 +114,7 @@ def sigmoid(x: np.ndarray) -> np.ndarray:
 
 def sparse_attention(q, k_cache, v_cache, token_ids, sm_scale: float, group: int,
                      page_table=None, page_size: int = 1, rows_per_seq: int = 1,
-                     gate=None, rows=None, k_scale=None, v_scale=None):
+                     gate=None, rows=None, k_scale=None, v_scale=None, distinct=False):
     """Outputs of the sparse attention.
 
     q: uint16 bf16 [R, Hkv * G, D]; k_cache, v_cache: uint16 bf16
@@ -117,6 +122,7 @@ def sparse_attention(q, k_cache, v_cache, token_ids, sm_scale: float, group: int
     (fp8 caches); token_ids: int32 [R, K] (positions, -1 pads);
     page_table: int32 [num_seqs, pages_per_seq] or None; gate: uint16 bf16
     [R, Hkv * G, D] or None.  ``rows`` limits the work to some rows.
+    ``distinct``: a position listed twice in one row is attended once.
 
     Returns (out float64 [R, Hq, D], lse float64 [R, Hq], bad int64 [R]);
     rows not computed are zero / -inf.
@@ -139,9 +145,14 @@ def sparse_attention(q, k_cache, v_cache, token_ids, sm_scale: float, group: int
     for r in (range(R) if rows is None else rows):
         seq = r // rows_per_seq
         slots = []
+        seen = set()
         for p in np.asarray(token_ids[r]).tolist():
             if p < 0:
                 continue                                  # padding
+            if distinct:
+                if p in seen:
+                    continue                              # listed before
+                seen.add(p)
             sl = slot_of(p, seq, page_table, page_size, num_slots)
             if sl < 0:
                 bad[r] += 1

@@ -80,6 +80,22 @@ def pin_two_tokens_worked(o):
     assert abs(lse[0, 0] - math.log(4.0)) < 1e-14
 
 
+def pin_repeated_ids(o):
+    """The two-token case with token 1 listed three times.  Taken as a set
+    (distinct) it is the same case: o = (1, 6), lse = ln 4.  Listed three
+    times it weighs 3 * 3 against 1: o = (4 / 10, 8 * 9 / 10), lse = ln 10."""
+    q = _b([[1.0, 0.0]])[None]
+    k = _cache([[0.0, 5.0], [1.0, 7.0]])
+    v = _cache([[4.0, 0.0], [0.0, 8.0]])
+    ids = np.array([[1, 0, -1, 1, 1]], np.int32)
+    out, lse, _ = o.sparse_attention(q, k, v, ids, math.log(3.0), 1, distinct=True)
+    assert np.allclose(out[0, 0], [1.0, 6.0], rtol=0, atol=1e-14), out
+    assert abs(lse[0, 0] - math.log(4.0)) < 1e-14
+    out, lse, _ = o.sparse_attention(q, k, v, ids, math.log(3.0), 1)
+    assert np.allclose(out[0, 0], [0.4, 7.2], rtol=0, atol=1e-14), out
+    assert abs(lse[0, 0] - math.log(10.0)) < 1e-14
+
+
 def pin_equal_scores_mean(o):
     """q = 0: every score is 0, o is the mean of the attended values, lse = ln 3
     (the two -1 pads are not attended)."""
@@ -249,6 +265,9 @@ MUTANTS = {
     "empty_lse_zero": ("return np.zeros((hg, d)), np.full(hg, -np.inf)",
                        "return np.zeros((hg, d)), np.zeros(hg)"),
     "bad_ids_read_last_slot": ("bad[r] += 1\n                continue", "bad[r] += 1"),
+    "distinct_ignored": ("                if p in seen:", "                if False:"),
+    "distinct_always": ("            if distinct:\n                if p in seen:",
+                        "            if True:\n                if p in seen:"),
     "fp8_scale_ignored": ("return e4m3_decode(cache[sl, g, :]) * float(scale)",
                           "return e4m3_decode(cache[sl, g, :])"),
 }
