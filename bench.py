@@ -17,8 +17,9 @@ The same run also times the long-decode workload (32 rows x 1M width, the
 bandwidth-bound case) under the key "long_decode", the fused FP8 indexer on a
 prefill chunk ("indexer_prefill"), the cooperative top-k of 16M-column rows
 ("row_topk") and the sparse attention over the selected tokens at decode
-("sparse_attn"), and the C oracle is timed on all host threads over whole
-passes of the default workload.
+("sparse_attn": per-row and, for the batch whose rows overlap, union mode),
+and the C oracle is timed on all host threads over whole passes of the
+default workload.
 
 Prints one JSON line.  ``--gpus`` above 1 is refused: this path runs on one GPU.
 """
@@ -339,14 +340,18 @@ def attn_device_caches(case):
 
 
 def run_attn(name: str, steps: int, warmup: int) -> dict:
-    """Graph replay of `steps` sparse-attention calls over a configuration."""
+    """Graph replay of `steps` sparse-attention calls over a configuration;
+    a name ending in ":union" runs it in union mode (each request's rows over
+    the union of their ids)."""
     import numpy as np
     import torch
     from sparse_attention_indexer_start_amd import binding
     from sparse_attention_indexer_start_amd import workloads as wl
 
+    base, _, mode = name.partition(":")
+    union = mode == "union"
     log(f"{name}: generating")
-    case = wl.make_attn_config(name)
+    case = wl.make_attn_config(base)
     dev = torch.device("cuda", 0)
     kd, vd = attn_device_caches(case)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
@@ -359,7 +364,8 @@ def run_attn(name: str, steps: int, warmup: int) -> dict:
     lse = torch.empty((case.rows, hq), dtype=torch.float32, device=dev)
     op = binding.SparseAttn(case.rows, case.kv_heads, case.group, case.head_dim, case.k_tokens,
                             case.num_slots, rows_per_seq=case.rows_per_seq,
-                            page_size=case.page_size, pages_per_seq=case.page_table.shape[1])
+                            page_size=case.page_size, pages_per_seq=case.page_table.shape[1],
+                            union_rows=case.rows_per_seq if union else 0)
     stream = torch.cuda.current_stream(dev)
 
     def call():
@@ -387,9 +393,12 @@ def run_attn(name: str, steps: int, warmup: int) -> dict:
     if status != 0:
         raise RuntimeError(f"{name}: status word {status} after the timed calls")
     n_valid = int((case.token_ids >= 0).sum())
+    rps = case.rows_per_seq
+    n_union = sum(int(np.unique(g[g >= 0]).size) for g in
+                  (case.token_ids[i:i + rps] for i in range(0, case.rows, rps)))
     D = case.head_dim
     elem = 1 if case.kv_fp8 else 2
-    gathered = n_valid * case.kv_heads * D * elem * 2
+    gathered = (n_union if union else n_valid) * case.kv_heads * D * elem * 2
     per_row = case.rows * (hq * D * 2 * 3 + case.k_tokens * 4 + hq * 4)
     alg = gathered + per_row
     achieved = alg / (ms * 1e-3) / 1e9
@@ -398,17 +407,21 @@ def run_attn(name: str, steps: int, warmup: int) -> dict:
     return dict(
         ms_per_step=ms, rows_per_s=case.rows / (ms * 1e-3),
         config={"workload": name, "rows": case.rows, "rows_per_seq": case.rows_per_seq,
+                "union_rows": case.rows_per_seq if union else 1,
                 "kv_heads": case.kv_heads, "group": case.group, "head_dim": D,
                 "k_tokens": case.k_tokens, "page_size": case.page_size, "gate": True,
                 "chunks": chunks,
                 "dtype": ("fp8 e4m3 K/V, " if case.kv_fp8 else "") + "bf16 in, fp32 accumulate, bf16 out",
                 "graph": True},
-        attended_tokens_per_call=n_valid, alg_bytes_per_call=alg,
+        attended_tokens_per_call=n_valid, union_tokens_per_call=n_union,
+        alg_bytes_per_call=alg,
         roofline={"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                   "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                  "basis": "K and V rows of every attended token (2 * kv_heads * head_dim "
-                           "elements, bf16 or fp8) + q, gate and out (bf16) + ids + lse, over "
-                           "the graph replay's time per call; page-table reads not counted"},
+                  "basis": ("K and V rows of every distinct token of each request's rows "
+                            "(union mode)" if union else "K and V rows of every attended token")
+                           + " (2 * kv_heads * head_dim elements, bf16 or fp8) + q, gate and out "
+                           "(bf16) + ids + lse, over the graph replay's time per call; page-table "
+                           "reads not counted"},
     )
 
 
@@ -440,7 +453,8 @@ def main() -> int:
                     help="do not also time the sparse attention over the selected tokens")
     ap.add_argument("--attn-only", action="store_true",
                     help="time only the sparse attention")
-    ap.add_argument("--attn-workloads", default="attn_decode,attn_decode_fp8,attn_c1",
+    ap.add_argument("--attn-workloads",
+                    default="attn_decode,attn_decode_fp8,attn_c1,attn_decode_g3,attn_decode_g3:union",
                     help="comma-separated sparse-attention workloads to time")
     args = ap.parse_args()
 

@@ -31,9 +31,25 @@
  * rounded to bf16 before they multiply V), the output is rounded to bf16.
  *
  * Limits: head_dim 128 or 256; group 1..16; kv_heads >= 1; page_size a power
- * of two; num_slots < 2^31.
+ * of two; num_slots < 2^31.  Union mode also needs union_rows * group <= 16,
+ * union_rows * k_tokens <= 32768 and rows_per_seq % union_rows == 0.
  *
- * dsa_sparse_attn enqueues one launch on `stream`, allocates nothing, never
+ * Union mode (shape.union_rows >= 2; the page on vllm PR #48726, "LiteDSA:
+ * grouped masked sparse attention", packs neighbouring queries into one
+ * matrix tile and runs one product over the union of their selected
+ * positions, each query still attending exactly its own set): consecutive rows are taken in groups of
+ * union_rows (all of one sequence, so union_rows divides rows_per_seq; the
+ * last group may be shorter).  The group's ids are merged into one list of
+ * distinct positions, each with a bit per row that selected it, and every
+ * union token's K and V rows are read once for all union_rows * group
+ * (row, head) pairs, which share one 16-row matrix tile (union_rows * group <=
+ * 16).  The result is the attention above with each row's ids taken as a
+ * set: an id a row lists twice counts once (ids from the selection are
+ * distinct, so the two modes then agree).  Union mode issues two launches
+ * (the union, then the attention) and holds union_rows * k_tokens 8-byte
+ * entries per group in the workspace.
+ *
+ * dsa_sparse_attn enqueues its launches on `stream`, allocates nothing, never
  * synchronizes and can be captured in a HIP graph.  When a row's tokens are
  * split over several workgroups (chunks > 1), each writes a partial
  * (maximum, sum, unnormalised output) to the context's workspace and the last
@@ -65,7 +81,8 @@ typedef struct dsa_attn_shape {
   int64_t num_slots;      /* cache slots, < 2^31 */
   int64_t k_slot_stride, k_head_stride;   /* elements */
   int64_t v_slot_stride, v_head_stride;   /* elements */
-  int32_t chunks;         /* workgroups per (row, kv head); 0 = chosen at init */
+  int32_t chunks;         /* workgroups per (row or union group, kv head); 0 = chosen at init */
+  int32_t union_rows;     /* 0 or 1: each row on its own; >= 2: union mode (see above) */
 } dsa_attn_shape;
 
 typedef struct dsa_attn_ctx dsa_attn_ctx;
@@ -78,7 +95,8 @@ int dsa_sparse_attn_init(const dsa_attn_shape* shape, int device, dsa_attn_ctx**
 /* Frees the workspace (after the device finished using it). */
 int dsa_sparse_attn_destroy(dsa_attn_ctx* ctx);
 
-/* Chunks per (row, kv head) chosen at init (> 0), or a negative dsa_status. */
+/* Chunks per (row, kv head), or per (union group, kv head) in union mode,
+ * chosen at init (> 0), or a negative dsa_status. */
 int dsa_sparse_attn_chunks(const dsa_attn_ctx* ctx);
 
 int dsa_sparse_attn(dsa_attn_ctx* ctx, const uint16_t* q, const uint16_t* k_cache,

@@ -90,7 +90,7 @@ class AttnShape(ctypes.Structure):
         ("pages_per_seq", ctypes.c_int32), ("num_slots", ctypes.c_int64),
         ("k_slot_stride", ctypes.c_int64), ("k_head_stride", ctypes.c_int64),
         ("v_slot_stride", ctypes.c_int64), ("v_head_stride", ctypes.c_int64),
-        ("chunks", ctypes.c_int32),
+        ("chunks", ctypes.c_int32), ("union_rows", ctypes.c_int32),
     ]
 
 
@@ -486,18 +486,20 @@ class SparseAttn:
     The caches are bf16 tensors [num_slots, kv_heads, head_dim], or uint8
     tensors of E4M3 codes with k_scale and v_scale given (any slot and head
     strides that are multiples of 8 elements, innermost dimension
-    contiguous); q and gate are bf16 [rows, kv_heads * group, head_dim]."""
+    contiguous); q and gate are bf16 [rows, kv_heads * group, head_dim].
+    union_rows >= 2 selects union mode: each group of that many consecutive rows
+    is attended in one pass over the union of its ids."""
 
     def __init__(self, rows: int, kv_heads: int, group: int, head_dim: int, k_tokens: int,
                  num_slots: int, rows_per_seq: int = 1, page_size: int = 1,
                  pages_per_seq: int = 0, k_strides=None, v_strides=None, chunks: int = 0,
-                 device: int = 0):
+                 device: int = 0, union_rows: int = 0):
         lib = load()
         ks = (kv_heads * head_dim, head_dim) if k_strides is None else tuple(k_strides)
         vs = (kv_heads * head_dim, head_dim) if v_strides is None else tuple(v_strides)
         self.shape = AttnShape(rows, kv_heads, group, head_dim, k_tokens, rows_per_seq,
                                page_size, pages_per_seq, num_slots, ks[0], ks[1], vs[0], vs[1],
-                               chunks)
+                               chunks, union_rows)
         self.device = device
         h = ctypes.c_void_p()
         self._check(lib.dsa_sparse_attn_init(ctypes.byref(self.shape), device, ctypes.byref(h)))

@@ -22,6 +22,16 @@
 // with one chunk the workgroup writes the gated bf16 output and the LSE, else
 // it writes a partial (maximum, sum, unnormalised output) and the last
 // workgroup of the (row, kv head) to arrive merges the partials.
+//
+// Union mode (the page on vllm PR #48726, "LiteDSA: grouped masked sparse
+// attention": one product over the union of neighbouring queries'
+// selections, each query still attending exactly its own set).  A first launch merges the ids of each
+// group of union_rows consecutive rows into distinct positions, each with a
+// bit per row that selected it (k_union), and the attention kernel then runs
+// per (group, kv heads, chunk) with the group's (row, head) pairs as the 16
+// rows of the matrix tile, reading every union token's K and V once.  Scores
+// of tokens a row did not select are -inf before the online softmax, so each
+// row's result is its own set's attention.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -66,6 +76,25 @@ struct Args {
   int32_t hw;           // kv heads per workgroup (1, 2 or 4; divides hkv)
   float c2;             // sm_scale * log2(e) (times k_scale for fp8 caches)
   float vscale;         // v_scale for fp8 caches, else 1
+  // union mode
+  const int2* ent;      // [groups][cap]: (position, bit per row of the group)
+  const int32_t* cnt;   // [groups]: union entries of each group
+  int32_t U;            // rows per group (1 outside union mode)
+  int32_t P;            // (row, head) pairs per tile: G, or U * G
+  int32_t cap;          // entries per group, U * K
+};
+
+// --- union of a group's ids ------------------------------------------------
+constexpr int UNT = 1024;          // threads of the union kernel
+constexpr int UWIN = 262144;       // positions per window (a 32 KB presence bitmap)
+constexpr int UCAP = 32768;        // largest U * K
+constexpr int UIPT = UCAP / UNT;   // ids held per thread
+
+struct UArgs {
+  const int32_t* ids;
+  int2* ent;
+  int32_t* cnt;
+  int32_t rows, K, U, cap;
 };
 
 SA_DEV uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -116,6 +145,178 @@ SA_DEV int slot_of(const Args& a, int seq, int pos, bool& bad) {
   }
   if (slot >= a.num_slots) { bad = true; return -1; }
   return (int)slot;
+}
+
+// Block-wide sums and minima over the UNT threads of the union kernel.
+SA_DEV int wave_incl_sum(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(v, o);
+    if (lane >= o) v += x;
+  }
+  return v;
+}
+SA_DEV int wave_min(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+
+// One workgroup per group of U consecutive rows.  The group's U * K ids are
+// placed window by window (UWIN positions each; windows holding no id are
+// skipped): every id in the window sets its position's bit in a presence
+// bitmap; a block-wide prefix count over the bitmap's words then gives each
+// distinct position its union index (so a repeated id counts once), each id
+// ORs its row's bit into that entry's 16-bit row mask, and the ids of each
+// entry's lowest row write it out as (position, row mask) at its index.  The
+// work per thread follows its own ids and bitmap words, not the density of
+// the window.  The attention kernel maps positions to cache slots as it does
+// for a row's own list.
+__global__ void __launch_bounds__(UNT) k_union(UArgs a) {
+  constexpr int NW = UWIN / 32;               // bitmap words
+  constexpr int WPT = NW / UNT;               // words per thread
+  __shared__ uint4 pres4[NW / 4];             // presence bits
+  __shared__ int wpre[NW];                    // set bits in earlier words of the window
+  __shared__ uint4 mask4[UCAP / 8];           // 16-bit row masks by union index
+  __shared__ int wred[UNT / 64];
+  __shared__ int wmin[UNT / 64];
+  uint32_t* pres = reinterpret_cast<uint32_t*>(pres4);
+  uint32_t* maskw = reinterpret_cast<uint32_t*>(mask4);
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int gi = blockIdx.x;
+  const int r0 = gi * a.U, nr = min(a.U, a.rows - r0);
+  const int E = nr * a.K;
+  const int32_t* ids = a.ids + (int64_t)r0 * a.K;
+  // Thread t holds ids t + UNT * i; loads are clamped so that a batch of
+  // them is in flight at once, and the value of an index past E is ignored.
+  // Up to UNT * BATCH ids (every decode shape) stay in registers; more are
+  // re-read from the cache at each pass.
+  constexpr int BATCH = 8;
+  const bool held = E <= UNT * BATCH;
+  int hp[BATCH];
+  uint32_t hb[BATCH];                           // bit of the id's row in the group
+#pragma unroll
+  for (int i = 0; i < BATCH; ++i) {
+    const int e = min(t + UNT * i, E - 1);
+    hp[i] = ids[e];
+    hb[i] = 1u << (e / a.K);
+  }
+  // fn(position, row bit, valid) over this thread's ids; every lane of a
+  // wave takes part in each call (valid is false past E), so that fn may
+  // exchange values between lanes.
+  auto each_id = [&](auto&& fn) {
+    if (held) {
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) fn(hp[i], hb[i], t + UNT * i < E);
+      return;
+    }
+#pragma unroll 1
+    for (int i0 = 0; i0 < UIPT && 64 * wv + UNT * i0 < E; i0 += BATCH) {   // uniform per wave
+      int p[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) p[i] = ids[min(t + UNT * (i0 + i), E - 1)];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int e = t + UNT * (i0 + i);
+        fn(p[i], e < E ? 1u << (e / a.K) : 0u, e < E);
+      }
+    }
+  };
+  int lo = INT32_MAX;
+  each_id([&](int p, uint32_t, bool v) { if (v && p >= 0) lo = min(lo, p); });
+  lo = wave_min(lo);
+  if (lane == 0) wmin[wv] = lo;
+  __syncthreads();
+  lo = INT32_MAX;
+#pragma unroll
+  for (int k = 0; k < UNT / 64; ++k) lo = min(lo, wmin[k]);
+  int total = 0;
+  int2* ent = a.ent + (int64_t)gi * a.cap;
+  while (lo != INT32_MAX) {                     // uniform: every thread holds the same lo
+    const int base = lo - lo % UWIN;
+    const int64_t end = (int64_t)base + UWIN;
+    for (int k = t; k < NW / 4; k += UNT) pres4[k] = make_uint4(0, 0, 0, 0);
+    for (int k = t; k < UCAP / 8; k += UNT) mask4[k] = make_uint4(0, 0, 0, 0);
+    __syncthreads();                            // cleared
+    int nxt = INT32_MAX;
+    each_id([&](int p, uint32_t, bool v) {
+      const bool in = v && p >= base && p < end;
+      const int o = p - base;
+      int wd = in ? o >> 5 : -1 - lane;         // distinct for lanes outside the window
+      uint32_t bits = in ? 1u << (o & 31) : 0u;
+      // A dense window puts neighbouring lanes (neighbouring ids of one row)
+      // on one word: OR their bits along the run first, so that one lane per
+      // run issues the LDS atomic instead of up to 32 in a row.
+      if (__ballot(__shfl_down(wd, 1) == wd && lane < 63)) {
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t ob = __shfl_down(bits, off);
+          const int ow = __shfl_down(wd, off);
+          if (lane + off < 64 && ow == wd) bits |= ob;
+        }
+        const int pw = __shfl_up(wd, 1);
+        if (lane > 0 && pw == wd) bits = 0u;    // not the first lane of its run
+      }
+      if (bits) atomicOr(&pres[wd], bits);
+      if (v && p >= end) nxt = min(nxt, p);
+    });
+    nxt = wave_min(nxt);
+    if (lane == 0) wmin[wv] = nxt;
+    __syncthreads();                            // bitmap complete
+    // Thread t owns words WPT t .. WPT t + WPT - 1.
+    uint32_t w[WPT];
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < WPT / 4; ++k) {
+      const uint4 x = pres4[t * (WPT / 4) + k];
+      w[4 * k] = x.x; w[4 * k + 1] = x.y; w[4 * k + 2] = x.z; w[4 * k + 3] = x.w;
+    }
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) c += __popc(w[k]);
+    const int incl = wave_incl_sum(c, lane);
+    if (lane == 63) wred[wv] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int k = 0; k < UNT / 64; ++k) {
+      before += k < wv ? wred[k] : 0;
+      all += wred[k];
+    }
+    {
+      int run = before + incl - c;
+#pragma unroll
+      for (int k = 0; k < WPT; ++k) {
+        wpre[WPT * t + k] = run;
+        run += __popc(w[k]);
+      }
+    }
+    __syncthreads();                            // union indices known
+    each_id([&](int p, uint32_t rb, bool v) {
+      if (v && p >= base && p < end) {
+        const int o = p - base;
+        const int u = wpre[o >> 5] + __popc(pres[o >> 5] & ((1u << (o & 31)) - 1u));
+        atomicOr(&maskw[u >> 1], rb << (16 * (u & 1)));
+      }
+    });
+    __syncthreads();                            // row masks complete
+    // Each entry is written by the ids of its lowest row (the same value if
+    // that row lists the position twice), so that every thread writes at
+    // most its own ids' entries however dense the window.
+    each_id([&](int p, uint32_t rb, bool v) {
+      if (v && p >= base && p < end) {
+        const int o = p - base;
+        const int u = wpre[o >> 5] + __popc(pres[o >> 5] & ((1u << (o & 31)) - 1u));
+        const uint32_t m = (maskw[u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
+        if ((m & (0u - m)) == rb) ent[total + u] = make_int2(p, (int)m);
+      }
+    });
+    total += all;
+    lo = INT32_MAX;
+#pragma unroll
+    for (int k = 0; k < UNT / 64; ++k) lo = min(lo, wmin[k]);
+    __syncthreads();                            // masks, indices and wred read: clear after
+  }
+  if (t == 0) a.cnt[gi] = total;
 }
 
 // Agent-scope relaxed 64-bit accesses for words one workgroup writes and
@@ -171,7 +372,22 @@ SA_DEV void store_out(const Args& a, int row, int h, int d, float4 o, float L, f
     a.lse[(int64_t)row * hq + h] = L > 0.f ? (M + __log2f(L)) * 0.69314718055994531f : NEG_INF;
 }
 
-template <int D, bool FP8>
+// Row and query head of pair h of a tile: the tile of (row or group `ru`,
+// kv head g) holds heads g*G .. g*G + G - 1 of one row, or in union mode
+// those heads of each of the group's rows in turn.
+template <bool UN>
+SA_DEV void pair_of(const Args& a, int ru, int g, int h, int& row, int& head) {
+  if (UN) {
+    const int r = h / a.G;
+    row = ru * a.U + r;
+    head = g * a.G + (h - r * a.G);
+  } else {
+    row = ru;
+    head = g * a.G + h;
+  }
+}
+
+template <int D, bool FP8, bool UN>
 __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   typedef KV<FP8> T;
   constexpr int KS = D / 32;      // 32-dimension steps of q.k
@@ -197,17 +413,22 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   // (the same pages) at the same time.
   const int gblocks = a.hkv / a.hw, wph = WAVES / a.hw;
   const int wgp = unit / a.chunks, chunk = unit - wgp * a.chunks;
-  const int row = wgp / gblocks, gb = wgp - row * gblocks;
+  // ru: the row, or in union mode the group of rows
+  const int ru = wgp / gblocks, gb = wgp - ru * gblocks;
   const int g = gb * a.hw + w % a.hw, wi = w / a.hw;
-  const int seq = row / a.rows_per_seq;
+  const int seq = (UN ? ru * a.U : ru) / a.rows_per_seq;
   const int hq = a.hkv * a.G;
+  // (row, head) pairs in the tile: G, or G per row of the group
+  const int np = UN ? min(a.U, a.rows - ru * a.U) * a.G : a.G;
 
-  // Query operand: lane (head n, group j) holds q[row, g*G + n, 32s + 8j .. +8].
+  // Query operand: lane (pair n, group j) holds q[row, head, 32s + 8j .. +8].
   uint4 qr[KS];
   {
-    const uint16_t* qp = a.q + ((int64_t)row * hq + g * a.G + min(n, a.G - 1)) * D + 8 * j;
+    int qrow, qhead;
+    pair_of<UN>(a, ru, g, min(n, np - 1), qrow, qhead);
+    const uint16_t* qp = a.q + ((int64_t)qrow * hq + qhead) * D + 8 * j;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qr[s] = n < a.G ? ld16(qp + 32 * s) : make_uint4(0, 0, 0, 0);
+    for (int s = 0; s < KS; ++s) qr[s] = n < np ? ld16(qp + 32 * s) : make_uint4(0, 0, 0, 0);
   }
   f32x4 oacc[OT];
 #pragma unroll
@@ -215,23 +436,60 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   float m_run = NEG_INF, l_run = 0.f;
   bool bad = false;
 
-  const int steps = (a.K + STEP - 1) / STEP;
-  const int st0 = chunk * a.spc, st1 = min(steps, st0 + a.spc);
-  const int32_t* idrow = a.ids + (int64_t)row * a.K;
+  // Steps of this chunk.  In union mode the list is the group's union, whose
+  // length is known only now; the chunks split it evenly.
+  int nlist = a.K, spc = a.spc;
+  if (UN) {
+    nlist = a.cnt[ru];
+    const int st = (nlist + STEP - 1) / STEP;
+    spc = (st + a.chunks - 1) / a.chunks;
+  }
+  const int steps = (nlist + STEP - 1) / STEP;
+  const int st0 = chunk * spc, st1 = min(steps, st0 + spc);
+  const int32_t* idrow = a.ids + (int64_t)ru * a.K;
+  const int2* erow = a.ent + (int64_t)ru * a.cap;
 
-  // Token position of step st for this lane (-1 past the chunk or the list).
+  // Token of step st for this lane: its position (-1 past the chunk or the
+  // list), and in union mode its (position, row bits) entry.
   auto pos_of = [&](int st) -> int {
     const int tix = st * STEP + (lane & 31);
-    return (st < st1 && tix < a.K) ? idrow[tix] : -1;
+    return (st < st1 && tix < nlist) ? idrow[tix] : -1;
+  };
+  auto ent_of = [&](int st) -> int2 {
+    const int tix = st * STEP + (lane & 31);
+    return (st < st1 && tix < nlist) ? erow[tix] : make_int2(-1, 0);
   };
   // The next step's id is loaded while this step's K/V loads are in flight,
   // so a step waits for two memory round trips (page table, K/V) instead of
   // three.
-  int pos = pos_of(st0 + wi);
+  int pos = -1;
+  int2 en = make_int2(-1, 0);
+  if constexpr (UN) en = ent_of(st0 + wi);
+  else pos = pos_of(st0 + wi);
   for (int st = st0 + wi; st < st1; st += wph) {
-    const int slot = slot_of(a, seq, pos, bad);
-    pos = pos_of(st + wph);
+    int slot;
+    uint32_t rbits = 0;
+    if constexpr (UN) {
+      slot = slot_of(a, seq, en.x, bad);
+      rbits = (uint32_t)en.y;
+      en = ent_of(st + wph);
+    } else {
+      slot = slot_of(a, seq, pos, bad);
+      pos = pos_of(st + wph);
+    }
     if (__ballot(slot >= 0) == 0) continue;        // nothing to attend in this step
+    // Union mode: bit t of `mine` says whether this lane's row (pair n) lists
+    // token t of the step (lanes t and 32 + t hold the same token).
+    uint32_t mine = ~0u;
+    if (UN) {
+#pragma unroll
+      for (int r = 0; r < GMAX; ++r) {
+        if (r * a.G < np) {
+          const uint32_t b = (uint32_t)__ballot((rbits >> r) & 1u);
+          if (n / a.G == r) mine = b;
+        }
+      }
+    }
     // Slots of this lane's tokens: K rows n and 16 + n; V and score tokens
     // 4j + e and 16 + 4j + e (e < 4).
     const int sk0 = __shfl(slot, n), sk1 = __shfl(slot, 16 + n);
@@ -270,8 +528,10 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
     float sc[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      sc[r] = sv[r] >= 0 ? s0[r] * a.c2 : NEG_INF;
-      sc[4 + r] = sv[4 + r] >= 0 ? s1[r] * a.c2 : NEG_INF;
+      const bool m0 = sv[r] >= 0 && ((mine >> (4 * j + r)) & 1u);
+      const bool m1 = sv[4 + r] >= 0 && ((mine >> (16 + 4 * j + r)) & 1u);
+      sc[r] = m0 ? s0[r] * a.c2 : NEG_INF;
+      sc[4 + r] = m1 ? s1[r] * a.c2 : NEG_INF;
     }
     float tmax = sc[0];
 #pragma unroll
@@ -329,7 +589,7 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   // element r, head n and dimension 128c + 8(4j + r) + i.
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (n < a.G) {
+  if (n < np) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -348,11 +608,13 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   __syncthreads();
 
   constexpr int D4 = D / 4;
-  const int n4 = a.G * D4;
+  const int n4 = np * D4;
   for (int e = threadIdx.x; e < a.hw * n4; e += NT) {
     const int gl = e / n4, e2 = e - gl * n4;
     const int h = e2 / D4, d = (e2 - h * D4) * 4;
     const int gh = gb * a.hw + gl;
+    int orow, ohead;
+    pair_of<UN>(a, ru, gh, h, orow, ohead);
     float M = NEG_INF;
     for (int v = gl; v < WAVES; v += a.hw) M = fmaxf(M, sm.m[v][h]);
     float L = 0.f;
@@ -364,13 +626,13 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
       o.x += x.x * f; o.y += x.y * f; o.z += x.z * f; o.w += x.w * f;
     }
     if (a.chunks == 1) {
-      store_out(a, row, gh * a.G + h, d, o, L, M, D);
+      store_out(a, orow, ohead, d, o, L, M, D);
     } else {
-      const int64_t pu = ((int64_t)row * a.hkv + gh) * a.chunks + chunk;
-      float* po = a.part_o + (pu * a.G + h) * D + d;
+      const int64_t pu = ((int64_t)ru * a.hkv + gh) * a.chunks + chunk;
+      float* po = a.part_o + (pu * a.P + h) * D + d;
       st_coh64(po, o.x, o.y);
       st_coh64(po + 2, o.z, o.w);
-      if (d == 0) st_coh64(a.part_ml + (pu * a.G + h) * 2, M, L);
+      if (d == 0) st_coh64(a.part_ml + (pu * a.P + h) * 2, M, L);
     }
   }
   if (a.chunks == 1) return;
@@ -381,25 +643,69 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   if (threadIdx.x == 0) sm.last = atomicAdd(&a.tickets[wgp], 1u) == (uint32_t)(a.chunks - 1);
   __syncthreads();
   if (!sm.last) return;
-  for (int e = threadIdx.x; e < a.hw * n4; e += NT) {
-    const int gl = e / n4, e2 = e - gl * n4;
-    const int h = e2 / D4, d = (e2 - h * D4) * 4;
-    const int gh = gb * a.hw + gl;
-    const int64_t u0 = ((int64_t)row * a.hkv + gh) * a.chunks;
+  // Stage every chunk's (maximum, sum) of the workgroup's hw * np pairs in
+  // LDS (the wave partials' space, no longer needed), turn each pair's
+  // maxima into the chunks' weights there, then sum the partial outputs.
+  const int npp = a.hw * np;
+  float2* cw = reinterpret_cast<float2*>(&sm.o[0][0][0]);   // [npp][chunks]
+  float* pM = &sm.m[0][0];                                    // [npp]
+  float* pL = &sm.l[0][0];
+  auto unit_of = [&](int pr, int ch, int& h) -> int64_t {
+    const int gl = pr / np;
+    h = pr - gl * np;
+    return ((int64_t)ru * a.hkv + gb * a.hw + gl) * a.chunks + ch;
+  };
+  for (int e = threadIdx.x; e < npp * a.chunks; e += NT) {
+    const int pr = e / a.chunks, ch = e - pr * a.chunks;
+    int h;
+    const int64_t u = unit_of(pr, ch, h);
+    cw[e] = ld_coh64(a.part_ml + (u * a.P + h) * 2);
+  }
+  __syncthreads();
+  for (int pr = threadIdx.x; pr < npp; pr += NT) {
+    float2* c = cw + (int64_t)pr * a.chunks;
     float M = NEG_INF;
-    for (int ch = 0; ch < a.chunks; ++ch)
-      M = fmaxf(M, ld_coh64(a.part_ml + ((int64_t)(u0 + ch) * a.G + h) * 2).x);
+    for (int ch = 0; ch < a.chunks; ++ch) M = fmaxf(M, c[ch].x);
     float L = 0.f;
-    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int ch = 0; ch < a.chunks; ++ch) {
-      const float2 ml = ld_coh64(a.part_ml + ((int64_t)(u0 + ch) * a.G + h) * 2);
-      const float f = ml.x == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-      L += ml.y * f;
-      const float* po = a.part_o + ((int64_t)(u0 + ch) * a.G + h) * D + d;
+      const float f = c[ch].x == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(c[ch].x - M);
+      L += c[ch].y * f;
+      c[ch].x = f;
+    }
+    pM[pr] = M;
+    pL[pr] = L;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.hw * n4; e += NT) {
+    const int pr = e / D4, d = (e - pr * D4) * 4;
+    int h;
+    const int64_t u0 = unit_of(pr, 0, h);
+    int orow, ohead;
+    pair_of<UN>(a, ru, gb * a.hw + pr / np, h, orow, ohead);
+    const float2* c = cw + (int64_t)pr * a.chunks;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+    int ch = 0;
+    for (; ch + 4 <= a.chunks; ch += 4) {
+      float2 x[4][2];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float* po = a.part_o + ((u0 + ch + k) * a.P + h) * D + d;
+        x[k][0] = ld_coh64(po);
+        x[k][1] = ld_coh64(po + 2);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float f = c[ch + k].x;
+        o.x += x[k][0].x * f; o.y += x[k][0].y * f; o.z += x[k][1].x * f; o.w += x[k][1].y * f;
+      }
+    }
+    for (; ch < a.chunks; ++ch) {
+      const float* po = a.part_o + ((u0 + ch) * a.P + h) * D + d;
       const float2 x0 = ld_coh64(po), x1 = ld_coh64(po + 2);
+      const float f = c[ch].x;
       o.x += x0.x * f; o.y += x0.y * f; o.z += x1.x * f; o.w += x1.y * f;
     }
-    store_out(a, row, gh * a.G + h, d, o, L, M, D);
+    store_out(a, orow, ohead, d, o, pL[pr], pM[pr], D);
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(&a.tickets[wgp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -417,10 +723,13 @@ struct dsa_attn_ctx {
   dsa_attn_shape sh;
   int device;
   int chunks, spc, hw;
+  int U, nru, cap;      // rows per union group (1 outside union mode), groups or rows, U * K
   void* ws;
   size_t ws_bytes;
   float *part_o, *part_ml;
   uint32_t *tickets, *status;
+  int2* ent;            // union mode: [nru][cap]
+  int32_t* cnt;         // union mode: [nru]
   uint32_t magic;
 };
 
@@ -492,6 +801,18 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
       s->v_slot_stride < (s->kv_heads - 1) * s->v_head_stride + D)
     return sa_fail(DSA_ERR_INVALID_ARG, "cache strides overlap heads or slots");
   if (s->chunks < 0) return sa_fail(DSA_ERR_INVALID_ARG, "chunks must be >= 0");
+  if (s->union_rows < 0) return sa_fail(DSA_ERR_INVALID_ARG, "union_rows must be >= 0");
+  const int U = std::max(1, s->union_rows);
+  if (U > 1) {
+    if (U * s->group > GMAX)
+      return sa_fail(DSA_ERR_UNSUPPORTED, "union_rows * group must be <= %d (got %d * %d)", GMAX, U,
+                     s->group);
+    if ((int64_t)U * s->k_tokens > UCAP)
+      return sa_fail(DSA_ERR_UNSUPPORTED, "union_rows * k_tokens must be <= %d", UCAP);
+    if (s->rows_per_seq % U)
+      return sa_fail(DSA_ERR_INVALID_ARG, "union_rows must divide rows_per_seq (a group lies in "
+                     "one sequence)");
+  }
   const int64_t pairs = (int64_t)s->rows * s->kv_heads;
   if (pairs > ((int64_t)1 << 30)) return sa_fail(DSA_ERR_UNSUPPORTED, "too many rows");
   if (device < 0) return sa_fail(DSA_ERR_INVALID_ARG, "device must be >= 0");
@@ -507,24 +828,40 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   c->sh = *s;
   c->device = device;
   c->magic = SA_MAGIC;
-  // kv heads per workgroup, and chunks per (row, group of kv heads): enough
-  // workgroups for two per CU, each chunk at least one step per wave.
+  // kv heads per workgroup, and chunks per (row or union group, group of kv
+  // heads): enough workgroups for two per CU, each chunk at least one step per
+  // wave of one row's list (a union holds between k_tokens and U * k_tokens
+  // tokens; more chunks would multiply the partials the last workgroup
+  // merges, U * group pairs of them per chunk).
   const int hw = s->kv_heads % 4 == 0 ? 4 : s->kv_heads % 2 == 0 ? 2 : 1;
-  const int64_t wgp = (int64_t)s->rows * (s->kv_heads / hw);
+  const int64_t nru = U > 1 ? (s->rows + U - 1) / U : s->rows;
+  const int64_t wgp = nru * (s->kv_heads / hw);
   const int64_t steps = (s->k_tokens + STEP - 1) / STEP;
   const int64_t maxc = std::max<int64_t>(1, steps / (WAVES / hw));
   int64_t ch = s->chunks > 0 ? s->chunks
                              : (2 * (int64_t)cus + std::max<int64_t>(wgp, 1) - 1) / std::max<int64_t>(wgp, 1);
   ch = std::max<int64_t>(1, std::min<int64_t>(ch, s->chunks > 0 ? steps : maxc));
+  // the merge stages hw * U * group (maximum, sum) pairs per chunk in the
+  // waves' LDS partial space
+  ch = std::min<int64_t>(ch, (int64_t)WAVES * GMAX * D * 4 / (8 * hw * U * s->group));
   const int64_t spc = (steps + ch - 1) / ch;
   ch = (steps + spc - 1) / spc;
   if (wgp * ch > ((int64_t)1 << 31) - 1) { delete c; return sa_fail(DSA_ERR_UNSUPPORTED, "grid too large"); }
   c->chunks = (int)ch;
   c->spc = (int)spc;
   c->hw = hw;
-  const int64_t units = ch > 1 ? pairs * ch : 0;
-  const int64_t floats = units * s->group * (D + 2);
-  c->ws_bytes = (size_t)floats * 4 + (size_t)(pairs + 1) * 4 + 256;
+  c->U = U;
+  c->nru = (int)nru;
+  c->cap = U * s->k_tokens;
+  // [partial outputs][partial (max, sum)][tickets][status] then, in union
+  // mode, [entries][counts]
+  const int64_t P = (int64_t)U * s->group;
+  const int64_t units = ch > 1 ? nru * s->kv_heads * ch : 0;
+  const int64_t floats = units * P * (D + 2);
+  const int64_t nticket = nru * s->kv_heads;
+  const size_t head_bytes = ((size_t)floats * 4 + (size_t)(nticket + 1) * 4 + 255) & ~(size_t)255;
+  const size_t ent_bytes = U > 1 ? (size_t)nru * c->cap * 8 + (size_t)nru * 4 : 0;
+  c->ws_bytes = head_bytes + ent_bytes + 256;
   e = hipMalloc(&c->ws, c->ws_bytes);
   if (e != hipSuccess) { delete c; return sa_hip(e, "hipMalloc(workspace)"); }
   e = hipMemset(c->ws, 0, c->ws_bytes);
@@ -532,9 +869,13 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   if (e != hipSuccess) { (void)hipFree(c->ws); delete c; return sa_hip(e, "hipMemset(workspace)"); }
   float* f = static_cast<float*>(c->ws);
   c->part_o = f;
-  c->part_ml = f + units * s->group * D;
-  c->tickets = reinterpret_cast<uint32_t*>(c->part_ml + units * s->group * 2);
-  c->status = c->tickets + pairs;
+  c->part_ml = f + units * P * D;
+  c->tickets = reinterpret_cast<uint32_t*>(c->part_ml + units * P * 2);
+  c->status = c->tickets + nticket;
+  if (U > 1) {
+    c->ent = reinterpret_cast<int2*>(static_cast<char*>(c->ws) + head_bytes);
+    c->cnt = reinterpret_cast<int32_t*>(c->ent + (int64_t)nru * c->cap);
+  }
   *out = c;
   return DSA_OK;
 }
@@ -598,14 +939,32 @@ int sa_launch(dsa_attn_ctx* c, const uint16_t* q, const void* k_cache, const voi
   a.chunks = c->chunks; a.spc = c->spc; a.hw = c->hw;
   a.c2 = sm_scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
   a.vscale = fp8 ? v_scale : 1.0f;
-  const unsigned grid = (unsigned)((int64_t)s.rows * (s.kv_heads / c->hw) * c->chunks);
-  if (s.head_dim == 256) {
-    if (fp8) hipLaunchKernelGGL((k_sparse_attn<256, true>), dim3(grid), dim3(NT), 0, stream, a);
-    else hipLaunchKernelGGL((k_sparse_attn<256, false>), dim3(grid), dim3(NT), 0, stream, a);
-  } else {
-    if (fp8) hipLaunchKernelGGL((k_sparse_attn<128, true>), dim3(grid), dim3(NT), 0, stream, a);
-    else hipLaunchKernelGGL((k_sparse_attn<128, false>), dim3(grid), dim3(NT), 0, stream, a);
+  a.U = c->U;
+  a.P = c->U * s.group;
+  a.cap = c->cap;
+  a.ent = c->ent;
+  a.cnt = c->cnt;
+  const bool un = c->U > 1;
+  if (un) {
+    UArgs u;
+    std::memset(&u, 0, sizeof(u));
+    u.ids = token_ids; u.ent = c->ent; u.cnt = c->cnt;
+    u.rows = s.rows; u.K = s.k_tokens; u.U = c->U; u.cap = c->cap;
+    hipLaunchKernelGGL(k_union, dim3((unsigned)c->nru), dim3(UNT), 0, stream, u);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return sa_hip(e, "launch k_union");
   }
+  const unsigned grid = (unsigned)((int64_t)c->nru * (s.kv_heads / c->hw) * c->chunks);
+#define SA_GO(DD, F8, UN_) \
+  hipLaunchKernelGGL((k_sparse_attn<DD, F8, UN_>), dim3(grid), dim3(NT), 0, stream, a)
+  if (s.head_dim == 256) {
+    if (fp8) { if (un) SA_GO(256, true, true); else SA_GO(256, true, false); }
+    else { if (un) SA_GO(256, false, true); else SA_GO(256, false, false); }
+  } else {
+    if (fp8) { if (un) SA_GO(128, true, true); else SA_GO(128, true, false); }
+    else { if (un) SA_GO(128, false, true); else SA_GO(128, false, false); }
+  }
+#undef SA_GO
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return sa_hip(e, "launch k_sparse_attn");
   return DSA_OK;

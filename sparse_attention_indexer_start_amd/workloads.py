@@ -432,7 +432,7 @@ def make_attn_custom(seq_lens, rows_per_seq: int, kv_heads: int, group: int, hea
                      k_tokens: int, page_size: int = 16, paged: bool = True,
                      with_gate: bool = True, seed: int = 1, q_scale: float = 1.0,
                      host_caches: bool = True, spare_pages: int = 3, kv_fp8: bool = False,
-                     name: str = "attn_custom") -> AttnCase:
+                     shared: float = 0.0, name: str = "attn_custom") -> AttnCase:
     """Seeded synthetic attention inputs.
 
     Sequence n has seq_lens[n] cached positions; its rows_per_seq rows are
@@ -445,7 +445,11 @@ def make_attn_custom(seq_lens, rows_per_seq: int, kv_heads: int, group: int, hea
     N(0, 1) rounded to bf16 (q times ``q_scale``); the softmax scale is
     1 / sqrt(head_dim).  With ``kv_fp8`` the caches hold E4M3 codes (random
     sign, exponent field 3..9, random mantissa: magnitudes 1/16..7.5) with
-    k_scale 1/4 and v_scale 1/2.
+    k_scale 1/4 and v_scale 1/2.  With ``shared`` > 0 the rows of a request
+    select overlapping sets, as neighbouring queries do: the request draws a
+    base set of min(k_tokens, visible) positions that all its rows see, and
+    each row keeps round(shared * k) of them (a random subset) and draws the
+    rest uniformly from its other visible positions.
     """
     rng = np.random.default_rng([seed, 57273])
     seq_lens = np.asarray(seq_lens, dtype=np.int64)
@@ -468,9 +472,19 @@ def make_attn_custom(seq_lens, rows_per_seq: int, kv_heads: int, group: int, hea
         num_slots = int(seq_lens.max()) if nseq else 0
     ids = np.full((R, k_tokens), -1, dtype=np.int32)
     for n in range(nseq):
+        vis0 = max(0, int(seq_lens[n]) - (rows_per_seq - 1))
+        base = _sorted_sample(rng, vis0, min(k_tokens, vis0)) if shared > 0 else None
         for j in range(rows_per_seq):
             vis = max(0, int(seq_lens[n]) - (rows_per_seq - 1 - j))
-            pick = _sorted_sample(rng, vis, min(k_tokens, vis))
+            k = min(k_tokens, vis)
+            if base is not None and base.size:
+                keep = min(int(round(shared * k)), base.size)
+                kept = rng.choice(base, size=keep, replace=False)
+                pool = np.setdiff1d(np.arange(vis), kept)
+                extra = pool[_sorted_sample(rng, pool.size, k - keep)]
+                pick = np.sort(np.concatenate([kept, extra]))
+            else:
+                pick = _sorted_sample(rng, vis, k)
             ids[n * rows_per_seq + j, :pick.size] = pick
     q = bf16_bits(rng.standard_normal((R, hq, head_dim), dtype=np.float32) * np.float32(q_scale))
     gate = bf16_bits(rng.standard_normal((R, hq, head_dim), dtype=np.float32)) if with_gate else None
@@ -506,6 +520,18 @@ ATTN_CONFIGS = {
     "attn_c1": dict(num_seqs=1, rows_per_seq=4, kv_heads=1, group=3, head_dim=256,
                     k_tokens=2048, page_size=64, ctx=(65536, 65536), short_frac=0.0,
                     host_caches=False),
+    # the decode point of the QSA tuning page's benchmark (128 requests, 4
+    # query rows each, 3 query heads per kv head, 1 kv head), with the rows
+    # of a request sharing 3/4 of their selections (neighbouring queries
+    # select overlapping positions); the union form packs a request's 4 x 3
+    # (row, head) pairs into one matrix tile
+    "attn_decode_g3": dict(num_seqs=128, rows_per_seq=4, kv_heads=1, group=3, head_dim=256,
+                           k_tokens=2048, page_size=64, ctx=(32768, 131072), short_frac=0.05,
+                           host_caches=False, shared=0.75),
+    # parity-sized form of it: 8 requests, host caches
+    "attn_small_g3": dict(num_seqs=8, rows_per_seq=4, kv_heads=1, group=3, head_dim=256,
+                          k_tokens=2048, page_size=64, ctx=(1, 12000), short_frac=0.25,
+                          host_caches=True, q_scale=3.0, shared=0.75),
     # parity-sized: 8 requests x 4 rows, host caches, queries scaled by 3 so
     # that each softmax concentrates on a few tokens
     "attn_small": dict(num_seqs=8, rows_per_seq=4, kv_heads=2, group=12, head_dim=256,
@@ -525,4 +551,4 @@ def make_attn_config(name: str, seed_offset: int = 0) -> AttnCase:
                             c["k_tokens"], page_size=c["page_size"],
                             seed=BASE_SEED + 200 + seed_offset, host_caches=c["host_caches"],
                             q_scale=c.get("q_scale", 1.0), kv_fp8=c.get("kv_fp8", False),
-                            name=name)
+                            shared=c.get("shared", 0.0), name=name)

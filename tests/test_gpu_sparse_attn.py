@@ -62,7 +62,7 @@ def _cache_dev(a):
     return _bf(a)
 
 
-def _run(case, k_dev=None, v_dev=None, chunks=0, with_gate=True, with_lse=True, graph=False):
+def _run(case, k_dev=None, v_dev=None, chunks=0, with_gate=True, with_lse=True, union_rows=0):
     import torch
     hq = case.kv_heads * case.group
     kd = _cache_dev(case.k_cache) if k_dev is None else k_dev
@@ -72,7 +72,8 @@ def _run(case, k_dev=None, v_dev=None, chunks=0, with_gate=True, with_lse=True, 
                             case.num_slots, rows_per_seq=case.rows_per_seq,
                             page_size=case.page_size, pages_per_seq=pps,
                             k_strides=(kd.stride(0), kd.stride(1)),
-                            v_strides=(vd.stride(0), vd.stride(1)), chunks=chunks)
+                            v_strides=(vd.stride(0), vd.stride(1)), chunks=chunks,
+                            union_rows=union_rows)
     q = _bf(case.q)
     gate = _bf(case.gate) if (with_gate and case.gate is not None) else None
     ids = torch.from_numpy(case.token_ids).cuda()
@@ -85,16 +86,16 @@ def _run(case, k_dev=None, v_dev=None, chunks=0, with_gate=True, with_lse=True, 
     status = op.read_status()
     gh.log(f"  attention: {case.rows} rows, {case.kv_heads}x{case.group} heads, D={case.head_dim}, "
            f"K={case.k_tokens}, {'fp8' if case.kv_fp8 else 'bf16'} K/V, {op.chunks()} chunks, "
-           f"status {status}")
+           f"union_rows {union_rows}, status {status}")
     op.close()
     return _codes(out), (None if lse is None else lse.cpu().numpy()), status
 
 
-def _check(case, got_codes, got_lse, rows=None, with_gate=True):
+def _check(case, got_codes, got_lse, rows=None, with_gate=True, distinct=False):
     gate = case.gate if with_gate else None
     args = (case.q, case.k_cache, case.v_cache, case.token_ids, case.sm_scale, case.group,
             case.page_table, case.page_size, case.rows_per_seq)
-    sc = dict(k_scale=case.k_scale, v_scale=case.v_scale)
+    sc = dict(k_scale=case.k_scale, v_scale=case.v_scale, distinct=distinct)
     ref, ref_lse, bad = so.sparse_attention(*args, gate=gate, rows=rows, **sc)
     sign_off = np.uint8(0x7F) if case.kv_fp8 else np.uint16(0x7FFF)
     A, _, _ = so.sparse_attention(case.q, case.k_cache, case.v_cache & sign_off, *args[3:],
@@ -304,3 +305,159 @@ def test_attn_rejects_unsupported_shapes():
         binding.SparseAttn(4, 1, 4, 256, 64, 100, page_size=3)
     with pytest.raises(binding.DsaError):
         binding.SparseAttn(4, 2, 4, 256, 64, 100, k_strides=(516, 256))   # not a multiple of 8
+
+
+# ---------------------------------------------------------------------------
+# Union mode: groups of rows over the union of their ids, each row exact
+# ---------------------------------------------------------------------------
+
+def test_attn_union_small_config_every_row():
+    case = wl.make_attn_config("attn_small_g3")
+    got, lse, status = _run(case, union_rows=4)
+    assert status == 0
+    _check(case, got, lse, distinct=True)
+    # the per-row form of the same inputs agrees with the same oracle
+    got1, lse1, status1 = _run(case)
+    assert status1 == 0
+    _check(case, got1, lse1)
+
+
+@pytest.mark.parametrize("D,G,hkv,K,U,rps,chunks,paged,gate,shared", [
+    (256, 3, 1, 2048, 4, 4, 0, True, True, 0.75),
+    (256, 3, 1, 300, 5, 5, 3, True, True, 0.5),
+    (128, 8, 2, 700, 2, 4, 0, False, True, 0.9),
+    (128, 1, 4, 100, 16, 16, 0, True, False, 0.75),
+    (256, 6, 3, 1000, 2, 2, 1, True, True, 0.75),
+    (128, 2, 1, 2048, 8, 8, 64, True, True, 0.6),
+    (256, 4, 2, 4096, 4, 8, 0, True, True, 0.75),
+    (128, 1, 1, 2048, 16, 16, 0, True, True, 0.0),
+])
+def test_attn_union_shapes(D, G, hkv, K, U, rps, chunks, paged, gate, shared):
+    rng = np.random.default_rng(D + 7 * G + 11 * K + U)
+    lens = rng.integers(1, 3 * K + 40, size=3)
+    lens[0] = 1
+    case = wl.make_attn_custom(lens, rps, hkv, G, D, K, page_size=16, paged=paged,
+                               with_gate=gate, seed=G * 100 + K + U, q_scale=2.0, shared=shared)
+    got, lse, status = _run(case, chunks=chunks, with_gate=gate, union_rows=U)
+    assert status == 0
+    _check(case, got, lse, with_gate=gate, distinct=True)
+
+
+def test_attn_union_many_windows():
+    """Positions spread over several of the union kernel's 262144-position
+    windows (contexts of 270K-600K tokens), with windows left empty."""
+    case = wl.make_attn_custom([600000, 300000, 270000, 5], 4, 1, 3, 128, 1024, page_size=64,
+                               seed=31, q_scale=2.0, shared=0.5)
+    ids = case.token_ids
+    ids[4:8] = np.where(ids[4:8] >= 262144, ids[4:8], -1)    # request 1: its second window only
+    got, lse, status = _run(case, chunks=2, union_rows=4)
+    assert status == 0
+    _check(case, got, lse, distinct=True)
+
+
+def test_attn_union_repeats_pads_order_and_bad_ids():
+    """Ids in any order, repeated within a row (counted once), -1 pads
+    anywhere, a whole group without ids, a short last group, and ids that
+    are not addressable (skipped, status bit 0)."""
+    case = wl.make_attn_custom([900, 3, 2500, 40], 4, 2, 3, 256, 512, page_size=16, seed=27,
+                               q_scale=2.0, shared=0.5)
+    rng = np.random.default_rng(27)
+    ids = case.token_ids
+    for r in range(ids.shape[0]):
+        rng.shuffle(ids[r])                              # any order, pads scattered
+    ids[0, :40] = ids[0, 100]                            # one id forty times
+    ids[2, 7] = ids[2, 9] if ids[2, 9] >= 0 else ids[2, 7]
+    ids[4:8, :] = -1                                     # group 1 holds no id
+    ids[9, 3] = 10_000                                   # page beyond the table
+    ids[13, 0] = 50                                      # page 3 of a 40-token sequence: unmapped
+    keep = ids.shape[0] - 1                              # the last group has 3 rows
+    c2 = wl.AttnCase(**{**case.__dict__, "q": case.q[:keep], "token_ids": ids[:keep].copy(),
+                        "gate": case.gate[:keep]})
+    got, lse, status = _run(c2, chunks=3, union_rows=4)
+    assert status & 1, "unaddressable ids must set status bit 0"
+    bad = _check(c2, got, lse, distinct=True)
+    assert bad[9] == 1 and bad[13] == 1 and bad.sum() == 2
+    assert np.all(_f(got[4:8]) == 0.0) and np.all(lse[4:8] == -np.inf)
+
+
+@pytest.mark.parametrize("D,G,hkv,K,U,chunks", [(256, 3, 1, 1000, 4, 0), (128, 4, 2, 300, 4, 2)])
+def test_attn_union_fp8_caches(D, G, hkv, K, U, chunks):
+    rng = np.random.default_rng(D + G + K + 1)
+    lens = rng.integers(1, 3 * K + 40, size=3)
+    case = wl.make_attn_custom(lens, 4, hkv, G, D, K, page_size=32, seed=G + K + 1,
+                               q_scale=0.5, kv_fp8=True, shared=0.75)
+    got, lse, status = _run(case, chunks=chunks, union_rows=U)
+    assert status == 0
+    _check(case, got, lse, distinct=True)
+
+
+def test_attn_union_graph_replay_with_new_ids():
+    """The two launches of union mode under graph capture: replays follow
+    new ids, and a replay of the first ids repeats the eager call bit for bit."""
+    import torch
+    case = wl.make_attn_custom([3000, 2500, 4000, 100], 4, 1, 3, 256, 1024, page_size=64,
+                               seed=29, q_scale=2.0, shared=0.75)
+    hq = case.kv_heads * case.group
+    op = binding.SparseAttn(case.rows, 1, 3, 256, case.k_tokens, case.num_slots, rows_per_seq=4,
+                            page_size=64, pages_per_seq=case.page_table.shape[1], union_rows=4)
+    q, kd, vd, gate = _bf(case.q), _bf(case.k_cache), _bf(case.v_cache), _bf(case.gate)
+    ids = torch.from_numpy(case.token_ids).cuda()
+    table = torch.from_numpy(case.page_table).cuda()
+    out = torch.empty((case.rows, hq, 256), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((case.rows, hq), device="cuda")
+    op(q, kd, vd, ids, table, gate, case.sm_scale, out, lse)
+    torch.cuda.synchronize()
+    first = _codes(out).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        op(q, kd, vd, ids, table, gate, case.sm_scale, out, lse)
+    torch.cuda.synchronize()
+    for it in range(6):
+        if it % 2 == 0:
+            new = case.token_ids.copy()
+        else:
+            other = wl.make_attn_custom(case.seq_lens, 4, 1, 3, 256, 1024, page_size=64,
+                                        seed=200 + it, host_caches=False, shared=0.2 * it)
+            new = other.token_ids
+        ids.copy_(torch.from_numpy(new))
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if it % 2 == 0:
+            assert np.array_equal(_codes(out), first), f"replay {it} differs from the eager call"
+        else:
+            c2 = wl.AttnCase(**{**case.__dict__, "token_ids": new})
+            _check(c2, _codes(out), lse.cpu().numpy(), distinct=True)
+    assert op.read_status() == 0
+    op.close()
+
+
+def test_attn_union_full_size_sampled_rows():
+    """The decode batch of 128 requests x 4 rows, 1 kv head x 3 query heads,
+    in union mode over device caches; sampled rows against the oracle."""
+    import torch
+    case = wl.make_attn_config("attn_decode_g3")
+    gh.log(f"attn_decode_g3: {case.rows} rows, {case.num_slots} slots, union of 4 rows")
+    kd, vd = _device_caches(case)
+    got, lse, status = _run(case, k_dev=kd, v_dev=vd, union_rows=4)
+    assert status == 0
+    valid = (case.token_ids >= 0).sum(1)
+    rng = np.random.default_rng(5)
+    rows = sorted(set([0, 1, 2, 3, case.rows - 1] + list(np.nonzero(valid < case.k_tokens)[0][:8])
+                      + list(rng.choice(case.rows, size=24, replace=False))))
+    gc = _gathered_case(case, kd, vd, rows)
+    _check(gc, got[rows], lse[rows])
+    assert np.all(np.isfinite(_f(got)))
+    assert np.array_equal(np.isfinite(lse).all(1), valid > 0)
+    del kd, vd
+    torch.cuda.empty_cache()
+
+
+def test_attn_union_rejects():
+    with pytest.raises(binding.DsaError):
+        binding.SparseAttn(8, 1, 5, 256, 64, 100, rows_per_seq=4, union_rows=4)    # 20 pairs
+    with pytest.raises(binding.DsaError):
+        binding.SparseAttn(8, 1, 3, 256, 8193, 100, rows_per_seq=4, union_rows=4)  # 32772 ids
+    with pytest.raises(binding.DsaError):
+        binding.SparseAttn(8, 1, 3, 256, 64, 100, rows_per_seq=6, union_rows=4)    # straddles
