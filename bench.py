@@ -311,9 +311,10 @@ def run_row_topk(rows: int, width: int, k: int, steps: int, warmup: int) -> dict
                 roofline={"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                           "basis": "4*L read + 4*k index stores + 8 B bounds per row over the "
-                                   "graph replay's time per call (the row is read four times: "
-                                   "three digit passes and the emit; a count pass reads it once "
-                                   "more only for rows settled before the third digit)"})
+                                   "graph replay's time per call (the row is read twice: the "
+                                   "first digit pass, and the second, which also lists the keys "
+                                   "from the first digit's bin up; the later passes work on "
+                                   "those lists)"})
 
 
 def attn_device_caches(case):

@@ -21,11 +21,16 @@
  * ranked by the order-preserving key (u >= 2^31 ? ~u : u | 2^31 on its bits):
  * infinities rank as values, a NaN ranks by its bit pattern.
  *
- * The context owns a workspace of (8448 + 12 + 261 P) words per row, P pieces
- * per row fixed at init from the shape and the device's CU count (it does not
- * grow with the row length).  dsa_row_topk enqueues five launches on `stream`
- * (three digit passes, the placement of every piece's output, the emit); it
- * allocates nothing, never synchronizes and can be captured in a HIP graph.  Calls on one context must be ordered on one stream.  Returns
+ * The context owns a workspace of (66816 + 12 + P (269 + 2 seg)) words per
+ * row, P pieces per row fixed at init from the shape and the device's CU
+ * count and seg (list entries per piece) about 4 k / P + 256 (it does not grow
+ * with the row length).  dsa_row_topk enqueues five launches on `stream`
+ * (three digit passes, the placement of every piece's output, the emit); the
+ * second pass also lists each piece's keys from the first digit's bin up when
+ * they fit, and the later launches then work on those lists instead of
+ * reading the row again.  It allocates nothing, never synchronizes and can be
+ * captured in a HIP graph.  Calls on one context must be ordered on one
+ * stream.  Returns
  * DSA_OK or a negative dsa_status (see dsa_select.h); the message is
  * dsa_row_topk_last_error().
  */

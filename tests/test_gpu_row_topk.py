@@ -4,8 +4,10 @@ Every row is compared element by element with the numpy oracle's top-k (a
 full sort on (value desc, column asc), pinned in tests/oracle_pins.py):
 rows of 1..20,000 columns with every k from 1 to beyond the row, ties,
 special values, non-zero starts, repeats and a strided view; rows of 4 and
-16 million columns with k of 2048 and of a million; k above the row length;
-agreement with dsa_topk on rows of 200,000; graph replay with changed ends.
+16 million columns with k of 2048 and of a million; a row whose list part
+overflows (it falls back to reading the row) and a row settled after the
+second digit in list mode; k above the row length; agreement with dsa_topk on
+rows of 200,000; graph replay with changed ends.
 """
 import numpy as np
 import pytest
@@ -106,6 +108,31 @@ def test_row_topk_very_long_rows(W, k):
     case = wl.make_custom(len(ends), W, 8, 1, 1, ends, starts=starts, seed=W // 1000 + k,
                           dup_frac=0.01, outlier_frac=0.001)
     gh.log(f"very long rows W={W} k={k}")
+    _check_case(case, k)
+
+
+def test_row_topk_list_overflow_falls_back():
+    """Row 0 holds its 5000 largest values inside its first piece, so that
+    piece's list of the first digit's bin and up overflows and the row falls
+    back to reading the row; row 1 (ordinary values) runs on its lists."""
+    W, k = 4 * 2**20, 2048
+    case = wl.make_custom(2, W, 8, 1, 1, [W, W - 3], seed=13)
+    rng = np.random.default_rng(13)
+    cols = rng.choice(16384, size=5000, replace=False)
+    case.buf[0, cols] = (np.float32(100.0) + np.arange(5000, dtype=np.float32) * np.float32(0.01))
+    _check_case(case, k)
+
+
+def test_row_topk_list_mode_settles_on_third_digit():
+    """The 1500 largest values share the first digit's bin and have distinct
+    second digits, so the K-th key's bin after two digits holds it alone: the
+    row is settled before the third digit and counted from its lists."""
+    W, k = 2**20, 1000
+    case = wl.make_custom(1, W, 8, 1, 1, [W], seed=17)
+    rng = np.random.default_rng(17)
+    case.buf[0, :] = rng.random(W, dtype=np.float32) * np.float32(0.9)
+    cols = rng.choice(W, size=1500, replace=False)
+    case.buf[0, cols] = np.float32(1.0) + np.arange(1500, dtype=np.float32) * np.float32(2.0 ** -15)
     _check_case(case, k)
 
 
