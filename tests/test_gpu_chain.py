@@ -31,8 +31,9 @@ def _device():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("B,kb,kt", [(8, 64, 512), (16, 16, 200)])
-def test_indexer_selection_then_attention(B, kb, kt):
+@pytest.mark.parametrize("B,kb,kt,union", [(8, 64, 512, False), (16, 16, 200, False),
+                                            (8, 64, 512, True)])
+def test_indexer_selection_then_attention(B, kb, kt, union):
     import torch
     rng = np.random.default_rng(B + kb)
     lens = np.array([6000, 1500, 300, 9000])           # per request
@@ -54,26 +55,30 @@ def test_indexer_selection_then_attention(B, kb, kt):
     got_tok = tok.cpu().numpy()
     assert np.array_equal(got_tok, wt), "selected tokens differ from the oracle"
 
-    # attention of each row over its selected tokens, flat cache (slot = position)
-    hkv, G, D = 2, 6, 128
+    # attention of each row over its selected tokens, flat cache (slot = position);
+    # in union mode the 4 rows of a request run over the union of their ids
+    # (groups of 4 rows need 4 * G <= 16 (row, head) pairs, so G = 3)
+    hkv, G, D = (2, 3, 128) if union else (2, 6, 128)
     ac = wl.make_attn_custom([S], 1, hkv, G, D, kt, paged=False, seed=41 + B, q_scale=2.0)
     q = wl.bf16_bits(rng.standard_normal((Q, hkv * G, D), dtype=np.float32) * np.float32(2.0))
     gate = wl.bf16_bits(rng.standard_normal((Q, hkv * G, D), dtype=np.float32))
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
         torch.bfloat16).cuda()
-    op = binding.SparseAttn(Q, hkv, G, D, kt, ac.num_slots)
+    op = binding.SparseAttn(Q, hkv, G, D, kt, ac.num_slots, rows_per_seq=4 if union else 1,
+                            union_rows=4 if union else 0)
     out = op(bf(q), bf(ac.k_cache), bf(ac.v_cache), tok, None, bf(gate), ac.sm_scale)
     torch.cuda.synchronize()
     assert op.read_status() == 0
     op.close()
     got = (out.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16).view(
         np.float32).astype(np.float64)
-    ref, _, bad = so.sparse_attention(q, ac.k_cache, ac.v_cache, wt, ac.sm_scale, G, gate=gate)
+    ref, _, bad = so.sparse_attention(q, ac.k_cache, ac.v_cache, wt, ac.sm_scale, G, gate=gate,
+                                      distinct=union)
     A, _, _ = so.sparse_attention(q, ac.k_cache, ac.v_cache & np.uint16(0x7FFF), wt,
-                                  ac.sm_scale, G, gate=gate)
+                                  ac.sm_scale, G, gate=gate, distinct=union)
     assert bad.sum() == 0
     tol = 2.0 ** -7 * A + 2.0 ** -8 * np.abs(ref)
     err = np.abs(got - ref)
     assert np.all(err <= tol), f"worst excess {np.max(err - tol):.3e}"
     gh.log(f"  chain: {Q} rows over {S} keys, B={B}, top-{kb} blocks, top-{kt} tokens, "
-           f"then attention {hkv}x{G}x{D}")
+           f"then attention {hkv}x{G}x{D}{' in union mode' if union else ''}")
