@@ -50,10 +50,19 @@ namespace dsa {
 namespace idx {
 
 constexpr int WAVES = 4;            // query rows per workgroup
-constexpr int CAP = 1024;           // candidate entries per wave
-constexpr int KMAX = CAP / 2;       // largest K the streaming select keeps
+// Two forms of the per-row machinery.  The narrow one (768 candidate entries
+// per wave, keys staged 64 at a time: 51 KB of LDS and at most 168 VGPRs)
+// fits three workgroups per CU, and the extra waves hide the matrix and LDS
+// latencies between the epilogues' vector instructions; the wide one (1024
+// entries, 128 keys per stage, two workgroups per CU) keeps K up to 512.
+template <bool WIDE>
+struct Form {
+  static constexpr int CAP = WIDE ? 1024 : 768;   // candidate entries per wave
+  static constexpr int KMAX = CAP / 2;            // largest K the streaming select keeps
+  static constexpr int STAGE = WIDE ? 128 : 64;   // keys staged in LDS per step (shared mode)
+  static constexpr int MIN_WG = WIDE ? 2 : 3;     // workgroups per CU the registers allow
+};
 constexpr int D = 128;              // head dimension (bytes per FP8 key)
-constexpr int STAGE = 128;          // keys staged in LDS per step (shared mode)
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -72,11 +81,12 @@ struct Args {
   int32_t Q, H, B, k_blocks, k_tokens, starts_repeat, ends_repeat;
 };
 
+template <int CAP>
 struct WaveLds {
   uint32_t key[CAP];
   uint32_t id[CAP];
   uint32_t hist[256];
-  uint32_t sel[KMAX];
+  uint32_t sel[CAP / 2];
 };
 
 // Completes this wave's LDS operations and keeps the compiler from moving
@@ -90,7 +100,8 @@ DSA_DEV void wave_lds_sync() {
 // order: afterwards the buffer holds exactly min(K, n) entries in their
 // original order.  Returns the key of the K-th best (the new threshold), or
 // 0 when n <= K.
-DSA_DEV uint32_t wave_keep_top(WaveLds& s, int n, int K) {
+template <int CAP>
+DSA_DEV uint32_t wave_keep_top(WaveLds<CAP>& s, int n, int K) {
   const int l = lane();
   if (n <= K) return 0u;
   constexpr int PER = CAP / 64;
@@ -172,7 +183,8 @@ DSA_DEV uint32_t wave_keep_top(WaveLds& s, int n, int K) {
 // Offers one (key, id) per lane (where `valid`); entries above the running
 // threshold `thr` are appended in lane order.  A full buffer is first cut to
 // its K best, which raises the threshold.
-DSA_DEV void wave_offer(WaveLds& s, int& n, uint32_t& thr, int K, bool valid, uint32_t key,
+template <int CAP>
+DSA_DEV void wave_offer(WaveLds<CAP>& s, int& n, uint32_t& thr, int K, bool valid, uint32_t key,
                         uint32_t id) {
   uint64_t m = ballot(valid && key > thr);
   if (m == 0) return;
@@ -270,13 +282,15 @@ DSA_DEV v8i lds_key_slice(const uint8_t* tile, int h) {
   return v;
 }
 
-template <int HG, int BS>
-__global__ __launch_bounds__(64 * WAVES) void k_indexer_select(Args a) {
-  __shared__ WaveLds lds[WAVES];
+template <int HG, int BS, bool WIDE>
+__global__ __launch_bounds__(64 * WAVES, Form<WIDE>::MIN_WG) void k_indexer_select(Args a) {
+  constexpr int CAP = Form<WIDE>::CAP;
+  constexpr int STAGE = Form<WIDE>::STAGE;
+  __shared__ WaveLds<CAP> lds[WAVES];
   __shared__ __align__(16) uint8_t ktile[2][STAGE * D];   // staged keys, double buffered
   __shared__ int64_t row_s[WAVES], row_e[WAVES];
   const int w = wave(), l = lane();
-  WaveLds& s = lds[w];
+  WaveLds<CAP>& s = lds[w];
   const int t = (int)blockIdx.x * WAVES + w;
   // Row bounds (both loads issued before either is used); rows past the
   // last query are empty.
@@ -353,30 +367,35 @@ __global__ __launch_bounds__(64 * WAVES) void k_indexer_select(Args a) {
     wave_offer(s, n, thr, Kb, head, key, (uint32_t)b);
   };
   if (shared_mode) {
-    // Each thread stages 4 of the 1024 16-byte chunks of a 128-key step;
-    // the next step's chunks are loaded into registers while this step's
-    // 8 halves are computed from LDS.
+    // Each thread stages PER_T of the 16-byte chunks of a STAGE-key step
+    // (8 per key); the next step's chunks are loaded into registers while
+    // this step's halves are computed from LDS.
     const int tid = (int)threadIdx.x;
     constexpr int PER_T = STAGE * D / 16 / (64 * WAVES);
+    static_assert(PER_T * 32 == STAGE, "32 key rows per staged chunk round");
     // chunk u of this thread: key row (tid >> 3) + 32 u, chunk tid & 7
     const int tr = tid >> 3, tj = tid & 7;
     const int soff0 = tr * D + 16 * (tj ^ (tr & 7));     // (row + 32 u) & 7 == row & 7
-    int4 nxt0, nxt1, nxt2, nxt3;
-    static_assert(PER_T == 4, "four staged chunks per thread");
+    static_assert(PER_T == 2 || PER_T == 4, "two or four staged chunks per thread");
+    int4 nxt0, nxt1, nxt2, nxt3;                         // nxt2, nxt3: four per thread
 #define DSA_IDX_FETCH(k0)                                                                   \
     do {                                                                                    \
       const uint8_t* src_ = a.k + 16 * tj;                                                  \
       nxt0 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr, top - 1) * D);            \
       nxt1 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr + 32, top - 1) * D);       \
-      nxt2 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr + 64, top - 1) * D);       \
-      nxt3 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr + 96, top - 1) * D);       \
+      if constexpr (PER_T == 4) {                                                           \
+        nxt2 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr + 64, top - 1) * D);     \
+        nxt3 = *reinterpret_cast<const int4*>(src_ + min((k0) + tr + 96, top - 1) * D);     \
+      }                                                                                     \
     } while (0)
 #define DSA_IDX_STAGE(buf)                                                                  \
     do {                                                                                    \
       *reinterpret_cast<int4*>((buf) + soff0) = nxt0;                                       \
       *reinterpret_cast<int4*>((buf) + soff0 + 32 * D) = nxt1;                              \
-      *reinterpret_cast<int4*>((buf) + soff0 + 64 * D) = nxt2;                              \
-      *reinterpret_cast<int4*>((buf) + soff0 + 96 * D) = nxt3;                              \
+      if constexpr (PER_T == 4) {                                                           \
+        *reinterpret_cast<int4*>((buf) + soff0 + 64 * D) = nxt2;                            \
+        *reinterpret_cast<int4*>((buf) + soff0 + 96 * D) = nxt3;                            \
+      }                                                                                     \
     } while (0)
     // key scales of this lane's keys in a step (k0 + 32 m + l % 32), one
     // step ahead like the keys
@@ -532,15 +551,16 @@ int idx_fail(int code, const char* fmt, ...) {
   return code;
 }
 
-template <int HG>
+template <int HG, bool WIDE>
 int launch_hg(int B, unsigned grid, const dsa::idx::Args& a, hipStream_t st) {
   using namespace dsa::idx;
+  const dim3 g(grid), t(64 * WAVES);
   switch (B) {
-    case 1: hipLaunchKernelGGL((k_indexer_select<HG, 1>), dim3(grid), dim3(64 * WAVES), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_indexer_select<HG, 2>), dim3(grid), dim3(64 * WAVES), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_indexer_select<HG, 4>), dim3(grid), dim3(64 * WAVES), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_indexer_select<HG, 8>), dim3(grid), dim3(64 * WAVES), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_indexer_select<HG, 16>), dim3(grid), dim3(64 * WAVES), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_indexer_select<HG, 1, WIDE>), g, t, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_indexer_select<HG, 2, WIDE>), g, t, 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_indexer_select<HG, 4, WIDE>), g, t, 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_indexer_select<HG, 8, WIDE>), g, t, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_indexer_select<HG, 16, WIDE>), g, t, 0, st, a); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return idx_fail(DSA_ERR_HIP, "k_indexer_select launch: %s", hipGetErrorString(e));
@@ -569,10 +589,15 @@ int dsa_indexer_select(const dsa_indexer_shape* sh, int device, const uint8_t* q
     return idx_fail(DSA_ERR_UNSUPPORTED, "block_size must be 1, 2, 4, 8 or 16");
   if (sh->k_blocks < 1 || sh->k_tokens < 1)
     return idx_fail(DSA_ERR_INVALID_ARG, "k_blocks and k_tokens must be >= 1");
+  constexpr int KMAX = Form<true>::KMAX;
   if (sh->k_blocks > KMAX) return idx_fail(DSA_ERR_UNSUPPORTED, "k_blocks must be <= %d", KMAX);
-  if ((int64_t)sh->k_blocks * B > sh->k_tokens && sh->k_tokens > KMAX)
+  const bool recompute = (int64_t)sh->k_blocks * B > sh->k_tokens;   // tokens selected again
+  if (recompute && sh->k_tokens > KMAX)
     return idx_fail(DSA_ERR_UNSUPPORTED,
                     "k_tokens must be <= %d when k_blocks * block_size exceeds it", KMAX);
+  // the narrow form when its buffer holds every K the call keeps
+  constexpr int KN = Form<false>::KMAX;
+  const bool wide = sh->k_blocks > KN || (recompute && sh->k_tokens > KN);
   if (sh->starts_repeat < 1 || sh->ends_repeat < 1)
     return idx_fail(DSA_ERR_INVALID_ARG, "repeats must be >= 1");
   if (device < 0) return idx_fail(DSA_ERR_INVALID_ARG, "device must be >= 0");
@@ -595,9 +620,12 @@ int dsa_indexer_select(const dsa_indexer_shape* sh, int device, const uint8_t* q
   a.starts_repeat = sh->starts_repeat; a.ends_repeat = sh->ends_repeat;
   const unsigned grid = (unsigned)((sh->queries + WAVES - 1) / WAVES);
   int rc;
-  if (sh->heads == 16) rc = launch_hg<1>(B, grid, a, stream);
-  else if (sh->heads == 32) rc = launch_hg<2>(B, grid, a, stream);
-  else rc = launch_hg<4>(B, grid, a, stream);
+  if (sh->heads == 16)
+    rc = wide ? launch_hg<1, true>(B, grid, a, stream) : launch_hg<1, false>(B, grid, a, stream);
+  else if (sh->heads == 32)
+    rc = wide ? launch_hg<2, true>(B, grid, a, stream) : launch_hg<2, false>(B, grid, a, stream);
+  else
+    rc = wide ? launch_hg<4, true>(B, grid, a, stream) : launch_hg<4, false>(B, grid, a, stream);
   if (cur != device) (void)hipSetDevice(cur);
   return rc;
 }
