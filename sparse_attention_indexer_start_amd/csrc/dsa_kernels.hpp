@@ -217,9 +217,15 @@ DSA_DEV uint32_t block_max_key(const float* rowp, int64_t cs, bool vec, int64_t 
 // Block scores of blocks [b0, b1): emit(b, key) once per block.
 // ---------------------------------------------------------------------------
 // `low` is set when some live value of the range ranks at or below -inf.
-template <int BS, int UNR = UNROLL, class Emit>
+// On a contiguous range with B >= 4, mid() runs once, in every thread, after
+// the first round's loads are issued and before any is used (work that can
+// overlap their latency; it may hold a barrier).
+struct NoMid {
+  DSA_DEV void operator()() const {}
+};
+template <int BS, int UNR = UNROLL, class Emit, class Mid = NoMid>
 DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, int b1,
-                          int nlb, bool vec, Emit emit, bool& low) {
+                          int nlb, bool vec, Emit emit, bool& low, Mid mid = Mid()) {
   if constexpr (BS >= 4) {
     constexpr int G = BS / 4;          // lanes per block, 4 columns per lane
     const int64_t cbeg = (int64_t)b0 * BS;
@@ -319,6 +325,7 @@ DSA_DEV void score_blocks(const float* rowp, int64_t cs, int B, int L, int b0, i
 #pragma unroll
         for (int u = 0; u < UNR; ++u)
           if (u == tu) v[u] = f4v{t0, t1, t2, z};
+        if (c0 == cbeg) mid();
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
           const int64_t col = c0 + (int64_t)u * NT * 4 + t4;
@@ -766,17 +773,31 @@ DSA_DEV void small_row(const Params& p, int r, const Row& rb, Smem& sm) {
     // completes it.  The histogram is cleared first, behind a barrier of its
     // own: a lane's count may land before another wave's clear otherwise.
     const bool do_select = nlb > Kp;
-    if (do_select) {
+    // On a contiguous row (B >= 4) the clear runs while the row's first loads
+    // are in flight: score_blocks calls it after issuing them, and its barrier
+    // waits for the LDS stores only.
+    const bool clear_mid = BS >= 4 && vec;
+    if (do_select && !clear_mid) {
       for (int j = threadIdx.x; j < HIST_WORDS; j += NT) sm.hist[j] = 0;
       if (!vec)
         for (int j = threadIdx.x; j < (nlb + 31) / 32; j += NT) sm.bits[j] = 0;
       __syncthreads();
     }
+    auto clear_hist = [&]() {
+      if (do_select && clear_mid) {
+        static_assert(HIST_WORDS == 8 * NT, "two 16-byte stores per thread");
+        uint4* h4 = reinterpret_cast<uint4*>(sm.hist);   // the first member of Smem
+        h4[threadIdx.x] = make_uint4(0, 0, 0, 0);
+        h4[threadIdx.x + NT] = make_uint4(0, 0, 0, 0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+      }
+    };
     score_blocks<BS>(rowp, p.col_stride, B, L, 0, nlb, nlb, vec, [&](int b, uint32_t k) {
       keys[b] = k;
       if (sc) sc[b] = key2f(k);
       if (do_select) atomicAdd(&sm.hist[k >> 20], 1u);
-    }, low);
+    }, low, clear_hist);
     no_low = __syncthreads_or(low) == 0;
     auto getk = [&](int i) { return keys[i]; };
     if (do_select) wg_radix_select<NT>(nlb, (uint32_t)Kp, getk, sm, T, q, true, true);
