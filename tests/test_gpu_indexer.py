@@ -85,7 +85,11 @@ def test_indexer_recomputed_token_route():
 
 
 @pytest.mark.parametrize("H,B,kb,kt", [(16, 1, 200, 150), (32, 2, 100, 200), (64, 4, 50, 200),
-                                       (16, 16, 20, 320), (32, 16, 40, 100), (64, 8, 512, 4096)])
+                                       (16, 16, 20, 320), (32, 16, 40, 100), (64, 8, 512, 4096),
+                                       # either side of the narrow form's limit (384):
+                                       # narrow with the recompute route at 384 tokens, wide
+                                       # with 385 blocks and with 385 recomputed tokens
+                                       (64, 2, 384, 384), (32, 2, 385, 1000), (16, 4, 200, 385)])
 def test_indexer_shapes(H, B, kb, kt):
     rng = np.random.default_rng(H * 100 + B)
     Q, S = 6, 9000
