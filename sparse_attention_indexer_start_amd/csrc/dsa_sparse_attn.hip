@@ -180,6 +180,7 @@ __global__ void __launch_bounds__(UNT) k_union(UArgs a) {
   __shared__ uint4 mask4[UCAP / 8];           // 16-bit row masks by union index
   __shared__ int wred[UNT / 64];
   __shared__ int wmin[UNT / 64];
+  __shared__ int wmax[UNT / 64];
   uint32_t* pres = reinterpret_cast<uint32_t*>(pres4);
   uint32_t* maskw = reinterpret_cast<uint32_t*>(mask4);
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -222,42 +223,43 @@ __global__ void __launch_bounds__(UNT) k_union(UArgs a) {
       }
     }
   };
-  int lo = INT32_MAX;
-  each_id([&](int p, uint32_t, bool v) { if (v && p >= 0) lo = min(lo, p); });
+  // lo, hi: the group's lowest and highest position
+  int lo = INT32_MAX, hi = -1;
+  each_id([&](int p, uint32_t, bool v) {
+    if (v && p >= 0) {
+      lo = min(lo, p);
+      hi = max(hi, p);
+    }
+  });
   lo = wave_min(lo);
-  if (lane == 0) wmin[wv] = lo;
+  hi = -wave_min(-hi);
+  if (lane == 0) {
+    wmin[wv] = lo;
+    wmax[wv] = hi;
+  }
   __syncthreads();
   lo = INT32_MAX;
 #pragma unroll
-  for (int k = 0; k < UNT / 64; ++k) lo = min(lo, wmin[k]);
+  for (int k = 0; k < UNT / 64; ++k) {
+    lo = min(lo, wmin[k]);
+    hi = max(hi, wmax[k]);
+  }
   int total = 0;
   int2* ent = a.ent + (int64_t)gi * a.cap;
   while (lo != INT32_MAX) {                     // uniform: every thread holds the same lo
     const int base = lo - lo % UWIN;
     const int64_t end = (int64_t)base + UWIN;
-    for (int k = t; k < NW / 4; k += UNT) pres4[k] = make_uint4(0, 0, 0, 0);
-    for (int k = t; k < UCAP / 8; k += UNT) mask4[k] = make_uint4(0, 0, 0, 0);
+    // Only the bitmap's words up to the group's highest position are used
+    // (cleared and scanned); the rest count as empty.
+    const int nwc = (int)min((int64_t)NW, ((int64_t)hi - base) / 32 + 1);
+    const int nq = (nwc + 3) / 4;               // 16-byte groups of words in use
+    for (int k = t; k < nq; k += UNT) pres4[k] = make_uint4(0, 0, 0, 0);
     __syncthreads();                            // cleared
     int nxt = INT32_MAX;
     each_id([&](int p, uint32_t, bool v) {
       const bool in = v && p >= base && p < end;
       const int o = p - base;
-      int wd = in ? o >> 5 : -1 - lane;         // distinct for lanes outside the window
-      uint32_t bits = in ? 1u << (o & 31) : 0u;
-      // A dense window puts neighbouring lanes (neighbouring ids of one row)
-      // on one word: OR their bits along the run first, so that one lane per
-      // run issues the LDS atomic instead of up to 32 in a row.
-      if (__ballot(__shfl_down(wd, 1) == wd && lane < 63)) {
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t ob = __shfl_down(bits, off);
-          const int ow = __shfl_down(wd, off);
-          if (lane + off < 64 && ow == wd) bits |= ob;
-        }
-        const int pw = __shfl_up(wd, 1);
-        if (lane > 0 && pw == wd) bits = 0u;    // not the first lane of its run
-      }
-      if (bits) atomicOr(&pres[wd], bits);
+      if (in) atomicOr(&pres[o >> 5], 1u << (o & 31));
       if (v && p >= end) nxt = min(nxt, p);
     });
     nxt = wave_min(nxt);
@@ -268,7 +270,8 @@ __global__ void __launch_bounds__(UNT) k_union(UArgs a) {
     int c = 0;
 #pragma unroll
     for (int k = 0; k < WPT / 4; ++k) {
-      const uint4 x = pres4[t * (WPT / 4) + k];
+      const int qk = t * (WPT / 4) + k;
+      const uint4 x = qk < nq ? pres4[qk] : make_uint4(0, 0, 0, 0);
       w[4 * k] = x.x; w[4 * k + 1] = x.y; w[4 * k + 2] = x.z; w[4 * k + 3] = x.w;
     }
 #pragma unroll
@@ -290,7 +293,9 @@ __global__ void __launch_bounds__(UNT) k_union(UArgs a) {
         run += __popc(w[k]);
       }
     }
-    __syncthreads();                            // union indices known
+    // the row masks of this window's `all` entries (two per word)
+    for (int k = t; k < (all + 7) / 8; k += UNT) mask4[k] = make_uint4(0, 0, 0, 0);
+    __syncthreads();                            // union indices known, masks cleared
     each_id([&](int p, uint32_t rb, bool v) {
       if (v && p >= base && p < end) {
         const int o = p - base;
