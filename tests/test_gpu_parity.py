@@ -89,12 +89,46 @@ def test_fused_fuzz(seed):
     (16, 65536, [65536, 30000, 16385, 16384], 128, 2048),   # medium rows: split
     (8, 32768, [32768, 16385, 16384, 20001], 300, 3000),
     (4, 200000, [200000, 100003], 600, 5000),
+    (64, 40000, [40000, 30001, 16385], 700, 3000),          # medium rows, every block kept
 ])
 def test_fused_long_rows(B, W, ends, kb, kt, two):
     """Rows longer than one workgroup's LDS share: the two-pass path."""
     case = wl.make_custom(len(ends), W, B, kb, kt, ends, seed=B * 7 + kb, dup_frac=0.02,
                           outlier_frac=0.01)
     gh.log(f"long rows B={B} W={W} ends={ends} kb={kb} kt={kt} two_launches={two}")
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused(two_launches=two)
+    _full_check(dc, bids, tids, scores)
+
+
+@pytest.mark.parametrize("with_scores", [True, False], ids=["scores", "no_scores"])
+def test_fused_medium_rows_keep_all(with_scores):
+    """Rows of at most LIST_CAP blocks that are longer than one workgroup
+    reads alone (the two-pass split), with K_blk at or above their block
+    count: every block is kept, with and without a scores output."""
+    ends = [65536, 40000, 16385, 16384, 30000]
+    case = wl.make_custom(len(ends), 65536, 32, 2048, 3000, ends, seed=313, dup_frac=0.05)
+    gh.log(f"medium rows keep all ends={ends} with_scores={with_scores}")
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused(with_scores=with_scores)
+    gh.check_rows_against_oracle(dc, range(dc.sh.rows), bids, tids, scores)
+    gh.check_all_rows_c(dc, bids, tids, scores)
+    gh.check_whole_buffer(dc)
+
+
+@pytest.mark.parametrize("two", [False, True], ids=["one_launch", "two_launches"])
+def test_fused_medium_rows_per_row_split(two):
+    """300 rows take the per-row split with two workgroups per row: rows of at
+    most LIST_CAP blocks but longer than one workgroup reads alone go through
+    both passes and the final workgroup, in one launch and in two."""
+    rng = np.random.default_rng(4242)
+    R, W = 300, 32768
+    ends = rng.integers(16385, W + 1, size=R)
+    ends[:8] = [W, 16385, 16384, 1, 0, 20000, W - 1, 30001]
+    starts = rng.integers(0, 64, size=R)
+    case = wl.make_custom(R, W, 8, 300, 3000, ends, starts=starts, col_stride=2 if two else 1,
+                          seed=4242, dup_frac=0.02, outlier_frac=0.01)
+    gh.log(f"medium rows per-row split R={R} W={W} two_launches={two}")
     dc = gh.DevCase(case)
     bids, tids, scores = dc.run_fused(two_launches=two)
     _full_check(dc, bids, tids, scores)
