@@ -136,6 +136,20 @@ def test_row_topk_list_mode_settles_on_third_digit():
     _check_case(case, k)
 
 
+def test_row_topk_many_listed_settles_on_third_digit():
+    """8000 large values: 3904 in the first digit's top bin and 4096 in the
+    next one, with distinct second digits, and k = 6500: the row is settled
+    after two digits with 2596 of the 4096 keys of the second bin taken,
+    counted and emitted from lists that span both bins."""
+    W, k = 2**20, 6500
+    case = wl.make_custom(1, W, 8, 1, 1, [W], seed=19)
+    rng = np.random.default_rng(19)
+    case.buf[0, :] = rng.random(W, dtype=np.float32) * np.float32(0.9)
+    cols = rng.choice(W, size=8000, replace=False)
+    case.buf[0, cols] = np.float32(1.0) + np.arange(8000, dtype=np.float32) * np.float32(2.0 ** -15)
+    _check_case(case, k)
+
+
 def test_row_topk_k_beyond_row():
     W = 3 * 2**20
     case = wl.make_custom(2, W, 8, 1, 1, [W, 2 * 2**20], seed=9)
