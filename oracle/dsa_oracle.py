@@ -33,9 +33,11 @@ notes):
   picks are the lowest-index ``-inf`` columns, which is what ranking the whole
   masked row with ties to the lower index gives.
 
-Parity against printed values is unpinned: the pages print no worked
-input/output pair.  The oracle is pinned instead by brute force, closed forms,
-special cases and invariants in ``tests/test_oracle_pins.py``.
+The pages print no worked input/output pair for this chain, so no pin
+compares with printed outputs; every function here is pinned instead by brute
+force, closed forms, special cases and invariants in
+``tests/test_oracle_pins.py``, and by the cases the pages do print (ragged
+ends, sentinels) under ``tests/golden/``.
 """
 from __future__ import annotations
 
