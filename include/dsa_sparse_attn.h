@@ -30,9 +30,18 @@
  * fp32 with bf16 products on the matrix cores (the softmax weights are
  * rounded to bf16 before they multiply V), the output is rounded to bf16.
  *
- * Limits: head_dim 128 or 256; group 1..16; kv_heads >= 1; page_size a power
- * of two; num_slots < 2^31.  Union mode also needs union_rows * group <= 16,
- * union_rows * k_tokens <= 32768 and rows_per_seq % union_rows == 0.
+ * Limits: head_dim 128 or 256; group >= 1 and kv_heads >= 1 with kv_heads *
+ * group <= 2^20; page_size a power of two; num_slots < 2^31.  Union mode also
+ * needs union_rows <= 16, union_rows * k_tokens <= 32768 and rows_per_seq %
+ * union_rows == 0.
+ *
+ * Head tiles: one matrix product covers 16 (row, query head) pairs, so each
+ * kv head's group of query heads is cut into T equal tiles, T the smallest
+ * divisor of group with union_rows * group / T <= 16 (union_rows counts 1
+ * outside union mode): T = 1 up to 16 heads per kv head, 8 for 128.  The
+ * tiles of one kv head run side by side in one workgroup where they fit
+ * (up to four tiles), so its K and V rows are read once from memory for all
+ * of them.
  *
  * Union mode (shape.union_rows >= 2; the page on vllm PR #48726, "LiteDSA:
  * grouped masked sparse attention", packs neighbouring queries into one
@@ -41,9 +50,8 @@
  * union_rows (all of one sequence, so union_rows divides rows_per_seq; the
  * last group may be shorter).  The group's ids are merged into one list of
  * distinct positions, each with a bit per row that selected it, and every
- * union token's K and V rows are read once for all union_rows * group
- * (row, head) pairs, which share one 16-row matrix tile (union_rows * group <=
- * 16).  The result is the attention above with each row's ids taken as a
+ * union token's K and V rows are read for all union_rows * group (row, head)
+ * pairs at once, union_rows * group / T of them per matrix tile.  The result is the attention above with each row's ids taken as a
  * set: an id a row lists twice counts once (ids from the selection are
  * distinct, so the two modes then agree).  Union mode issues two launches
  * (the union, then the attention) and holds union_rows * k_tokens 8-byte
@@ -72,7 +80,7 @@ extern "C" {
 typedef struct dsa_attn_shape {
   int32_t rows;           /* query rows, >= 0 */
   int32_t kv_heads;       /* >= 1 */
-  int32_t group;          /* query heads per kv head, 1..16 */
+  int32_t group;          /* query heads per kv head, >= 1 */
   int32_t head_dim;       /* 128 or 256 */
   int32_t k_tokens;       /* ids per row, >= 1 */
   int32_t rows_per_seq;   /* rows sharing one page-table row, >= 1 */
@@ -81,7 +89,7 @@ typedef struct dsa_attn_shape {
   int64_t num_slots;      /* cache slots, < 2^31 */
   int64_t k_slot_stride, k_head_stride;   /* elements */
   int64_t v_slot_stride, v_head_stride;   /* elements */
-  int32_t chunks;         /* workgroups per (row or union group, kv head); 0 = chosen at init */
+  int32_t chunks;         /* workgroups per (row or union group, head tile); 0 = chosen at init */
   int32_t union_rows;     /* 0 or 1: each row on its own; >= 2: union mode (see above) */
 } dsa_attn_shape;
 
@@ -95,8 +103,8 @@ int dsa_sparse_attn_init(const dsa_attn_shape* shape, int device, dsa_attn_ctx**
 /* Frees the workspace (after the device finished using it). */
 int dsa_sparse_attn_destroy(dsa_attn_ctx* ctx);
 
-/* Chunks per (row, kv head), or per (union group, kv head) in union mode,
- * chosen at init (> 0), or a negative dsa_status. */
+/* Chunks per (row, head tile), or per (union group, head tile) in union
+ * mode, chosen at init (> 0), or a negative dsa_status. */
 int dsa_sparse_attn_chunks(const dsa_attn_ctx* ctx);
 
 int dsa_sparse_attn(dsa_attn_ctx* ctx, const uint16_t* q, const uint16_t* k_cache,

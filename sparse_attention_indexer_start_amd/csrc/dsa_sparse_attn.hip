@@ -72,8 +72,12 @@ struct Args {
   uint32_t* tickets;    // [rows * hkv / hw]
   uint32_t* status;
   int64_t k_ss, k_hs, v_ss, v_hs, num_slots;
+  // hkv and G count head tiles: the group's query heads are cut into tdiv
+  // tiles of G heads (kv head k's tiles are k * tdiv .. k * tdiv + tdiv - 1),
+  // so that each tile's (row, head) pairs fit one matrix tile.
   int32_t rows, hkv, G, K, rows_per_seq, page_shift, pps, chunks, spc;
-  int32_t hw;           // kv heads per workgroup (1, 2 or 4; divides hkv)
+  int32_t hw;           // head tiles per workgroup (1, 2 or 4; divides hkv)
+  int32_t tdiv;         // head tiles per kv head
   float c2;             // sm_scale * log2(e) (times k_scale for fp8 caches)
   float vscale;         // v_scale for fp8 caches, else 1
   // union mode
@@ -421,6 +425,7 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
   // ru: the row, or in union mode the group of rows
   const int ru = wgp / gblocks, gb = wgp - ru * gblocks;
   const int g = gb * a.hw + w % a.hw, wi = w / a.hw;
+  const int kvh = g / a.tdiv;     // the cache's kv head of head tile g
   const int seq = (UN ? ru * a.U : ru) / a.rows_per_seq;
   const int hq = a.hkv * a.G;
   // (row, head) pairs in the tile: G, or G per row of the group
@@ -506,8 +511,8 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
     }
     typename T::raw ka[KS], kb[KS];
     {
-      const int64_t o0 = (int64_t)max(sk0, 0) * a.k_ss + (int64_t)g * a.k_hs + 8 * j;
-      const int64_t o1 = (int64_t)max(sk1, 0) * a.k_ss + (int64_t)g * a.k_hs + 8 * j;
+      const int64_t o0 = (int64_t)max(sk0, 0) * a.k_ss + (int64_t)kvh * a.k_hs + 8 * j;
+      const int64_t o1 = (int64_t)max(sk1, 0) * a.k_ss + (int64_t)kvh * a.k_hs + 8 * j;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         ka[s] = sk0 >= 0 ? T::ld(a.kc, o0 + 32 * s) : T::zero();
@@ -517,7 +522,7 @@ __global__ void __launch_bounds__(NT, 2) k_sparse_attn(Args a) {
     typename T::raw vr[8][NC];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int64_t ov = (int64_t)max(sv[e], 0) * a.v_ss + (int64_t)g * a.v_hs + 8 * n;
+      const int64_t ov = (int64_t)max(sv[e], 0) * a.v_ss + (int64_t)kvh * a.v_hs + 8 * n;
 #pragma unroll
       for (int c = 0; c < NC; ++c) vr[e][c] = sv[e] >= 0 ? T::ld(a.vc, ov + 128 * c) : T::zero();
     }
@@ -728,6 +733,7 @@ struct dsa_attn_ctx {
   dsa_attn_shape sh;
   int device;
   int chunks, spc, hw;
+  int T, hkv, G;        // head tiles per kv head, head tiles in all, query heads per tile
   int U, nru, cap;      // rows per union group (1 outside union mode), groups or rows, U * K
   void* ws;
   size_t ws_bytes;
@@ -787,8 +793,9 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   if (!s) return sa_fail(DSA_ERR_INVALID_ARG, "shape is null");
   if (s->rows < 0) return sa_fail(DSA_ERR_INVALID_ARG, "rows must be >= 0");
   if (s->kv_heads < 1) return sa_fail(DSA_ERR_INVALID_ARG, "kv_heads must be >= 1");
-  if (s->group < 1 || s->group > GMAX)
-    return sa_fail(DSA_ERR_UNSUPPORTED, "group must be in 1..%d (got %d)", GMAX, s->group);
+  if (s->group < 1) return sa_fail(DSA_ERR_INVALID_ARG, "group must be >= 1 (got %d)", s->group);
+  if ((int64_t)s->kv_heads * s->group > (1 << 20))
+    return sa_fail(DSA_ERR_UNSUPPORTED, "kv_heads * group must be <= 2^20");
   if (s->head_dim != 128 && s->head_dim != 256)
     return sa_fail(DSA_ERR_UNSUPPORTED, "head_dim must be 128 or 256 (got %d)", s->head_dim);
   if (s->k_tokens < 1) return sa_fail(DSA_ERR_INVALID_ARG, "k_tokens must be >= 1");
@@ -809,17 +816,22 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   if (s->union_rows < 0) return sa_fail(DSA_ERR_INVALID_ARG, "union_rows must be >= 0");
   const int U = std::max(1, s->union_rows);
   if (U > 1) {
-    if (U * s->group > GMAX)
-      return sa_fail(DSA_ERR_UNSUPPORTED, "union_rows * group must be <= %d (got %d * %d)", GMAX, U,
-                     s->group);
+    if (U > GMAX)
+      return sa_fail(DSA_ERR_UNSUPPORTED, "union_rows must be <= %d (one bit per row; got %d)", GMAX,
+                     U);
     if ((int64_t)U * s->k_tokens > UCAP)
       return sa_fail(DSA_ERR_UNSUPPORTED, "union_rows * k_tokens must be <= %d", UCAP);
     if (s->rows_per_seq % U)
       return sa_fail(DSA_ERR_INVALID_ARG, "union_rows must divide rows_per_seq (a group lies in "
                      "one sequence)");
   }
-  const int64_t pairs = (int64_t)s->rows * s->kv_heads;
-  if (pairs > ((int64_t)1 << 30)) return sa_fail(DSA_ERR_UNSUPPORTED, "too many rows");
+  // Head tiles: the fewest equal parts of the group whose (row, head) pairs,
+  // union_rows rows of them in union mode, fit one 16-row matrix tile.
+  int T = 1;
+  while (s->group % T || (int64_t)U * (s->group / T) > GMAX) ++T;
+  const int64_t hkv = (int64_t)s->kv_heads * T;
+  const int64_t pairs = (int64_t)s->rows * hkv;
+  if (pairs > ((int64_t)1 << 30)) return sa_fail(DSA_ERR_UNSUPPORTED, "too many rows or heads");
   if (device < 0) return sa_fail(DSA_ERR_INVALID_ARG, "device must be >= 0");
   DeviceScope ds(device);
   if (ds.e != hipSuccess) return sa_hip(ds.e, "hipSetDevice");
@@ -833,14 +845,16 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   c->sh = *s;
   c->device = device;
   c->magic = SA_MAGIC;
-  // kv heads per workgroup, and chunks per (row or union group, group of kv
-  // heads): enough workgroups for two per CU, each chunk at least one step per
-  // wave of one row's list (a union holds between k_tokens and U * k_tokens
-  // tokens; more chunks would multiply the partials the last workgroup
-  // merges, U * group pairs of them per chunk).
-  const int hw = s->kv_heads % 4 == 0 ? 4 : s->kv_heads % 2 == 0 ? 2 : 1;
+  // Head tiles per workgroup (the tiles of one kv head are neighbours, so a
+  // workgroup's waves read the same cache rows), and chunks per (row or union
+  // group, group of head tiles): enough workgroups for two per CU, each chunk
+  // at least one step per wave of one row's list (a union holds between
+  // k_tokens and U * k_tokens tokens; more chunks would multiply the partials
+  // the last workgroup merges, U * G pairs of them per chunk and tile).
+  const int G = s->group / T;
+  const int hw = hkv % 4 == 0 ? 4 : hkv % 2 == 0 ? 2 : 1;
   const int64_t nru = U > 1 ? (s->rows + U - 1) / U : s->rows;
-  const int64_t wgp = nru * (s->kv_heads / hw);
+  const int64_t wgp = nru * (hkv / hw);
   const int64_t steps = (s->k_tokens + STEP - 1) / STEP;
   const int64_t maxc = std::max<int64_t>(1, steps / (WAVES / hw));
   int64_t ch = s->chunks > 0 ? s->chunks
@@ -848,22 +862,25 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   ch = std::max<int64_t>(1, std::min<int64_t>(ch, s->chunks > 0 ? steps : maxc));
   // the merge stages hw * U * group (maximum, sum) pairs per chunk in the
   // waves' LDS partial space
-  ch = std::min<int64_t>(ch, (int64_t)WAVES * GMAX * D * 4 / (8 * hw * U * s->group));
+  ch = std::min<int64_t>(ch, (int64_t)WAVES * GMAX * D * 4 / (8 * hw * U * G));
   const int64_t spc = (steps + ch - 1) / ch;
   ch = (steps + spc - 1) / spc;
   if (wgp * ch > ((int64_t)1 << 31) - 1) { delete c; return sa_fail(DSA_ERR_UNSUPPORTED, "grid too large"); }
   c->chunks = (int)ch;
   c->spc = (int)spc;
   c->hw = hw;
+  c->T = T;
+  c->hkv = (int)hkv;
+  c->G = G;
   c->U = U;
   c->nru = (int)nru;
   c->cap = U * s->k_tokens;
   // [partial outputs][partial (max, sum)][tickets][status] then, in union
   // mode, [entries][counts]
-  const int64_t P = (int64_t)U * s->group;
-  const int64_t units = ch > 1 ? nru * s->kv_heads * ch : 0;
+  const int64_t P = (int64_t)U * G;
+  const int64_t units = ch > 1 ? nru * hkv * ch : 0;
   const int64_t floats = units * P * (D + 2);
-  const int64_t nticket = nru * s->kv_heads;
+  const int64_t nticket = nru * hkv;
   const size_t head_bytes = ((size_t)floats * 4 + (size_t)(nticket + 1) * 4 + 255) & ~(size_t)255;
   const size_t ent_bytes = U > 1 ? (size_t)nru * c->cap * 8 + (size_t)nru * 4 : 0;
   c->ws_bytes = head_bytes + ent_bytes + 256;
@@ -935,7 +952,7 @@ int sa_launch(dsa_attn_ctx* c, const uint16_t* q, const void* k_cache, const voi
   a.part_o = c->part_o; a.part_ml = c->part_ml; a.tickets = c->tickets; a.status = c->status;
   a.k_ss = s.k_slot_stride; a.k_hs = s.k_head_stride;
   a.v_ss = s.v_slot_stride; a.v_hs = s.v_head_stride; a.num_slots = s.num_slots;
-  a.rows = s.rows; a.hkv = s.kv_heads; a.G = s.group; a.K = s.k_tokens;
+  a.rows = s.rows; a.hkv = c->hkv; a.G = c->G; a.tdiv = c->T; a.K = s.k_tokens;
   a.rows_per_seq = s.rows_per_seq;
   int shift = 0;
   while ((1 << shift) < s.page_size) ++shift;
@@ -945,7 +962,7 @@ int sa_launch(dsa_attn_ctx* c, const uint16_t* q, const void* k_cache, const voi
   a.c2 = sm_scale * 1.4426950408889634f * (fp8 ? k_scale : 1.0f);
   a.vscale = fp8 ? v_scale : 1.0f;
   a.U = c->U;
-  a.P = c->U * s.group;
+  a.P = c->U * c->G;
   a.cap = c->cap;
   a.ent = c->ent;
   a.cnt = c->cnt;
@@ -959,7 +976,7 @@ int sa_launch(dsa_attn_ctx* c, const uint16_t* q, const void* k_cache, const voi
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return sa_hip(e, "launch k_union");
   }
-  const unsigned grid = (unsigned)((int64_t)c->nru * (s.kv_heads / c->hw) * c->chunks);
+  const unsigned grid = (unsigned)((int64_t)c->nru * (c->hkv / c->hw) * c->chunks);
 #define SA_GO(DD, F8, UN_) \
   hipLaunchKernelGGL((k_sparse_attn<DD, F8, UN_>), dim3(grid), dim3(NT), 0, stream, a)
   if (s.head_dim == 256) {

@@ -148,6 +148,11 @@ def test_attn_small_config_every_row():
     (128, 2, 4, 700, 0, True, True, True),
     (256, 4, 6, 200, 2, True, True, True),
     (256, 8, 8, 2048, 0, True, False, True),
+    # groups above one matrix tile: 2, 8, 3 and 5 head tiles per kv head
+    (128, 32, 1, 500, 0, True, True, True),
+    (128, 128, 1, 300, 0, True, True, True),
+    (256, 24, 2, 700, 3, True, True, True),
+    (128, 17, 2, 200, 0, True, False, True),
 ])
 def test_attn_shapes(D, G, hkv, K, chunks, paged, gate, with_lse):
     rng = np.random.default_rng(D + 7 * G + 11 * K)
@@ -285,6 +290,7 @@ def test_attn_full_size_sampled_rows(name):
 
 @pytest.mark.parametrize("D,G,hkv,K,chunks", [
     (256, 12, 2, 2048, 0), (256, 3, 1, 300, 4), (128, 16, 2, 700, 0), (128, 5, 3, 33, 1),
+    (128, 64, 1, 500, 0),
 ])
 def test_attn_fp8_caches(D, G, hkv, K, chunks):
     rng = np.random.default_rng(D + G + K)
@@ -298,7 +304,7 @@ def test_attn_fp8_caches(D, G, hkv, K, chunks):
 
 def test_attn_rejects_unsupported_shapes():
     with pytest.raises(binding.DsaError):
-        binding.SparseAttn(4, 1, 17, 256, 64, 100)           # group 17
+        binding.SparseAttn(4, 1, 0, 256, 64, 100)            # group 0
     with pytest.raises(binding.DsaError):
         binding.SparseAttn(4, 1, 4, 64, 64, 100)            # head_dim 64
     with pytest.raises(binding.DsaError):
@@ -331,6 +337,11 @@ def test_attn_union_small_config_every_row():
     (128, 2, 1, 2048, 8, 8, 64, True, True, 0.6),
     (256, 4, 2, 4096, 4, 8, 0, True, True, 0.75),
     (128, 1, 1, 2048, 16, 16, 0, True, True, 0.0),
+    # union_rows * group above 16: the group's heads in 4, 5, 3 and 2 tiles
+    (128, 16, 1, 500, 4, 4, 0, True, True, 0.75),
+    (256, 5, 1, 300, 4, 4, 2, True, True, 0.5),
+    (256, 12, 2, 400, 4, 8, 0, True, True, 0.75),
+    (128, 6, 1, 1000, 4, 4, 0, True, False, 0.75),
 ])
 def test_attn_union_shapes(D, G, hkv, K, U, rps, chunks, paged, gate, shared):
     rng = np.random.default_rng(D + 7 * G + 11 * K + U)
@@ -456,7 +467,7 @@ def test_attn_union_full_size_sampled_rows():
 
 def test_attn_union_rejects():
     with pytest.raises(binding.DsaError):
-        binding.SparseAttn(8, 1, 5, 256, 64, 100, rows_per_seq=4, union_rows=4)    # 20 pairs
+        binding.SparseAttn(34, 1, 1, 256, 64, 100, rows_per_seq=17, union_rows=17)  # 17 rows
     with pytest.raises(binding.DsaError):
         binding.SparseAttn(8, 1, 3, 256, 8193, 100, rows_per_seq=4, union_rows=4)  # 32772 ids
     with pytest.raises(binding.DsaError):
