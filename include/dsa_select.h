@@ -80,7 +80,7 @@ typedef struct dsa_ctx dsa_ctx;
 /*
  * Launch geometry chosen at init (for benchmarks and tests).  Rows longer
  * than one workgroup's share are split either per row (P workgroups each) or,
- * when rows <= min(CUs, 256), by a balanced split in which equal ranges of the
+ * when rows <= min(CUs / 2, 256), by a balanced split in which equal ranges of the
  * concatenated long rows go to the workgroups of each pass (then
  * programs_per_row is 0).
  */

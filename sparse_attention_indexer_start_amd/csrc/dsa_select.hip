@@ -242,18 +242,23 @@ int plan_ctx(const dsa_shape* s, int device, int cus, dsa_ctx* c, int64_t* words
   if (G > (int64_t)1 << 30) return fail(DSA_ERR_UNSUPPORTED, "too many rows");
   c->G = (int32_t)G;
   // Balanced split of long rows when one workgroup can scan every row's
-  // bounds (rows <= CUs and <= 256).  A pass has at most NQ + rows - 1 non-empty pieces
+  // bounds and the rows are few: rows <= CUs / 2 (and <= 256).  With more rows
+  // the owners and final workgroups leave too few workers, and the per-row
+  // split is faster (208 rows of up to 65,536 strided columns: 48.9 us
+  // against 51.6; a 96-row decode batch keeps the balanced kernel, whose
+  // short-row path also emits the token ids in closed form: 9.6 us against
+  // 10.4).  A pass has at most NQ + rows - 1 non-empty pieces
   // (one per worker plus one per row boundary inside a worker's range);
   // with the rows' owners that is one resident round at two workgroups per
   // CU when NQ = 2 * CUs - rows + 1, less a reserve of slots for the rows'
   // final workgroups, which run while the pass-2 pieces still store -inf.
   // (Without it a 32-row decode batch of 1M-wide rows took 83 us instead of
-  // 62; on a 208-row batch a reserve of 64 measured faster than 32, 48, 80,
-  // 96, 128 or every row.)
+  // 62; a 208-row batch on the balanced split ran fastest with 64, against
+  // 32, 48, 80, 96, 128 or every row.)
   const int64_t reserve = std::min<int64_t>(s->rows, 64);
   c->NQ = (int32_t)std::max<int64_t>(
       1, std::min<int64_t>((int64_t)cus * 2 - s->rows + 1 - reserve, NT));
-  c->balanced = (s->rows >= 1 && s->rows <= cus && s->rows <= 256) ? 1 : 0;
+  c->balanced = (s->rows >= 1 && s->rows <= cus / 2 && s->rows <= 256) ? 1 : 0;
   c->cnt_stride = std::max(c->P, c->NQ);
   const int64_t F = (s->k_tokens + s->block_size - 1) / s->block_size;
   // Token domain of a row: at most nlow + Kp <= 2*K_blk + F blocks (also
