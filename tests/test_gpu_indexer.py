@@ -150,6 +150,49 @@ def test_indexer_prefill_config_sampled_rows():
     _check(case, rows=rows, with_logits=False)
 
 
+@pytest.mark.parametrize("kb,kt", [(32, 256), (64, 100)], ids=["closed_form", "recompute"])
+def test_indexer_graph_replay_with_new_ends(kb, kt):
+    """A captured indexer call replayed with new ends (the launch shape is
+    fixed by the shape; trip counts follow the ends on the device): every
+    replay equals the oracle on the new bounds, and five replays of the same
+    ends agree bit for bit."""
+    import dataclasses
+    import torch
+    S = 6000
+    case = wl.make_indexer_custom(8, S, 64, 128, 8, kb, kt, [S] * 8, seed=15 + kb)
+    q8, k8, w, ks, st, en = _to_dev(case)
+    bids = torch.empty((case.queries, kb), dtype=torch.int32, device="cuda")
+    tids = torch.empty((case.queries, kt), dtype=torch.int32, device="cuda")
+    call = lambda: binding.indexer_select(q8, k8, w, ks, st, en, case.block_size, kb, kt,
+                                          block_ids=bids, token_ids=tids)
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for new in ([S, 1, 4097, 0, 2500, 17, S - 1, 3000], [9, 9, 9, 9, S, S, 100, 101]):
+        ends = np.asarray(new, np.int32)
+        en.copy_(torch.from_numpy(ends))
+        outs = []
+        for _ in range(5):
+            bids.fill_(-7)
+            tids.fill_(-7)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            outs.append((bids.cpu().numpy(), tids.cpu().numpy()))
+        for b, t in outs[1:]:
+            assert np.array_equal(b, outs[0][0]) and np.array_equal(t, outs[0][1])
+        c2 = dataclasses.replace(case, ends=ends)
+        wb, wt, _ = io.indexer_select(c2.q8, c2.k8, c2.w, c2.kscale, c2.starts, c2.ends,
+                                      c2.block_size, kb, kt, c2.starts_repeat, c2.ends_repeat,
+                                      return_logits=True)
+        assert np.array_equal(outs[0][0], wb), f"block ids differ for ends {new}"
+        assert np.array_equal(outs[0][1], wt), f"token ids differ for ends {new}"
+    gh.log(f"  indexer graph: replays with new ends bit-exact (kb={kb}, kt={kt})")
+
+
 def test_indexer_rejects_unsupported_shapes():
     import torch
     case = wl.make_indexer_custom(2, 100, 64, 128, 8, 4, 16, [100, 50], seed=1)
