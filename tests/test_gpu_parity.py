@@ -77,6 +77,43 @@ def test_fused_fuzz(seed):
     _full_check(dc, bids, tids, scores)
 
 
+def _long_fuzz_case(seed):
+    rng = np.random.default_rng(5000 + seed)
+    R = int(rng.choice([1, 2, 5, 17, 40, 130, 300]))
+    B = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    W = int(rng.integers(20000, 400000 if R <= 40 else 60000))
+    nb = -(-W // B)
+    kb = int(rng.choice([1, 5, 64, 300, 2048, min(nb, 8000)]))
+    kt = int(rng.choice([1, 100, 2048, 5000]))
+    kb = min(kb, 65536 - kt)
+    cs = int(rng.choice([1, 2]))
+    ends = rng.integers(0, W + 100, size=R)
+    ends[rng.random(R) < 0.25] = W
+    starts = rng.integers(0, W // 3, size=R) if rng.random() < 0.5 else None
+    return wl.make_custom(R, W, B, kb, kt, ends, starts=starts, col_stride=cs, seed=seed,
+                          dup_frac=0.02, outlier_frac=0.01)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_fused_long_fuzz(seed):
+    """Random shapes with long rows: 1 to 300 rows (balanced and per-row
+    splits), widths up to 400,000, block sizes 1 to 32, K from 1 to 8000,
+    strided views and starts, in one launch or two."""
+    case = _long_fuzz_case(seed)
+    sh = case.shape
+    two = bool(seed % 3 == 2)
+    gh.log(f"long fuzz seed={seed} R={sh.rows} W={sh.width} B={sh.block_size} kb={sh.k_blocks} "
+           f"kt={sh.k_tokens} cs={sh.col_stride} starts={'yes' if case.starts is not None else 'no'} "
+           f"two_launches={two}")
+    dc = gh.DevCase(case)
+    bids, tids, scores = dc.run_fused(two_launches=two)
+    rows = range(min(sh.rows, 8))
+    gh.check_rows_against_oracle(dc, rows, bids, tids, scores)
+    gh.check_all_rows_c(dc, bids, tids, scores)
+    gh.check_whole_buffer(dc)
+    gh.check_invariants_all_rows(dc, bids, tids)
+
+
 @pytest.mark.parametrize("two", [False, True], ids=["one_launch", "two_launches"])
 @pytest.mark.parametrize("B,W,ends,kb,kt", [
     (8, 65536, [65536, 40000, 16385], 16, 100),
