@@ -465,6 +465,35 @@ def test_attn_union_full_size_sampled_rows():
     torch.cuda.empty_cache()
 
 
+def _attn_fuzz_case(seed):
+    rng = np.random.default_rng(9000 + seed)
+    D = int(rng.choice([128, 256]))
+    hkv = int(rng.choice([1, 2, 3, 4]))
+    G = int(rng.choice([1, 2, 3, 5, 8, 12, 16, 20, 24, 32, 40]))
+    U = int(rng.choice([0, 0, 2, 3, 4, 8]))
+    rps = max(U, 1) * int(rng.choice([1, 2]))
+    K = int(rng.integers(1, 1500))
+    chunks = int(rng.choice([0, 0, 1, 2, 5]))
+    lens = rng.integers(1, 3 * K + 40, size=int(rng.integers(1, 4)))
+    case = wl.make_attn_custom(lens, rps, hkv, G, D, K, page_size=int(rng.choice([16, 64])),
+                               paged=bool(rng.random() < 0.8), with_gate=bool(rng.random() < 0.7),
+                               seed=seed, q_scale=2.0, kv_fp8=bool(rng.random() < 0.3),
+                               shared=float(rng.choice([0.0, 0.5, 0.75])))
+    return case, U, chunks
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_attn_fuzz(seed):
+    """Random shapes: head_dim, kv heads, 1-40 query heads per kv head (head
+    tiles), per-row or union mode with 2-8 rows per group, 1-1500 ids,
+    chunk counts, paged or flat, bf16 or fp8 caches, gate on or off."""
+    case, U, chunks = _attn_fuzz_case(seed)
+    gate = case.gate is not None
+    got, lse, status = _run(case, chunks=chunks, with_gate=gate, union_rows=U)
+    assert status == 0
+    _check(case, got, lse, with_gate=gate, distinct=U > 1)
+
+
 def test_attn_union_rejects():
     with pytest.raises(binding.DsaError):
         binding.SparseAttn(34, 1, 1, 256, 64, 100, rows_per_seq=17, union_rows=17)  # 17 rows
