@@ -150,6 +150,34 @@ def test_indexer_prefill_config_sampled_rows():
     _check(case, rows=rows, with_logits=False)
 
 
+def _indexer_fuzz_case(seed):
+    rng = np.random.default_rng(7000 + seed)
+    Q = int(rng.choice([1, 3, 8, 13]))
+    S = int(rng.integers(1, 20000))
+    H = int(rng.choice([16, 32, 64]))
+    B = int(rng.choice([1, 2, 4, 8, 16]))
+    kb = int(rng.integers(1, 513))
+    kt = int(rng.integers(1, 513)) if kb * B > 512 else int(rng.integers(1, 4097))
+    sr = int(rng.choice([1, 1, 2]))
+    er = int(rng.choice([1, 1, 2]))
+    ends = rng.integers(0, S + 30, size=-(-Q // er))
+    starts = rng.integers(0, max(1, S // 2), size=-(-Q // sr)) if rng.random() < 0.6 else None
+    return wl.make_indexer_custom(Q, S, H, 128, B, kb, kt, ends, starts=starts, seed=seed,
+                                  with_kscale=bool(rng.random() < 0.8), starts_repeat=sr,
+                                  ends_repeat=er)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_indexer_fuzz(seed):
+    """Random shapes: 1-13 queries, up to 20,000 keys, 16/32/64 heads, block
+    sizes 1-16, K_blk up to 512 (both forms), both token routes, starts,
+    repeats, with and without key scales; every row bit for bit."""
+    case = _indexer_fuzz_case(seed)
+    gh.log(f"indexer fuzz seed={seed} Q={case.queries} S={case.keys} B={case.block_size} "
+           f"kb={case.k_blocks} kt={case.k_tokens}")
+    _check(case)
+
+
 @pytest.mark.parametrize("kb,kt", [(32, 256), (64, 100)], ids=["closed_form", "recompute"])
 def test_indexer_graph_replay_with_new_ends(kb, kt):
     """A captured indexer call replayed with new ends (the launch shape is
