@@ -80,6 +80,24 @@ def test_row_topk_small_fuzz(seed):
     _check_case(case, k)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_row_topk_long_fuzz(seed):
+    """Random long rows: 1-4 rows of up to 4M columns, K from 1 to 2^20
+    (list mode, its overflow fallback and rows read four times), strided
+    views, starts, ties and outliers."""
+    rng = np.random.default_rng(800 + seed)
+    R = int(rng.integers(1, 5))
+    W = int(rng.integers(100000, 4 * 2**20))
+    k = int(rng.choice([1, 64, 2048, 30000, 2**20]))
+    cs = int(rng.choice([1, 1, 2]))
+    ends = rng.integers(W // 2, W + 30, size=R)
+    starts = rng.integers(0, W // 4, size=R) if rng.random() < 0.5 else None
+    case = wl.make_custom(R, W, 8, 1, 1, ends, starts=starts, col_stride=cs, seed=seed,
+                          dup_frac=0.05, outlier_frac=0.001)
+    gh.log(f"row top-k long fuzz seed={seed} R={R} W={W} k={k} cs={cs}")
+    _check_case(case, k)
+
+
 def test_row_topk_special_values_and_ties():
     W = 30000
     case = wl.make_custom(3, W, 8, 1, 1, [W, W - 1, 12345], seed=3, dup_frac=0.3)
