@@ -113,6 +113,15 @@ int dsa_select_destroy(dsa_ctx* ctx);
 int dsa_select_query(const dsa_ctx* ctx, dsa_launch_info* info);
 
 /*
+ * dsa_select_plan -- the launch geometry and workspace size that
+ * dsa_select_init would choose for `shape` on a device with `cus` compute
+ * units, computed on the host without touching any device (for sizing a
+ * workspace ahead of time and for host-side tests).  The shape is validated
+ * as dsa_select_init validates it.  Returns DSA_OK or a negative dsa_status.
+ */
+int dsa_select_plan(const dsa_shape* shape, int cus, dsa_launch_info* info);
+
+/*
  * dsa_block_scores -- [P1] Summary (block scoring over the row's range, the
  * newest-block pin).  For every row and every live block b < nlb:
  *   scores[r * nblocks + b] = the block's live value with the largest key,

@@ -27,7 +27,8 @@ STATUS_NAMES = {
 
 # Every entry point that include/dsa_select.h declares.
 EXPORTED = (
-    "dsa_select_init", "dsa_select_destroy", "dsa_select_query", "dsa_block_scores",
+    "dsa_select_init", "dsa_select_destroy", "dsa_select_query", "dsa_select_plan",
+    "dsa_block_scores",
     "dsa_topk", "dsa_candidate_mask", "dsa_select_fused", "dsa_read_status",
     "dsa_reset_workspace", "dsa_last_error", "dsa_select_fused_noalloc",
     "dsa_indexer_select", "dsa_indexer_last_error",
@@ -117,6 +118,7 @@ def load() -> ctypes.CDLL:
         lib.dsa_select_init.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(vp)]
         lib.dsa_select_destroy.argtypes = [vp]
         lib.dsa_select_query.argtypes = [vp, ctypes.POINTER(LaunchInfo)]
+        lib.dsa_select_plan.argtypes = [ctypes.POINTER(Shape), i32, ctypes.POINTER(LaunchInfo)]
         lib.dsa_block_scores.argtypes = [vp, vp, vp, vp, vp, vp]
         lib.dsa_topk.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp]
         lib.dsa_candidate_mask.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -158,6 +160,19 @@ def _check(rc: int) -> None:
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def plan(rows: int, width: int, block_size: int, k_blocks: int, k_tokens: int, cus: int,
+         row_stride: Optional[int] = None, col_stride: int = 1, starts_repeat: int = 1,
+         ends_repeat: int = 1) -> LaunchInfo:
+    """Launch geometry and workspace size of a shape on a device with ``cus``
+    compute units (dsa_select_plan: host only, no device needed)."""
+    shape = Shape(rows, block_size, k_blocks, k_tokens, width,
+                  max(1, width * col_stride) if row_stride is None else row_stride,
+                  col_stride, starts_repeat, ends_repeat)
+    li = LaunchInfo()
+    _check(load().dsa_select_plan(ctypes.byref(shape), cus, ctypes.byref(li)))
+    return li
 
 
 class Context:

@@ -402,10 +402,8 @@ int dsa_select_destroy(dsa_ctx* c) {
   return rc;
 }
 
-int dsa_select_query(const dsa_ctx* c, dsa_launch_info* info) {
-  int rc = check_ctx(c);
-  if (rc != DSA_OK) return rc;
-  if (!info) return fail(DSA_ERR_INVALID_ARG, "info is null");
+namespace {
+void fill_info(const dsa_ctx* c, dsa_launch_info* info) {
   const bool split = may_split(c) && c->balanced;
   info->programs_per_row = split ? 0 : c->P;
   info->threads_per_group = NT;
@@ -413,6 +411,27 @@ int dsa_select_query(const dsa_ctx* c, dsa_launch_info* info) {
   info->small_row_blocks = c->small_blocks;
   info->workspace_bytes = (int64_t)c->ws_bytes;
   info->fused_launches = 1;
+}
+}  // namespace
+
+int dsa_select_query(const dsa_ctx* c, dsa_launch_info* info) {
+  int rc = check_ctx(c);
+  if (rc != DSA_OK) return rc;
+  if (!info) return fail(DSA_ERR_INVALID_ARG, "info is null");
+  fill_info(c, info);
+  return DSA_OK;
+}
+
+int dsa_select_plan(const dsa_shape* s, int cus, dsa_launch_info* info) {
+  if (!info) return fail(DSA_ERR_INVALID_ARG, "info is null");
+  if (cus < 1) return fail(DSA_ERR_INVALID_ARG, "cus must be >= 1 (got %d)", cus);
+  int rc = validate_shape(s, 0);
+  if (rc != DSA_OK) return rc;
+  dsa_ctx c;
+  int64_t words[N_SLOTS];
+  rc = plan_ctx(s, 0, cus, &c, words);
+  if (rc != DSA_OK) return rc;
+  fill_info(&c, info);
   return DSA_OK;
 }
 

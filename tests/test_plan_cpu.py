@@ -1,0 +1,84 @@
+"""Launch planning of the selection library on the host (no GPU needed).
+
+dsa_select_plan returns the geometry dsa_select_init would choose for a
+shape on a device with a given CU count.  The expected values follow the
+rules the library documents for its launch shape: P workgroups per row
+(about two workgroups per CU over all rows, at most one per 256 blocks and
+512), the balanced split for batches of at most CUs / 2 rows (at most 256),
+its worker count NQ = 2 * CUs - rows + 1 - min(rows, 64), and one launch of
+fixed size whatever the rows' ends (rows of at most 4096 blocks and 16384
+columns never split).
+"""
+import ctypes
+import math
+
+import pytest
+
+from sparse_attention_indexer_start_amd import binding
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def _expected(rows, width, B, cus):
+    nb = math.ceil(width / B)
+    P = max(1, min(math.ceil(2 * cus / rows), max(1, math.ceil(nb / 256)), 512))
+    G = P * rows
+    NQ = max(1, min(2 * cus - rows + 1 - min(rows, 64), 512))
+    balanced = 1 <= rows <= cus // 2 and rows <= 256
+    may_split = nb > 4096 or (width > 16384 and (P > 1 or balanced))
+    if not may_split:
+        return P, G
+    if balanced:
+        return 0, 2 * rows + 2 * (NQ + rows - 1)
+    return P, 2 * G + rows
+
+
+@pytest.mark.parametrize("name,rows,width,B,kb,kt,cs", [
+    ("tiny", 4, 4096, 8, 64, 256, 1),
+    ("short_decode", 96, 1 << 20, 8, 256, 2048, 1),
+    ("mtp_ragged", 208, 131072, 16, 128, 2048, 2),
+    ("long_decode", 32, 1 << 20, 8, 2048, 2048, 1),
+    ("prefill_chunk", 8192, 131072, 8, 256, 2048, 1),
+    ("short_at_8192", 96, 8192, 8, 256, 2048, 1),
+])
+@pytest.mark.parametrize("cus", [256, 128, 80])
+def test_plan_matches_the_documented_launch_rules(lib, name, rows, width, B, kb, kt, cs, cus):
+    info = binding.plan(rows, width, B, kb, kt, cus, col_stride=cs)
+    ppr, grid = _expected(rows, width, B, cus)
+    assert (info.programs_per_row, info.grid_groups) == (ppr, grid), name
+    assert info.threads_per_group == 512
+    assert info.small_row_blocks == 4096
+    assert info.fused_launches == 1
+    assert info.workspace_bytes > 0
+
+
+def test_plan_split_choice_on_the_measured_batches():
+    """On 256 CUs the 96-row decode batch and the 32-row long batch take the
+    balanced split, the 208-row MTP batch and the prefill chunk the per-row
+    split (three and one workgroups per row)."""
+    assert binding.plan(96, 1 << 20, 8, 256, 2048, 256).programs_per_row == 0
+    assert binding.plan(32, 1 << 20, 8, 2048, 2048, 256).programs_per_row == 0
+    assert binding.plan(208, 131072, 16, 128, 2048, 256, col_stride=2).programs_per_row == 3
+    assert binding.plan(8192, 131072, 8, 256, 2048, 256).programs_per_row == 1
+
+
+def test_plan_workspace_grows_with_the_width():
+    """The workspace holds per-row key, list and candidate regions sized by
+    the width; a wider buffer never needs less."""
+    a = binding.plan(32, 1 << 18, 8, 2048, 2048, 256).workspace_bytes
+    b = binding.plan(32, 1 << 20, 8, 2048, 2048, 256).workspace_bytes
+    assert b > a
+
+
+def test_plan_rejects_bad_input(lib):
+    li = binding.LaunchInfo()
+    sh = binding.Shape(4, 8, 64, 256, 4096, 4096, 1, 1, 1)
+    assert lib.dsa_select_plan(ctypes.byref(sh), 0, ctypes.byref(li)) == -1
+    assert lib.dsa_select_plan(ctypes.byref(sh), 256, None) == -1
+    assert lib.dsa_select_plan(None, 256, ctypes.byref(li)) == -1
+    bad = binding.Shape(4, 0, 64, 256, 4096, 4096, 1, 1, 1)          # block_size 0
+    assert lib.dsa_select_plan(ctypes.byref(bad), 256, ctypes.byref(li)) == -1
+    assert lib.dsa_last_error()
