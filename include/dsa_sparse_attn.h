@@ -89,7 +89,7 @@ typedef struct dsa_attn_shape {
   int64_t num_slots;      /* cache slots, < 2^31 */
   int64_t k_slot_stride, k_head_stride;   /* elements */
   int64_t v_slot_stride, v_head_stride;   /* elements */
-  int32_t chunks;         /* workgroups per (row or union group, head tile); 0 = chosen at init */
+  int32_t chunks;         /* workgroups per (row or union group, workgroup's head tiles); 0 = chosen at init */
   int32_t union_rows;     /* 0 or 1: each row on its own; >= 2: union mode (see above) */
 } dsa_attn_shape;
 
@@ -103,8 +103,22 @@ int dsa_sparse_attn_init(const dsa_attn_shape* shape, int device, dsa_attn_ctx**
 /* Frees the workspace (after the device finished using it). */
 int dsa_sparse_attn_destroy(dsa_attn_ctx* ctx);
 
-/* Chunks per (row, head tile), or per (union group, head tile) in union
- * mode, chosen at init (> 0), or a negative dsa_status. */
+/* The launch plan of a shape on a device with `cus` compute units, computed
+ * on the host without touching any device (the same validation and choices
+ * as dsa_sparse_attn_init; for sizing ahead of time and for host-side tests).
+ * Returns DSA_OK or a negative dsa_status. */
+typedef struct dsa_attn_plan_info {
+  int32_t head_tiles;       /* T: equal parts of each kv head's group (see Head tiles) */
+  int32_t heads_per_tile;   /* group / T */
+  int32_t tiles_per_group;  /* head tiles per workgroup: 1, 2 or 4 */
+  int32_t chunks;           /* workgroups per (row or union group, workgroup's tiles) */
+  int32_t grid_groups;      /* workgroups of the attention launch */
+  int64_t workspace_bytes;
+} dsa_attn_plan_info;
+int dsa_sparse_attn_plan(const dsa_attn_shape* shape, int cus, dsa_attn_plan_info* info);
+
+/* Chunks per (row, workgroup's head tiles), or per (union group, workgroup's
+ * head tiles) in union mode, chosen at init (> 0), or a negative dsa_status. */
 int dsa_sparse_attn_chunks(const dsa_attn_ctx* ctx);
 
 int dsa_sparse_attn(dsa_attn_ctx* ctx, const uint16_t* q, const uint16_t* k_cache,

@@ -34,7 +34,8 @@ EXPORTED = (
     "dsa_indexer_select", "dsa_indexer_last_error",
     "dsa_row_topk_init", "dsa_row_topk_destroy", "dsa_row_topk_pieces", "dsa_row_topk",
     "dsa_row_topk_last_error",
-    "dsa_sparse_attn_init", "dsa_sparse_attn_destroy", "dsa_sparse_attn_chunks",
+    "dsa_sparse_attn_init", "dsa_sparse_attn_plan", "dsa_sparse_attn_destroy",
+    "dsa_sparse_attn_chunks",
     "dsa_sparse_attn", "dsa_sparse_attn_fp8", "dsa_sparse_attn_read_status",
     "dsa_sparse_attn_reset_status",
     "dsa_sparse_attn_last_error",
@@ -95,6 +96,14 @@ class AttnShape(ctypes.Structure):
     ]
 
 
+class AttnPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("head_tiles", ctypes.c_int32), ("heads_per_tile", ctypes.c_int32),
+        ("tiles_per_group", ctypes.c_int32), ("chunks", ctypes.c_int32),
+        ("grid_groups", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
 _lib = None
 _lock = threading.Lock()
 
@@ -136,6 +145,8 @@ def load() -> ctypes.CDLL:
         lib.dsa_row_topk.argtypes = [vp, vp, vp, vp, vp, vp]
         lib.dsa_row_topk_last_error.restype = ctypes.c_char_p
         lib.dsa_sparse_attn_init.argtypes = [ctypes.POINTER(AttnShape), i32, ctypes.POINTER(vp)]
+        lib.dsa_sparse_attn_plan.argtypes = [ctypes.POINTER(AttnShape), i32,
+                                             ctypes.POINTER(AttnPlanInfo)]
         lib.dsa_sparse_attn_destroy.argtypes = [vp]
         lib.dsa_sparse_attn_chunks.argtypes = [vp]
         lib.dsa_sparse_attn.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
@@ -493,6 +504,21 @@ class RowTopk:
             self.close()
         except Exception:
             pass
+
+
+def attn_plan(rows: int, kv_heads: int, group: int, head_dim: int, k_tokens: int, cus: int,
+              num_slots: int = 1, rows_per_seq: int = 1, chunks: int = 0,
+              union_rows: int = 0) -> AttnPlanInfo:
+    """Launch plan of a sparse-attention shape on a device with ``cus`` compute
+    units (dsa_sparse_attn_plan: host only, contiguous caches assumed)."""
+    shape = AttnShape(rows, kv_heads, group, head_dim, k_tokens, rows_per_seq, 1, 0, num_slots,
+                      kv_heads * head_dim, head_dim, kv_heads * head_dim, head_dim, chunks,
+                      union_rows)
+    li = AttnPlanInfo()
+    rc = load().dsa_sparse_attn_plan(ctypes.byref(shape), cus, ctypes.byref(li))
+    if rc != 0:
+        raise DsaError(rc, load().dsa_sparse_attn_last_error().decode(errors="replace"))
+    return li
 
 
 class SparseAttn:

@@ -736,7 +736,7 @@ struct dsa_attn_ctx {
   int T, hkv, G;        // head tiles per kv head, head tiles in all, query heads per tile
   int U, nru, cap;      // rows per union group (1 outside union mode), groups or rows, U * K
   void* ws;
-  size_t ws_bytes;
+  size_t ws_bytes, head_bytes;   // workspace, and its part before the union entries
   float *part_o, *part_ml;
   uint32_t *tickets, *status;
   int2* ent;            // union mode: [nru][cap]
@@ -787,9 +787,14 @@ extern "C" {
 
 const char* dsa_sparse_attn_last_error(void) { return g_sa_err.c_str(); }
 
-int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out) {
-  if (!out) return sa_fail(DSA_ERR_INVALID_ARG, "out is null");
-  *out = nullptr;
+}  // extern "C"
+
+namespace {
+
+// Validates a shape (everything but the device) and plans its launch on a
+// device with `cus` CUs into c: head tiles, tiles per workgroup, chunks and
+// the workspace size.  No device call.
+int attn_plan(const dsa_attn_shape* s, int cus, dsa_attn_ctx* c) {
   if (!s) return sa_fail(DSA_ERR_INVALID_ARG, "shape is null");
   if (s->rows < 0) return sa_fail(DSA_ERR_INVALID_ARG, "rows must be >= 0");
   if (s->kv_heads < 1) return sa_fail(DSA_ERR_INVALID_ARG, "kv_heads must be >= 1");
@@ -814,6 +819,7 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
     return sa_fail(DSA_ERR_INVALID_ARG, "cache strides overlap heads or slots");
   if (s->chunks < 0) return sa_fail(DSA_ERR_INVALID_ARG, "chunks must be >= 0");
   if (s->union_rows < 0) return sa_fail(DSA_ERR_INVALID_ARG, "union_rows must be >= 0");
+  if (cus < 1) return sa_fail(DSA_ERR_INVALID_ARG, "cus must be >= 1");
   const int U = std::max(1, s->union_rows);
   if (U > 1) {
     if (U > GMAX)
@@ -832,19 +838,6 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   const int64_t hkv = (int64_t)s->kv_heads * T;
   const int64_t pairs = (int64_t)s->rows * hkv;
   if (pairs > ((int64_t)1 << 30)) return sa_fail(DSA_ERR_UNSUPPORTED, "too many rows or heads");
-  if (device < 0) return sa_fail(DSA_ERR_INVALID_ARG, "device must be >= 0");
-  DeviceScope ds(device);
-  if (ds.e != hipSuccess) return sa_hip(ds.e, "hipSetDevice");
-  int cus = 0;
-  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
-  if (e != hipSuccess) return sa_hip(e, "hipDeviceGetAttribute(CU count)");
-
-  dsa_attn_ctx* c = new (std::nothrow) dsa_attn_ctx;
-  if (!c) return sa_fail(DSA_ERR_HIP, "host allocation failed");
-  std::memset(c, 0, sizeof(*c));
-  c->sh = *s;
-  c->device = device;
-  c->magic = SA_MAGIC;
   // Head tiles per workgroup (the tiles of one kv head are neighbours, so a
   // workgroup's waves read the same cache rows), and chunks per (row or union
   // group, group of head tiles): enough workgroups for two per CU, each chunk
@@ -865,7 +858,9 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   ch = std::min<int64_t>(ch, (int64_t)WAVES * GMAX * D * 4 / (8 * hw * U * G));
   const int64_t spc = (steps + ch - 1) / ch;
   ch = (steps + spc - 1) / spc;
-  if (wgp * ch > ((int64_t)1 << 31) - 1) { delete c; return sa_fail(DSA_ERR_UNSUPPORTED, "grid too large"); }
+  if (wgp * ch > ((int64_t)1 << 31) - 1) return sa_fail(DSA_ERR_UNSUPPORTED, "grid too large");
+  std::memset(c, 0, sizeof(*c));
+  c->sh = *s;
   c->chunks = (int)ch;
   c->spc = (int)spc;
   c->hw = hw;
@@ -881,9 +876,56 @@ int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out
   const int64_t units = ch > 1 ? nru * hkv * ch : 0;
   const int64_t floats = units * P * (D + 2);
   const int64_t nticket = nru * hkv;
-  const size_t head_bytes = ((size_t)floats * 4 + (size_t)(nticket + 1) * 4 + 255) & ~(size_t)255;
+  c->head_bytes = ((size_t)floats * 4 + (size_t)(nticket + 1) * 4 + 255) & ~(size_t)255;
   const size_t ent_bytes = U > 1 ? (size_t)nru * c->cap * 8 + (size_t)nru * 4 : 0;
-  c->ws_bytes = head_bytes + ent_bytes + 256;
+  c->ws_bytes = c->head_bytes + ent_bytes + 256;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_sparse_attn_plan(const dsa_attn_shape* s, int cus, dsa_attn_plan_info* info) {
+  if (!info) return sa_fail(DSA_ERR_INVALID_ARG, "info is null");
+  dsa_attn_ctx c;
+  const int rc = attn_plan(s, cus, &c);
+  if (rc != DSA_OK) return rc;
+  info->head_tiles = c.T;
+  info->heads_per_tile = c.G;
+  info->tiles_per_group = c.hw;
+  info->chunks = c.chunks;
+  info->grid_groups = (int32_t)((int64_t)c.nru * (c.hkv / c.hw) * c.chunks);
+  info->workspace_bytes = (int64_t)c.ws_bytes;
+  return DSA_OK;
+}
+
+int dsa_sparse_attn_init(const dsa_attn_shape* s, int device, dsa_attn_ctx** out) {
+  if (!out) return sa_fail(DSA_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  {
+    dsa_attn_ctx check;   // the shape is validated before any device call
+    const int rc = attn_plan(s, 1, &check);
+    if (rc != DSA_OK) return rc;
+  }
+  if (device < 0) return sa_fail(DSA_ERR_INVALID_ARG, "device must be >= 0");
+  DeviceScope ds(device);
+  if (ds.e != hipSuccess) return sa_hip(ds.e, "hipSetDevice");
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return sa_hip(e, "hipDeviceGetAttribute(CU count)");
+  dsa_attn_ctx* c = new (std::nothrow) dsa_attn_ctx;
+  if (!c) return sa_fail(DSA_ERR_HIP, "host allocation failed");
+  const int rc = attn_plan(s, cus, c);
+  if (rc != DSA_OK) { delete c; return rc; }
+  c->device = device;
+  c->magic = SA_MAGIC;
+  const size_t head_bytes = c->head_bytes;
+  const int64_t D = s->head_dim, P = (int64_t)c->U * c->G;
+  const int64_t units = c->chunks > 1 ? (int64_t)c->nru * c->hkv * c->chunks : 0;
+  const int64_t nticket = (int64_t)c->nru * c->hkv;
+  const int U = c->U;
+  const int64_t nru = c->nru;
   e = hipMalloc(&c->ws, c->ws_bytes);
   if (e != hipSuccess) { delete c; return sa_hip(e, "hipMalloc(workspace)"); }
   e = hipMemset(c->ws, 0, c->ws_bytes);

@@ -82,3 +82,57 @@ def test_plan_rejects_bad_input(lib):
     bad = binding.Shape(4, 0, 64, 256, 4096, 4096, 1, 1, 1)          # block_size 0
     assert lib.dsa_select_plan(ctypes.byref(bad), 256, ctypes.byref(li)) == -1
     assert lib.dsa_last_error()
+
+
+# ---------------------------------------------------------------------------
+# Sparse attention: head tiles, workgroups and chunks
+# ---------------------------------------------------------------------------
+
+def _attn_expected(rows, hkv, G, D, K, U, cus):
+    """The documented plan: T = the smallest divisor of G with max(U, 1) * G / T
+    <= 16; up to four neighbouring head tiles per workgroup; chunks for two
+    workgroups per CU, at most one 32-token step per wave and within the
+    merge's LDS staging; the chunk count then trimmed to whole steps."""
+    Ue = max(U, 1)
+    T = next(t for t in range(1, G + 1) if G % t == 0 and Ue * (G // t) <= 16)
+    Gt, tiles = G // T, hkv * T
+    hw = 4 if tiles % 4 == 0 else 2 if tiles % 2 == 0 else 1
+    nru = -(-rows // Ue)
+    wgp = nru * (tiles // hw)
+    steps = -(-K // 32)
+    ch = max(1, min(-(-2 * cus // max(wgp, 1)), max(1, steps // (4 // hw))))
+    ch = min(ch, 4 * 16 * D * 4 // (8 * hw * Ue * Gt))
+    spc = -(-steps // ch)
+    ch = -(-steps // spc)
+    return T, Gt, hw, ch, wgp * ch
+
+
+@pytest.mark.parametrize("rows,hkv,G,D,K,U", [
+    (512, 2, 12, 256, 2048, 0),     # the bf16 decode batch
+    (4, 1, 3, 256, 2048, 0),        # one request
+    (512, 1, 3, 256, 2048, 4),      # union mode, 4 rows of 3 heads per tile
+    (64, 1, 128, 128, 2048, 0),     # 128 heads: 8 tiles of 16
+    (64, 1, 16, 128, 500, 4),       # union mode, 4 tiles of 4 heads
+    (8, 2, 17, 128, 300, 0),        # a prime group: 17 tiles of one head
+    (24, 3, 40, 128, 275, 4),       # 10 tiles of 4 heads
+    (48, 3, 20, 128, 12, 8),        # 10 tiles of 2 heads, one step per row
+])
+@pytest.mark.parametrize("cus", [256, 80])
+def test_attn_plan_matches_the_documented_rules(rows, hkv, G, D, K, U, cus):
+    info = binding.attn_plan(rows, hkv, G, D, K, cus, rows_per_seq=max(U, 1), union_rows=U)
+    T, Gt, hw, ch, grid = _attn_expected(rows, hkv, G, D, K, U, cus)
+    assert (info.head_tiles, info.heads_per_tile, info.tiles_per_group) == (T, Gt, hw)
+    assert (info.chunks, info.grid_groups) == (ch, grid)
+    assert max(U, 1) * info.heads_per_tile <= 16
+    assert info.workspace_bytes > 0
+
+
+def test_attn_plan_rejects_bad_shapes():
+    with pytest.raises(binding.DsaError):
+        binding.attn_plan(4, 1, 0, 256, 64, 256)                            # group 0
+    with pytest.raises(binding.DsaError):
+        binding.attn_plan(34, 1, 1, 256, 64, 256, rows_per_seq=17, union_rows=17)
+    with pytest.raises(binding.DsaError):
+        binding.attn_plan(4, 1, 4, 64, 64, 256)                             # head_dim 64
+    with pytest.raises(binding.DsaError):
+        binding.attn_plan(4, 1, 4, 256, 64, 0)                              # no CUs
