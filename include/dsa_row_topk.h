@@ -68,6 +68,13 @@ int dsa_row_topk_destroy(dsa_topk_ctx* ctx);
 /* Pieces per row chosen at init (> 0), or a negative dsa_status. */
 int dsa_row_topk_pieces(const dsa_topk_ctx* ctx);
 
+/* The pieces per row and workspace size dsa_row_topk_init would choose for
+ * `shape` on a device with `cus` compute units, computed on the host without
+ * touching any device (same validation).  Either output may be NULL.
+ * Returns DSA_OK or a negative dsa_status. */
+int dsa_row_topk_plan(const dsa_topk_shape* shape, int cus, int32_t* pieces,
+                      int64_t* workspace_bytes);
+
 int dsa_row_topk(dsa_topk_ctx* ctx, const float* logits, const int32_t* starts,
                  const int32_t* ends, int32_t* out, hipStream_t stream);
 

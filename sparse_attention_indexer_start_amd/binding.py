@@ -32,7 +32,8 @@ EXPORTED = (
     "dsa_topk", "dsa_candidate_mask", "dsa_select_fused", "dsa_read_status",
     "dsa_reset_workspace", "dsa_last_error", "dsa_select_fused_noalloc",
     "dsa_indexer_select", "dsa_indexer_last_error",
-    "dsa_row_topk_init", "dsa_row_topk_destroy", "dsa_row_topk_pieces", "dsa_row_topk",
+    "dsa_row_topk_init", "dsa_row_topk_plan", "dsa_row_topk_destroy", "dsa_row_topk_pieces",
+    "dsa_row_topk",
     "dsa_row_topk_last_error",
     "dsa_sparse_attn_init", "dsa_sparse_attn_plan", "dsa_sparse_attn_destroy",
     "dsa_sparse_attn_chunks",
@@ -142,6 +143,9 @@ def load() -> ctypes.CDLL:
         lib.dsa_row_topk_init.argtypes = [ctypes.POINTER(TopkShape), i32, ctypes.POINTER(vp)]
         lib.dsa_row_topk_destroy.argtypes = [vp]
         lib.dsa_row_topk_pieces.argtypes = [vp]
+        lib.dsa_row_topk_plan.argtypes = [ctypes.POINTER(TopkShape), i32,
+                                          ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int64)]
         lib.dsa_row_topk.argtypes = [vp, vp, vp, vp, vp, vp]
         lib.dsa_row_topk_last_error.restype = ctypes.c_char_p
         lib.dsa_sparse_attn_init.argtypes = [ctypes.POINTER(AttnShape), i32, ctypes.POINTER(vp)]
@@ -437,6 +441,17 @@ def indexer_select(q8, k8, w, kscale, starts, ends, block_size: int, k_blocks: i
     if rc != 0:
         raise DsaError(rc, load().dsa_indexer_last_error().decode(errors="replace"))
     return block_ids, token_ids
+
+
+def row_topk_plan(rows: int, width: int, k: int, cus: int, col_stride: int = 1):
+    """(pieces per row, workspace bytes) of a row top-k shape on a device with
+    ``cus`` compute units (dsa_row_topk_plan: host only)."""
+    shape = TopkShape(rows, k, width, max(1, width * col_stride), col_stride, 1, 1)
+    p, w = ctypes.c_int32(), ctypes.c_int64()
+    rc = load().dsa_row_topk_plan(ctypes.byref(shape), cus, ctypes.byref(p), ctypes.byref(w))
+    if rc != 0:
+        raise DsaError(rc, load().dsa_row_topk_last_error().decode(errors="replace"))
+    return p.value, w.value
 
 
 class RowTopk:

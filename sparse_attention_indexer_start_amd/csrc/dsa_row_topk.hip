@@ -816,9 +816,13 @@ extern "C" {
 
 const char* dsa_row_topk_last_error(void) { return g_rt_err.c_str(); }
 
-int dsa_row_topk_init(const dsa_topk_shape* s, int device, dsa_topk_ctx** out) {
-  if (!out) return rt_fail(DSA_ERR_INVALID_ARG, "out is null");
-  *out = nullptr;
+}  // extern "C"
+
+namespace {
+
+// Validates a shape and plans it for a device with `cus` CUs into c: pieces
+// per row, list entries per piece and the workspace size.  No device call.
+int rt_plan(const dsa_topk_shape* s, int cus, dsa_topk_ctx* c) {
   if (!s) return rt_fail(DSA_ERR_INVALID_ARG, "shape is null");
   if (s->rows < 0 || s->width < 0) return rt_fail(DSA_ERR_INVALID_ARG, "rows and width must be >= 0");
   if (s->width >= ((int64_t)1 << 31)) return rt_fail(DSA_ERR_UNSUPPORTED, "width must be < 2^31");
@@ -827,18 +831,9 @@ int dsa_row_topk_init(const dsa_topk_shape* s, int device, dsa_topk_ctx** out) {
   if (s->starts_repeat < 1 || s->ends_repeat < 1) return rt_fail(DSA_ERR_INVALID_ARG, "repeats must be >= 1");
   if (s->rows > 1 && s->width > 0 && s->row_stride < (s->width - 1) * s->col_stride + 1)
     return rt_fail(DSA_ERR_INVALID_ARG, "row_stride overlaps rows");
-  if (device < 0) return rt_fail(DSA_ERR_INVALID_ARG, "device must be >= 0");
-  DeviceScope ds(device);
-  if (ds.e != hipSuccess) return rt_hip(ds.e, "hipSetDevice");
-  int cus = 0;
-  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
-  if (e != hipSuccess) return rt_hip(e, "hipDeviceGetAttribute(CU count)");
-  dsa_topk_ctx* c = new (std::nothrow) dsa_topk_ctx;
-  if (!c) return rt_fail(DSA_ERR_HIP, "host allocation failed");
+  if (cus < 1) return rt_fail(DSA_ERR_INVALID_ARG, "cus must be >= 1");
   std::memset(c, 0, sizeof(*c));
   c->sh = *s;
-  c->device = device;
-  c->magic = RT_MAGIC;
   // Pieces per row: about two workgroups per CU over all rows (each piece's
   // histogram is merged into its row's with atomics, so fewer, longer pieces
   // contend less), each piece at least MIN_PIECE columns of the widest row,
@@ -847,7 +842,7 @@ int dsa_row_topk_init(const dsa_topk_shape* s, int device, dsa_topk_ctx** out) {
   int64_t P = (2 * (int64_t)cus + R - 1) / R;
   P = std::min<int64_t>(P, std::max<int64_t>(1, (s->width + MIN_PIECE - 1) / MIN_PIECE));
   P = std::max<int64_t>(1, std::min<int64_t>(P, 4096));
-  if (P * R > ((int64_t)1 << 31) - 1) { delete c; return rt_fail(DSA_ERR_UNSUPPORTED, "too many rows"); }
+  if (P * R > ((int64_t)1 << 31) - 1) return rt_fail(DSA_ERR_UNSUPPORTED, "too many rows");
   c->P = (int)P;
   // List entries per piece: four times a piece's share of K plus 256 (the
   // first digit's bin usually holds far fewer keys than K), at most a piece.
@@ -860,6 +855,45 @@ int dsa_row_topk_init(const dsa_topk_shape* s, int device, dsa_topk_ctx** out) {
     const int64_t words = 2 * R * P * seg + R * ROW_HIST + R * STATE + 2 * R * P + 2 * R * P +
                           R * P * SFX + R * P * LW;
     c->ws_bytes = (size_t)words * 4;
+  }
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_row_topk_plan(const dsa_topk_shape* s, int cus, int32_t* pieces, int64_t* workspace_bytes) {
+  dsa_topk_ctx c;
+  const int rc = rt_plan(s, cus, &c);
+  if (rc != DSA_OK) return rc;
+  if (pieces) *pieces = c.P;
+  if (workspace_bytes) *workspace_bytes = (int64_t)c.ws_bytes;
+  return DSA_OK;
+}
+
+int dsa_row_topk_init(const dsa_topk_shape* s, int device, dsa_topk_ctx** out) {
+  if (!out) return rt_fail(DSA_ERR_INVALID_ARG, "out is null");
+  *out = nullptr;
+  {
+    dsa_topk_ctx check;   // the shape is validated before any device call
+    const int rc = rt_plan(s, 1, &check);
+    if (rc != DSA_OK) return rc;
+  }
+  if (device < 0) return rt_fail(DSA_ERR_INVALID_ARG, "device must be >= 0");
+  DeviceScope ds(device);
+  if (ds.e != hipSuccess) return rt_hip(ds.e, "hipSetDevice");
+  int cus = 0;
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return rt_hip(e, "hipDeviceGetAttribute(CU count)");
+  dsa_topk_ctx* c = new (std::nothrow) dsa_topk_ctx;
+  if (!c) return rt_fail(DSA_ERR_HIP, "host allocation failed");
+  const int rc = rt_plan(s, cus, c);
+  if (rc != DSA_OK) { delete c; return rc; }
+  c->device = device;
+  c->magic = RT_MAGIC;
+  const int64_t R = std::max<int64_t>(1, s->rows), P = c->P, seg = c->seg;
+  if (s->rows > 0 && s->width > 0) {
     e = hipMalloc(&c->ws, c->ws_bytes);
     if (e != hipSuccess) { delete c; return rt_hip(e, "hipMalloc(workspace)"); }
     e = hipMemset(c->ws, 0, c->ws_bytes);

@@ -136,3 +136,39 @@ def test_attn_plan_rejects_bad_shapes():
         binding.attn_plan(4, 1, 4, 64, 64, 256)                             # head_dim 64
     with pytest.raises(binding.DsaError):
         binding.attn_plan(4, 1, 4, 256, 64, 0)                              # no CUs
+
+
+# ---------------------------------------------------------------------------
+# Cooperative row top-k: pieces per row and workspace
+# ---------------------------------------------------------------------------
+
+def _rt_expected(rows, width, k, cus):
+    """About two workgroups per CU over all rows, at least 8192 columns per
+    piece and at most 4096 pieces; the workspace holds (66,816 + 12 + P *
+    (269 + 2 * seg)) words per row, seg = the list entries per piece (four
+    times a piece's share of K plus 256, at most a piece, in 8 equal parts
+    plus 8)."""
+    R = max(1, rows)
+    P = max(1, min(-(-2 * cus // R), max(1, -(-width // 8192)), 4096))
+    cmax = (-(-width // P) + 3) & ~3
+    seg = max(1, min(cmax, 4 * -(-k // P) + 256))
+    seg = -(-seg // 8) * 8 + 8
+    words = R * (66816 + 12 + P * (269 + 2 * seg))
+    return P, words * 4
+
+
+@pytest.mark.parametrize("rows,width,k", [(1, 16 << 20, 2048), (1, 16 << 20, 1 << 20),
+                                          (4, 4 << 20, 2048), (96, 1 << 20, 2048),
+                                          (8192, 131072, 2048), (3, 20000, 7)])
+@pytest.mark.parametrize("cus", [256, 80])
+def test_row_topk_plan_matches_the_documented_rules(rows, width, k, cus):
+    assert binding.row_topk_plan(rows, width, k, cus) == _rt_expected(rows, width, k, cus)
+
+
+def test_row_topk_plan_rejects_bad_shapes():
+    with pytest.raises(binding.DsaError):
+        binding.row_topk_plan(1, 1000, 0, 256)          # k 0
+    with pytest.raises(binding.DsaError):
+        binding.row_topk_plan(1, 1 << 31, 8, 256)       # width 2^31
+    with pytest.raises(binding.DsaError):
+        binding.row_topk_plan(1, 1000, 8, 0)            # no CUs
